@@ -1,0 +1,109 @@
+"""The pins reject plausible mistakes planted in the oracle.
+
+Each case edits one expression of ``oracle/ep_oracle.c`` (a dropped term, a
+wrong index, an inclusive count, a wrong rounding rule ...), builds the edited
+copy with gcc into a temporary directory and runs a compact version of the pin
+suite against it; at least one pin must fail.  Everything runs on the CPU.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from combine_ep_layout_07_amd.workloads import Workload, draw_expert_outputs, generate
+from tests.brute import (assert_tables_equal, brute_layout, check_dispatch, combine_rows_for_token,
+                         exact_combine_row, fraction_to_bf16_bits, sorted_layout)
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ep_oracle.c")
+
+MUTANTS = {
+    "dedup_by_expert_not_rank": ("if (e2 >= 0 && e2 / El == e / El) return 0;", "if (e2 >= 0 && e2 == e) return 0;"),
+    "row_base_uses_T": ("slot[k] = (int32_t)((int64_t)s * Nmax + run[e / El]);",
+                        "slot[k] = (int32_t)((int64_t)s * T + run[e / El]);"),
+    "inclusive_running_count": ("slot[k] = (int32_t)((int64_t)s * Nmax + run[e / El]);",
+                                "slot[k] = (int32_t)((int64_t)s * Nmax + run[e / El] + 1);"),
+    "psum_drops_carry": ("ps[s + 1] = ps[s] + tokens_per_rank[(size_t)s * R + d];",
+                         "ps[s + 1] = tokens_per_rank[(size_t)s * R + d];"),
+    "recv_base_wrong_column": ("recv_base[d + 1] = recv_base[d] + recv_psum[(size_t)d * (S + 1) + S];",
+                               "recv_base[d + 1] = recv_base[d] + recv_psum[(size_t)d * (S + 1) + S - 1];"),
+    "no_alignment_padding": ("int64_t padded = (cnt + A - 1) / A * A;", "int64_t padded = cnt;"),
+    "expand_pos_preincrement": ("expand_pos[i] = e >= 0 ? next[e]++ : -1;", "expand_pos[i] = e >= 0 ? ++next[e] - 1 + (e % 2) : -1;"),
+    "error_flag_off_by_one": ("if (tok[k] >= E) flags |= 1;", "if (tok[k] > E) flags |= 1;"),
+    "meta_global_token": ("meta[0] = t;", "meta[0] = s * T + t;"),
+    "src_idx_drops_source": ("recv_src_idx[i] = (int32_t)((int64_t)s * T + meta[0]);", "recv_src_idx[i] = meta[0];"),
+    "topk_idx_not_local": ("recv_topk_idx[i * K + k] = e - d * El;", "recv_topk_idx[i * K + k] = e;"),
+    "masked_weight_negative_zero": ("recv_topk_weights[i * K + k] = 0.0f;", "recv_topk_weights[i * K + k] = -0.0f;"),
+    "combine_wrong_weight_index": ("acc[h] += (double)w[k] * bf16_to_double(yr[h]);",
+                                   "acc[h] += (double)w[0] * bf16_to_double(yr[h]);"),
+    "combine_row_drops_psum": (
+        "row = (size_t)recv_base[d] + (size_t)recv_psum[(size_t)d * (S + 1) + s] + (size_t)j;",
+        "row = (size_t)recv_base[d] + (size_t)j;"),
+    "rounding_ties_away": ("double n = nearbyint(a / q);", "double n = floor(a / q + 0.5);"),
+    "rounding_no_subnormals": ("if (e < -126) e = -126;", ""),
+    "expand_weight_from_owner": ("recv_topk_weights[r] = topk_weights[((size_t)s * T + t) * K + k];",
+                                 "recv_topk_weights[r] = topk_weights[((size_t)s * T + t) * K + k0];"),
+    "padding_src_zero": ("recv_src_idx[r] = -1;", "recv_src_idx[r] = 0;"),
+}
+
+SMALL = [
+    Workload("m1", S=2, T=21, H=64, K=4, E=16, R=4, Nmax=24),
+    Workload("m2", S=2, T=17, H=128, K=3, E=12, R=6, Nmax=17, expand=True, alignment=4, dtype="fp8"),
+]
+
+
+def pin_suite():
+    """A compact run of the oracle pins; raises AssertionError on the first failure."""
+    for seed in range(12):
+        rng = np.random.default_rng(seed)
+        S, R, El, K = 1 + seed % 3, 1 + seed % 4, 1 + seed % 3, 1 + seed % 4
+        E, T = R * El, 3 + seed
+        topk = rng.integers(-1, E + 1, size=(S, T, K)).astype(np.int64)
+        for expand, A in ((False, 1), (True, 1 + seed % 3)):
+            got = oracle.layout(S, T, K, E, R, T + 2, topk, expand, A)
+            assert_tables_equal(got, brute_layout(S, T, K, E, R, T + 2, topk, expand, A))
+    rng = np.random.default_rng(99)
+    topk = rng.integers(-1, 40, size=(2, 200, 6)).astype(np.int64)
+    got = oracle.layout(2, 200, 6, 40, 8, 200, topk, True, 2)
+    assert_tables_equal(got, sorted_layout(2, 200, 6, 40, 8, 200, topk, True, 2))
+    for w in SMALL:
+        d = generate(w, 3, masked_frac=0.15, invalid_frac=0.03, dup_frac=0.3)
+        lay = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, d["topk_idx"], w.expand, w.alignment)
+        disp = oracle.dispatch(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.dtype == "fp8", w.expand, w.alignment,
+                               d["x"], d.get("x_sf"), d["topk_idx"], d["topk_weights"], lay)
+        check_dispatch(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.dtype == "fp8", w.expand, w.alignment, d, lay, disp)
+        rows = oracle.recv_rows(w.S, w.T, w.K, w.E, w.R, lay, w.expand)
+        y = draw_expert_outputs(max(rows, 1), 16, 8)
+        out = oracle.combine(w.S, w.T, 16, w.K, w.E, w.R, w.Nmax, w.expand, d["topk_idx"], d["topk_weights"],
+                             lay, y)
+        for s in range(w.S):
+            for t in range(w.T):
+                pairs = combine_rows_for_token(w.S, w.T, w.K, w.E, w.R, w.Nmax, d["topk_idx"], lay, s, t, w.expand)
+                want = exact_combine_row([y[r] for r, _ in pairs], [d["topk_weights"][s, t, k] for _, k in pairs]) \
+                    if pairs else np.zeros(16, np.uint16)
+                assert (out[s, t] == want).all()
+    one, q = Fraction(1), Fraction(1, 128)
+    for c in (one + q / 2, one + 3 * q / 2, Fraction(3, 2) * Fraction(2) ** -133, Fraction(2) ** -130):
+        assert oracle.bf16_from_double(float(c)) == fraction_to_bf16_bits(c)
+
+
+def test_pin_suite_passes_on_the_oracle():
+    oracle.use_library(None)
+    pin_suite()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mutated = tmp_path / "ep_oracle_mutant.c"
+    mutated.write_text(src.replace(old, new))
+    lib = oracle.compile_oracle(str(mutated), str(tmp_path / "libmutant.so"))
+    oracle.use_library(lib)
+    try:
+        with pytest.raises((AssertionError, ValueError)):
+            pin_suite()
+    finally:
+        oracle.use_library(None)
