@@ -1,0 +1,326 @@
+// ep_dispatch.hip -- scatter and copy epilogue of the deterministic dispatch.
+//
+// DeepEP v2 "Kernel-side deterministic dispatch for the non-expand layout"
+// (PR #753), section Direct vs hybrid dispatch: on the direct path the
+// receive buffer of a destination holds one Nmax-row region per source rank,
+// and senders replay the slots the layout computed.  "Add experimental direct
+// recv_x dispatch path" (PR #690), section Background: dispatch first writes
+// rows into that staging area and a copy epilogue then materialises the
+// compact recv_x plus the metadata and top-k tensors.
+//
+// Here all source and destination ranks are partitions of one GPU's HBM, so a
+// send is a local store.  Both kernels are pure HBM streams: one wavefront per
+// row, each lane moving 16-byte chunks c = lane + 64*i, the whole row (or a
+// CPL-chunk slice of it) loaded into VGPRs before any store, so every lane has
+// CPL independent 16-byte loads in flight.
+#include "ep_device.h"
+#include "ep_kernels.h"
+
+namespace ep {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / kWave;
+
+__device__ __forceinline__ u32x4 ld16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void st16(uint8_t *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+// ----------------------------------------------------------------- scatter
+// One wave per token (s, t): load the row once, store it to the staging row
+// (d, s, slot - s*Nmax) of every owner lane, with the fp8 scales and the
+// metadata record {t, expert ids, weight bits}.
+template <int CPL>
+__global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
+    const Shape &sh = a.sh;
+    const int lane = lane_id();
+    const int64_t n_tok = (int64_t)sh.S * sh.T;
+    const int nchunks = sh.row_bytes / 16;
+    const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t g = wave0; g < n_tok; g += nwaves) {
+        const int s = (int)(g / sh.T), t = (int)(g - (int64_t)s * sh.T);
+        int e = -1, slot = -1, wbits = 0;
+        if (lane < sh.K) {
+            const int64_t e64 = a.topk_idx[g * sh.K + lane];
+            e = (e64 >= 0 && e64 < sh.E) ? (int)e64 : -1;
+            slot = a.dst_slot[g * sh.K + lane];
+            wbits = __float_as_int(a.topk_weights[g * sh.K + lane]);
+        }
+        const uint64_t owners = ballot(lane < sh.K && slot >= 0);
+        const uint8_t *src = a.x + g * sh.row_bytes;
+        for (int c0 = 0; c0 < nchunks; c0 += CPL * kWave) {
+            u32x4 v[CPL];
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = c0 + i * kWave + lane;
+                if (c < nchunks) v[i] = ld16(src + (int64_t)c * 16);
+            }
+            for (uint64_t m = owners; m; m &= m - 1) {
+                const int k = __builtin_ctzll(m);
+                const int d = read_lane(e, k) / sh.El;
+                const int j = read_lane(slot, k) - s * sh.Nmax;
+                if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for a layout of this topk_idx
+                uint8_t *dst = a.staging_x + (((int64_t)d * sh.S + s) * sh.Nmax + j) * sh.row_bytes;
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
+                    const int c = c0 + i * kWave + lane;
+                    if (c < nchunks) st16(dst + (int64_t)c * 16, v[i]);
+                }
+            }
+        }
+        // Metadata words i = lane and i = lane + 64 (K = 32 needs 65 words):
+        // word 0 = t, words 1..K = expert ids, words K+1..2K = weight bits.
+        // Shuffled with every lane active, before any divergent store.
+        const int ev = shfl(e, lane >= 1 ? lane - 1 : 0);
+        const int wv = shfl(wbits, lane - 1 - sh.K >= 0 ? lane - 1 - sh.K : 0);
+        const int hi_src = lane + kWave - 1 - sh.K;
+        const int wv_hi = shfl(wbits, hi_src >= 0 && hi_src < kWave ? hi_src : 0);
+        const int word0 = lane == 0 ? t : (lane <= sh.K ? ev : wv);
+        // Scales and metadata of every owner's staging row.
+        for (uint64_t m = owners; m; m &= m - 1) {
+            const int k = __builtin_ctzll(m);
+            const int d = read_lane(e, k) / sh.El;
+            const int j = read_lane(slot, k) - s * sh.Nmax;
+            if ((unsigned)j >= (unsigned)sh.Nmax) continue;
+            const int64_t row = ((int64_t)d * sh.S + s) * sh.Nmax + j;
+            for (int i = lane; i < sh.sf_per_row; i += kWave)
+                a.staging_sf[row * sh.sf_per_row + i] = a.x_sf[g * sh.sf_per_row + i];
+            if (lane < sh.meta_words) a.staging_meta[row * sh.meta_words + lane] = word0;
+            if (lane + kWave < sh.meta_words) a.staging_meta[row * sh.meta_words + lane + kWave] = wv_hi;
+        }
+    }
+}
+
+// Which (destination, source, row) a compact receive row i comes from:
+// d = last d with recv_base[d] <= i, s = last s with recv_psum[d][s] <= i - base.
+__device__ __forceinline__ void locate_row(const int32_t *recv_base, const int32_t *recv_psum, int R, int S,
+                                           int i, int &d, int &s, int &j) {
+    int lo = 0, hi = R;  // invariant: recv_base[lo] <= i < recv_base[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (recv_base[mid] <= i) lo = mid; else hi = mid;
+    }
+    d = lo;
+    const int off = i - recv_base[d];
+    const int32_t *ps = recv_psum + (int64_t)d * (S + 1);
+    lo = 0;
+    hi = S;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (ps[mid] <= off) lo = mid; else hi = mid;
+    }
+    s = lo;
+    j = off - ps[s];
+}
+
+// Receiver tables in LDS: recv_base [R+1] then recv_psum [R][S+1].
+__device__ __forceinline__ const int32_t *stage_tables(const DispatchArgs &a, int32_t *lds, bool fits) {
+    if (!fits) return nullptr;
+    const int nb = a.sh.R + 1, np = a.sh.R * (a.sh.S + 1);
+    for (int i = threadIdx.x; i < nb + np; i += kThreads) lds[i] = i < nb ? a.recv_base[i] : a.recv_psum[i - nb];
+    __syncthreads();
+    return lds;
+}
+
+// ------------------------------------------------- compact copy epilogue
+// One wave per filled receive row i < recv_base[R]: copy staging row
+// (d, s, j) to recv row i, and derive the per-row metadata.
+template <int CPL>
+__global__ void __launch_bounds__(kThreads) k_epilogue(DispatchArgs a, int tables_in_lds) {
+    const Shape &sh = a.sh;
+    extern __shared__ int32_t lds_tab[];
+    const int32_t *tab = stage_tables(a, lds_tab, tables_in_lds != 0);
+    const int32_t *rbase = tab ? tab : a.recv_base;
+    const int32_t *rpsum = tab ? tab + sh.R + 1 : a.recv_psum;
+    const int lane = lane_id();
+    const int n_rows = (int)min((int64_t)a.recv_base[sh.R], a.recv_capacity_rows);
+    const int nchunks = sh.row_bytes / 16;
+    const int wave0 = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    const int nwaves = gridDim.x * kWavesPerBlock;
+    for (int i = wave0; i < n_rows; i += nwaves) {
+        int d, s, j;
+        locate_row(rbase, rpsum, sh.R, sh.S, i, d, s, j);
+        if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for tables of one layout
+        const int64_t row = ((int64_t)d * sh.S + s) * sh.Nmax + j;
+        const uint8_t *src = a.staging_x + row * sh.row_bytes;
+        uint8_t *dst = a.recv_x + (int64_t)i * sh.row_bytes;
+        for (int c0 = 0; c0 < nchunks; c0 += CPL * kWave) {
+            u32x4 v[CPL];
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) {
+                const int c = c0 + q * kWave + lane;
+                if (c < nchunks) v[q] = ld16(src + (int64_t)c * 16);
+            }
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) {
+                const int c = c0 + q * kWave + lane;
+                if (c < nchunks) st16(dst + (int64_t)c * 16, v[q]);
+            }
+        }
+        for (int q = lane; q < sh.sf_per_row; q += kWave)
+            a.recv_sf[(int64_t)i * sh.sf_per_row + q] = a.staging_sf[row * sh.sf_per_row + q];
+        const int32_t *meta = a.staging_meta + row * sh.meta_words;
+        const int t = meta[0];
+        if (lane == 0) a.recv_src_idx[i] = s * sh.T + t;
+        for (int k = lane; k < sh.K; k += kWave) {
+            const int e = meta[1 + k];
+            const bool on_d = e >= 0 && e / sh.El == d;
+            a.recv_topk_idx[(int64_t)i * sh.K + k] = on_d ? e - d * sh.El : -1;
+            a.recv_topk_weights[(int64_t)i * sh.K + k] = on_d ? __int_as_float(meta[1 + sh.K + k]) : 0.0f;
+        }
+    }
+}
+
+// -------------------------------------------------- expand copy epilogue
+// One wave per filled staging row (d, s, j): the row goes to the expand row of
+// every lane of that token on destination d (one per lane, duplicates
+// included), with the source index and the lane's weight.
+template <int CPL>
+__global__ void __launch_bounds__(kThreads) k_epilogue_expand(DispatchArgs a, int tables_in_lds) {
+    const Shape &sh = a.sh;
+    extern __shared__ int32_t lds_tab[];
+    const int32_t *tab = stage_tables(a, lds_tab, tables_in_lds != 0);
+    const int32_t *rbase = tab ? tab : a.recv_base;
+    const int32_t *rpsum = tab ? tab + sh.R + 1 : a.recv_psum;
+    const int lane = lane_id();
+    const int n_rows = (int)min((int64_t)a.recv_base[sh.R], a.recv_capacity_rows);
+    const int nchunks = sh.row_bytes / 16;
+    const int wave0 = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    const int nwaves = gridDim.x * kWavesPerBlock;
+    for (int i = wave0; i < n_rows; i += nwaves) {
+        int d, s, j;
+        locate_row(rbase, rpsum, sh.R, sh.S, i, d, s, j);
+        if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for tables of one layout
+        const int64_t row = ((int64_t)d * sh.S + s) * sh.Nmax + j;
+        const int32_t *meta = a.staging_meta + row * sh.meta_words;
+        const int t = meta[0];
+        int pos = -1, wbits = 0;
+        if (lane < sh.K) {
+            const int e = meta[1 + lane];
+            if (e >= 0 && e / sh.El == d) {
+                pos = a.expand_pos[((int64_t)s * sh.T + t) * sh.K + lane];
+                wbits = meta[1 + sh.K + lane];
+            }
+        }
+        const uint64_t lanes_on_d = ballot(pos >= 0);
+        const uint8_t *src = a.staging_x + row * sh.row_bytes;
+        for (int c0 = 0; c0 < nchunks; c0 += CPL * kWave) {
+            u32x4 v[CPL];
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) {
+                const int c = c0 + q * kWave + lane;
+                if (c < nchunks) v[q] = ld16(src + (int64_t)c * 16);
+            }
+            for (uint64_t m = lanes_on_d; m; m &= m - 1) {
+                const int r = read_lane(pos, __builtin_ctzll(m));
+                if ((uint64_t)r >= (uint64_t)a.recv_capacity_rows) continue;
+                uint8_t *dst = a.recv_x + (int64_t)r * sh.row_bytes;
+#pragma unroll
+                for (int q = 0; q < CPL; ++q) {
+                    const int c = c0 + q * kWave + lane;
+                    if (c < nchunks) st16(dst + (int64_t)c * 16, v[q]);
+                }
+            }
+        }
+        for (uint64_t m = lanes_on_d; m; m &= m - 1) {
+            const int k = __builtin_ctzll(m);
+            const int r = read_lane(pos, k);
+            if ((uint64_t)r >= (uint64_t)a.recv_capacity_rows) continue;
+            for (int q = lane; q < sh.sf_per_row; q += kWave)
+                a.recv_sf[(int64_t)r * sh.sf_per_row + q] = a.staging_sf[row * sh.sf_per_row + q];
+            if (lane == k) {
+                a.recv_src_idx[r] = s * sh.T + t;
+                a.recv_topk_weights[r] = __int_as_float(wbits);
+            }
+        }
+    }
+}
+
+// Padding rows of each expert segment (alignment A > 1): zero row and
+// scales, source index -1, weight +0.  One workgroup per expert.
+__global__ void __launch_bounds__(kThreads) k_expand_padding(DispatchArgs a) {
+    const Shape &sh = a.sh;
+    const int e = blockIdx.x;
+    int cnt = 0;
+    for (int s = 0; s < sh.S; ++s) cnt += a.tokens_per_expert[(int64_t)s * sh.E + e];
+    const int r0 = a.expert_base[e] + cnt;
+    const int r1 = (int)min((int64_t)a.expert_base[e + 1], a.recv_capacity_rows);
+    const int nchunks = sh.row_bytes / 16;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int r = r0; r < r1; ++r) {
+        uint8_t *dst = a.recv_x + (int64_t)r * sh.row_bytes;
+        for (int c = threadIdx.x; c < nchunks; c += kThreads) st16(dst + (int64_t)c * 16, zero);
+        for (int q = threadIdx.x; q < sh.sf_per_row; q += kThreads) a.recv_sf[(int64_t)r * sh.sf_per_row + q] = 0.0f;
+        if (threadIdx.x == 0) {
+            a.recv_src_idx[r] = -1;
+            a.recv_topk_weights[r] = 0.0f;
+        }
+    }
+}
+
+int chunks_per_lane(const Shape &sh) { return (sh.row_bytes / 16 + kWave - 1) / kWave; }
+
+template <template <int> class Launcher, typename... Args>
+hipError_t dispatch_cpl(int need, Args &&...args) {
+    if (need <= 1) return Launcher<1>::run(args...);
+    if (need <= 2) return Launcher<2>::run(args...);
+    if (need <= 4) return Launcher<4>::run(args...);
+    if (need <= 7) return Launcher<7>::run(args...);
+    if (need <= 8) return Launcher<8>::run(args...);
+    if (need <= 14) return Launcher<14>::run(args...);
+    return Launcher<16>::run(args...);
+}
+
+int grid_for(int64_t work_waves) {
+    // Enough waves to fill 256 CUs several times over; extra work is strided.
+    int64_t blocks = (work_waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (blocks > 2048) blocks = 2048;
+    if (blocks < 1) blocks = 1;
+    return (int)blocks;
+}
+
+template <int CPL>
+struct ScatterL {
+    static hipError_t run(const DispatchArgs &a, hipStream_t st) {
+        const int64_t n_tok = (int64_t)a.sh.S * a.sh.T;
+        hipLaunchKernelGGL(k_scatter<CPL>, dim3(grid_for(n_tok)), dim3(kThreads), 0, st, a);
+        return hipGetLastError();
+    }
+};
+
+template <int CPL>
+struct EpilogueL {
+    static hipError_t run(const DispatchArgs &a, hipStream_t st) {
+        const size_t tab = sizeof(int32_t) * ((size_t)a.sh.R + 1 + (size_t)a.sh.R * (a.sh.S + 1));
+        const bool fits = tab <= 32768;
+        const int64_t rows = a.sh.expand ? (int64_t)a.sh.S * a.sh.T * (a.sh.K < a.sh.R ? a.sh.K : a.sh.R)
+                                         : a.recv_capacity_rows;
+        if (a.sh.expand)
+            hipLaunchKernelGGL(k_epilogue_expand<CPL>, dim3(grid_for(rows)), dim3(kThreads), fits ? tab : 0, st, a,
+                               (int)fits);
+        else
+            hipLaunchKernelGGL(k_epilogue<CPL>, dim3(grid_for(rows)), dim3(kThreads), fits ? tab : 0, st, a,
+                               (int)fits);
+        return hipGetLastError();
+    }
+};
+
+}  // namespace
+
+hipError_t launch_scatter(const DispatchArgs &a, hipStream_t stream) {
+    if ((int64_t)a.sh.S * a.sh.T == 0) return hipSuccess;
+    return dispatch_cpl<ScatterL>(chunks_per_lane(a.sh), a, stream);
+}
+
+hipError_t launch_epilogue(const DispatchArgs &a, hipStream_t stream) {
+    hipError_t err = hipSuccess;
+    if ((int64_t)a.sh.S * a.sh.T > 0) err = dispatch_cpl<EpilogueL>(chunks_per_lane(a.sh), a, stream);
+    if (err != hipSuccess) return err;
+    if (a.sh.expand && a.sh.A > 1) {
+        hipLaunchKernelGGL(k_expand_padding, dim3(a.sh.E), dim3(kThreads), 0, stream, a);
+        err = hipGetLastError();
+    }
+    return err;
+}
+
+}  // namespace ep

@@ -1,0 +1,75 @@
+// ep_kernels.h -- launch arguments and launchers of the libep kernels.  Host
+// code (ep_api.cpp) validates a configuration, fills these structs and calls
+// the launchers; each launcher only enqueues on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+// Shape shared by all kernels (validated on the host).
+struct Shape {
+    int S, T, H, K, E, R, El, Nmax;
+    int expand, A;
+    int is_fp8;
+    int row_bytes;   // bytes of one dispatched hidden row
+    int sf_per_row;  // fp32 scales per row (fp8), else 0
+    int meta_words;  // 1 + 2K
+    int bits_R, bits_E;  // key widths for ballot matching of ranks / experts
+};
+
+// Layout pass geometry: B workgroups per source, each owning `chunk` tokens
+// (split into 4 equal wave ranges of chunk/4 tokens).
+struct LayoutGeom {
+    int blocks_per_src;
+    int chunk;
+};
+
+LayoutGeom layout_geometry(const Shape &sh, int num_layout_cus);
+uint64_t layout_scratch_bytes(const Shape &sh, const LayoutGeom &g);
+
+struct LayoutArgs {
+    Shape sh;
+    LayoutGeom g;
+    const int64_t *topk_idx;
+    int32_t *dst_slot, *tokens_per_rank, *tokens_per_expert, *recv_psum, *recv_base;
+    int32_t *expert_base, *expand_pos, *error_flags;
+    int32_t *blk_cnt_rank;    // scratch [S*B][R]
+    int32_t *blk_cnt_expert;  // scratch [S*B][E]
+    int32_t *blk_flags;       // scratch [S*B]
+};
+
+struct DispatchArgs {
+    Shape sh;
+    const uint8_t *x;
+    const float *x_sf;
+    const int64_t *topk_idx;
+    const float *topk_weights;
+    const int32_t *dst_slot, *recv_psum, *recv_base, *tokens_per_expert, *expert_base, *expand_pos;
+    uint8_t *staging_x;
+    float *staging_sf;
+    int32_t *staging_meta;
+    uint8_t *recv_x;
+    float *recv_sf;
+    int32_t *recv_src_idx, *recv_topk_idx;
+    float *recv_topk_weights;
+    int64_t recv_capacity_rows;
+};
+
+struct CombineArgs {
+    Shape sh;
+    const int64_t *topk_idx;
+    const float *topk_weights;
+    const int32_t *dst_slot, *recv_psum, *recv_base, *expand_pos;
+    const uint16_t *y;
+    uint16_t *out;
+    int64_t y_rows;  // rows of y (the receive capacity)
+};
+
+hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream);
+hipError_t launch_scatter(const DispatchArgs &a, hipStream_t stream);
+hipError_t launch_epilogue(const DispatchArgs &a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
+
+}  // namespace ep

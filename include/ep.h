@@ -1,0 +1,217 @@
+/*
+ * ep.h -- C ABI of libep: deterministic MoE expert-parallel dispatch layout,
+ * dispatch (scatter + copy epilogue) and combine on one GPU's share of the
+ * work, as HIP kernels for CDNA4 (gfx950).
+ *
+ * Sources (DeepEP v2 pages):
+ *   [DET] "DeepEP v2: Kernel-side deterministic dispatch for the non-expand
+ *         layout" (PR #753): sections Motivation, Approach, Direct vs hybrid
+ *         dispatch, Compatibility, New API.
+ *   [DRX] "DeepEP v2: Add experimental direct recv_x dispatch path" (PR #690):
+ *         sections Background, Direct Recv X design, Implementation, and the
+ *         review's buffer-size and guardrail comments.
+ *   [UNO] "Add unordered hybrid kernels for transports without ordered
+ *         delivery" (PR #732): section Changes (combine reduce epilogue).
+ *
+ * Model.  S source partitions ("source ranks") each hold T tokens; every token
+ * routes to K experts out of E, and expert e lives on logical rank e / El,
+ * El = E / R.  All S sources and all R destinations are partitions of the one
+ * GPU's HBM: a "send" is a local store, and stream order replaces the pages'
+ * signals and release atomics.
+ *
+ * Conventions for every call:
+ *   - pointers named *_dev are device pointers the caller allocated (for
+ *     example with torch.empty(..., device="cuda")); the library never
+ *     allocates, frees or keeps state between calls;
+ *   - all arrays are dense row-major; rows of x, staging and recv are 16-byte
+ *     aligned (the base pointers must be 16-byte aligned, and the row size in
+ *     bytes is a multiple of 16);
+ *   - `stream` is a hipStream_t (NULL = the default stream); calls only
+ *     enqueue work on it and never synchronise;
+ *   - argument errors are detected on the host before anything is enqueued
+ *     and return a negative ep_status; a failed launch returns EP_ERR_HIP;
+ *   - data errors found on the device (a top-k id >= E) set bit 0 of
+ *     *error_flags and the lane is then treated as masked (id < 0);
+ *   - calls on different streams with disjoint buffers may run concurrently.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum ep_status {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARG = -1, /* a size, dtype or pointer is not acceptable    */
+    EP_ERR_CAPACITY = -2,    /* Nmax < T, or a buffer is smaller than needed  */
+    EP_ERR_UNSUPPORTED = -3, /* outside the limits below                      */
+    EP_ERR_HIP = -4          /* the HIP runtime refused a launch              */
+};
+
+enum ep_dtype {
+    EP_DTYPE_BF16 = 0,        /* rows of H bf16                                */
+    EP_DTYPE_FP8_E4M3FN = 1   /* rows of H OCP e4m3fn bytes + H/128 fp32 scales */
+};
+
+/* Phases of ep_dispatch.  The pages time the sender's dispatch kernel and the
+ * receiver's copy epilogue separately ([DET] Performance, [DRX] Background);
+ * a caller may enqueue them in two calls (for example with its own event
+ * between them).  EP_PHASE_ALL runs both. */
+enum ep_phase {
+    EP_PHASE_SCATTER = 1,
+    EP_PHASE_EPILOGUE = 2,
+    EP_PHASE_ALL = 3
+};
+
+/* Limits (checked on the host): 1 <= R <= 64, 1 <= K <= 32, E % R == 0,
+ * E <= 1024, S * Nmax < 2^31, S * T * K < 2^31, H * element size a multiple of
+ * 16 bytes, fp8 needs H % 128 == 0. */
+#define EP_MAX_RANKS 64
+#define EP_MAX_TOPK 32
+#define EP_MAX_EXPERTS 1024
+
+typedef struct ep_config {
+    int32_t num_src_ranks;            /* S >= 1                                  */
+    int32_t num_tokens;               /* T >= 0, tokens per source               */
+    int32_t hidden;                   /* H                                       */
+    int32_t num_topk;                 /* K                                       */
+    int32_t num_experts;              /* E                                       */
+    int32_t num_ranks;                /* R, destination ranks                    */
+    int32_t num_max_tokens_per_rank;  /* Nmax >= T, else EP_ERR_CAPACITY: the
+                                         rows a source may fill at one
+                                         destination ([DET] Approach)            */
+    int32_t x_dtype;                  /* enum ep_dtype                           */
+    int32_t expand;                   /* 0: compact receive layout; 1: one row
+                                         per valid (token, top-k) lane, grouped
+                                         by expert                               */
+    int32_t expert_alignment;         /* A >= 1; expand segments are padded to a
+                                         multiple of A (ignored if !expand)      */
+    int32_t num_layout_cus;           /* workgroups of the layout pass; 0 = auto
+                                         (the pages' num_prologue_sms, [DET] New
+                                         API); never changes any result          */
+    int32_t reserved;                 /* must be 0                               */
+} ep_config_t;
+
+/* Byte sizes of every caller-allocated buffer for a configuration (0 = not
+ * used).  recv_rows is the receive capacity in rows: S*T*min(K,R) for the
+ * compact layout, the largest count a destination-sum of deduplicated rows can
+ * reach; S*T*K + E*(A-1) for expand. */
+typedef struct ep_sizes {
+    uint64_t dst_slot, tokens_per_rank, tokens_per_expert, recv_psum, recv_base;
+    uint64_t expert_base, expand_pos, error_flags, layout_scratch;
+    uint64_t staging_x, staging_sf, staging_meta;
+    uint64_t recv_rows;
+    uint64_t recv_x, recv_sf, recv_src_idx, recv_topk_idx, recv_topk_weights;
+    uint64_t y, out;
+} ep_sizes_t;
+
+/* Layout tables ("handle"): written by ep_layout, read by ep_dispatch and
+ * ep_combine.  All device pointers, int32:
+ *   dst_slot          [S][T][K]  s*Nmax + the number of earlier tokens of
+ *                                source s that reach the same destination,
+ *                                on the lowest valid lane of each destination
+ *                                of a token; -1 on every other lane
+ *                                ([DET] Motivation and Approach)
+ *   tokens_per_rank   [S][R]     deduplicated tokens source s sends to rank d
+ *   tokens_per_expert [S][E]     valid lanes of source s routed to expert e
+ *   recv_psum         [R][S+1]   exclusive prefix over sources of
+ *                                tokens_per_rank[.][d]: the base of source s
+ *                                in destination d's compact receive rows
+ *                                ([DRX] Direct Recv X design)
+ *   recv_base         [R+1]      exclusive prefix over destinations of the
+ *                                deduplicated row totals recv_psum[d][S];
+ *                                recv_base[R] = rows in the compact layout
+ *   expert_base       [E+1]      expand only: first row of expert e, segments
+ *                                padded to a multiple of A
+ *   expand_pos        [S][T][K]  expand only: receive row of a valid lane
+ *                                (ascending (s,t,k) inside the expert), else -1
+ *   error_flags       [1]        bit 0: some top-k id was >= E
+ *   scratch           bytes      ep_sizes_t.layout_scratch, private to the
+ *                                library; contents need no initialisation  */
+typedef struct ep_layout {
+    int32_t *dst_slot_dev;
+    int32_t *tokens_per_rank_dev;
+    int32_t *tokens_per_expert_dev;
+    int32_t *recv_psum_dev;
+    int32_t *recv_base_dev;
+    int32_t *expert_base_dev;   /* NULL unless expand */
+    int32_t *expand_pos_dev;    /* NULL unless expand */
+    int32_t *error_flags_dev;
+    void *scratch_dev;
+} ep_layout_t;
+
+/* Staging ([R][S][Nmax] rows: destination d's receive buffer holds one Nmax-row
+ * region per source, [DET] Direct vs hybrid dispatch) and receive buffers.
+ *   staging_x     [R][S][Nmax][row bytes]
+ *   staging_sf    [R][S][Nmax][H/128] fp32 (fp8 only, else NULL)
+ *   staging_meta  [R][S][Nmax][1+2K] int32: token index t, the token's K
+ *                 expert ids (masked/invalid as -1), the K weights' fp32 bits
+ *   compact layout (expand == 0), row i of destination d's source s slot j is
+ *   i = recv_base[d] + recv_psum[d][s] + j:
+ *     recv_x [recv_rows][row bytes], recv_sf [recv_rows][H/128],
+ *     recv_src_idx [recv_rows] (= s*T + t), recv_topk_idx [recv_rows][K]
+ *     (local expert id on d, else -1), recv_topk_weights [recv_rows][K]
+ *     (weight, else +0)
+ *   expand layout: recv_x, recv_sf, recv_src_idx as above at expand_pos rows,
+ *     recv_topk_weights [recv_rows] (the lane's weight); recv_topk_idx unused;
+ *     padding rows get zero bytes, src -1 and weight +0.
+ * Rows beyond the filled ones are left untouched. */
+typedef struct ep_recv {
+    void *staging_x_dev;
+    float *staging_sf_dev;
+    int32_t *staging_meta_dev;
+    void *recv_x_dev;
+    float *recv_sf_dev;
+    int32_t *recv_src_idx_dev;
+    int32_t *recv_topk_idx_dev;
+    float *recv_topk_weights_dev;
+    int64_t recv_capacity_rows;       /* rows allocated; must be >= recv_rows */
+} ep_recv_t;
+
+/* Host only (no HIP call): validate cfg and fill *sizes.  Returns EP_OK or the
+ * validation error ([DRX] review: the buffer sizes are derived in one place). */
+int ep_query_sizes(const ep_config_t *cfg, ep_sizes_t *sizes);
+
+/* Deterministic layout prologue ([DET] Approach): a two-pass scan over
+ * topk_idx_dev (int64 [S][T][K]) producing every table of *layout.  The result
+ * is a pure function of topk_idx; num_layout_cus changes only the speed. */
+int ep_layout(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layout_t *layout,
+              void *stream);
+
+/* Dispatch: scatter ([DET] Direct vs hybrid dispatch: senders replay the
+ * layout's slots) of every token's row, scales and metadata into the staging
+ * rows, then the copy epilogue ([DRX] Background) into the receive buffers.
+ *   x_dev            [S][T][row bytes] (bf16, or e4m3fn bytes)
+ *   x_sf_dev         [S][T][H/128] fp32 (fp8 only, else NULL)
+ *   topk_idx_dev     int64 [S][T][K];  topk_weights_dev fp32 [S][T][K]
+ *   phases           enum ep_phase mask; the epilogue reads the staging rows
+ *                    the scatter of the same layout wrote. */
+int ep_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev,
+                const int64_t *topk_idx_dev, const float *topk_weights_dev,
+                const ep_layout_t *layout, const ep_recv_t *recv, int32_t phases, void *stream);
+
+/* Combine ([UNO] Changes: the reduce epilogue brings expert outputs back to
+ * token order): out[s][t] = bf16(sum over valid lanes k, ascending, of
+ * w[s][t][k] * Y(s,t,k)), accumulated in fp32 and rounded to nearest-even
+ * once.  Y is, in the compact layout, row recv_base[d] + recv_psum[d][s] +
+ * run of y_dev for the lane's rank d (lanes sharing a rank weight the same
+ * row); in the expand layout, row expand_pos[s][t][k].  A token with no valid
+ * lane gives +0.
+ *   y_dev   bf16 [rows][H] in the receive row order (at least recv_rows rows)
+ *   out_dev bf16 [S][T][H] */
+int ep_combine(const ep_config_t *cfg, const ep_layout_t *layout, const int64_t *topk_idx_dev,
+               const float *topk_weights_dev, const void *y_dev, void *out_dev, void *stream);
+
+/* Static description of a status code. */
+const char *ep_status_string(int status);
+
+/* Library version, MAJOR*10000 + MINOR*100 + PATCH. */
+int ep_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EP_H */

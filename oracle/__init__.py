@@ -51,6 +51,8 @@ def _open(path: str) -> ctypes.CDLL:
     lib.epo_dispatch.restype = I
     lib.epo_combine.argtypes = [I] * 8 + [P] * 8
     lib.epo_combine.restype = I
+    lib.epo_combine_tokens.argtypes = [I] * 8 + [P] * 7 + [I, P, P]
+    lib.epo_combine_tokens.restype = I
     lib.epo_bf16_from_double.argtypes = [ctypes.c_double]
     lib.epo_bf16_from_double.restype = ctypes.c_uint16
     return lib
@@ -166,6 +168,23 @@ def combine(S, T, H, K, E, R, Nmax, expand: bool, topk_idx: np.ndarray, topk_wei
                          _p(lay.get("expand_pos")), _p(yy), _p(out))
     if rc != 0:
         raise ValueError(f"epo_combine rejected the sizes (rc={rc})")
+    return out
+
+
+def combine_tokens(S, T, H, K, E, R, Nmax, expand: bool, topk_idx: np.ndarray, topk_weights: np.ndarray,
+                   lay: Dict[str, np.ndarray], y: np.ndarray, sel: np.ndarray) -> np.ndarray:
+    """Combine for the global token indices ``sel`` only; returns uint16 [len(sel)][H]."""
+    lib = _load()
+    sel = np.ascontiguousarray(sel, dtype=np.int64)
+    out = np.empty((sel.size, H), np.uint16)
+    yy = np.ascontiguousarray(y, dtype=np.uint16)
+    rc = lib.epo_combine_tokens(S, T, H, K, E, R, Nmax, int(expand),
+                                _p(np.ascontiguousarray(topk_idx, dtype=np.int64)),
+                                _p(np.ascontiguousarray(topk_weights, dtype=np.float32)),
+                                _p(lay["dst_slot"]), _p(lay["recv_psum"]), _p(lay["recv_base"]),
+                                _p(lay.get("expand_pos")), _p(yy), int(sel.size), _p(sel), _p(out))
+    if rc != 0:
+        raise ValueError(f"epo_combine_tokens rejected the arguments (rc={rc})")
     return out
 
 

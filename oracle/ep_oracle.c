@@ -273,40 +273,66 @@ uint16_t epo_bf16_from_double(double v) {
     return (uint16_t)(sign | (uint16_t)(u >> 16));
 }
 
+/* One token's combine row: acc = sum over valid lanes k (ascending) of
+ * w[k] * Y(k) in double, then one rounding to bf16 per element. */
+static void combine_token(int S, int T, int H, int K, int E, int R, int Nmax, int expand,
+                          const int64_t *topk_idx, const float *topk_weights,
+                          const int32_t *dst_slot, const int32_t *recv_psum,
+                          const int32_t *recv_base, const int32_t *expand_pos,
+                          const uint16_t *y, int s, int t, double *acc, uint16_t *o) {
+    const int El = E / R;
+    const int64_t *tok = topk_idx + ((size_t)s * T + t) * K;
+    const float *w = topk_weights + ((size_t)s * T + t) * K;
+    for (int h = 0; h < H; ++h) acc[h] = 0.0;
+    for (int k = 0; k < K; ++k) {
+        int64_t e = lane_expert(tok[k], E);
+        if (e < 0) continue;
+        size_t row;
+        if (expand) {
+            row = (size_t)expand_pos[((size_t)s * T + t) * K + k];
+        } else {
+            /* Non-expand: the one returned row per (token, rank), at the
+             * receive position of the owner lane's slot; every lane on that
+             * rank weights the same row. */
+            int d = (int)(e / El);
+            int k0 = owner_lane(tok, K, E, El, d);
+            int64_t j = (int64_t)dst_slot[((size_t)s * T + t) * K + k0] - (int64_t)s * Nmax;
+            row = (size_t)recv_base[d] + (size_t)recv_psum[(size_t)d * (S + 1) + s] + (size_t)j;
+        }
+        const uint16_t *yr = y + row * (size_t)H;
+        for (int h = 0; h < H; ++h) acc[h] += (double)w[k] * bf16_to_double(yr[h]);
+    }
+    for (int h = 0; h < H; ++h) o[h] = epo_bf16_from_double(acc[h]);
+}
+
 int epo_combine(int S, int T, int H, int K, int E, int R, int Nmax, int expand,
                 const int64_t *topk_idx, const float *topk_weights,
                 const int32_t *dst_slot, const int32_t *recv_psum,
                 const int32_t *recv_base, const int32_t *expand_pos,
                 const uint16_t *y, uint16_t *out) {
     if (!sizes_ok(S, T, K, E, R, Nmax) || H < 1) return -1;
-    const int El = E / R;
     double *acc = (double *)malloc(sizeof(double) * (size_t)H);
     for (int s = 0; s < S; ++s)
-        for (int t = 0; t < T; ++t) {
-            const int64_t *tok = topk_idx + ((size_t)s * T + t) * K;
-            const float *w = topk_weights + ((size_t)s * T + t) * K;
-            for (int h = 0; h < H; ++h) acc[h] = 0.0;
-            for (int k = 0; k < K; ++k) {
-                int64_t e = lane_expert(tok[k], E);
-                if (e < 0) continue;
-                size_t row;
-                if (expand) {
-                    row = (size_t)expand_pos[((size_t)s * T + t) * K + k];
-                } else {
-                    /* Non-expand: the one returned row per (token, rank), at
-                     * the receive position of the owner lane's slot; every
-                     * lane on that rank weights the same row. */
-                    int d = (int)(e / El);
-                    int k0 = owner_lane(tok, K, E, El, d);
-                    int64_t j = (int64_t)dst_slot[((size_t)s * T + t) * K + k0] - (int64_t)s * Nmax;
-                    row = (size_t)recv_base[d] + (size_t)recv_psum[(size_t)d * (S + 1) + s] + (size_t)j;
-                }
-                const uint16_t *yr = y + row * (size_t)H;
-                for (int h = 0; h < H; ++h) acc[h] += (double)w[k] * bf16_to_double(yr[h]);
-            }
-            uint16_t *o = out + ((size_t)s * T + t) * H;
-            for (int h = 0; h < H; ++h) o[h] = epo_bf16_from_double(acc[h]);
-        }
+        for (int t = 0; t < T; ++t)
+            combine_token(S, T, H, K, E, R, Nmax, expand, topk_idx, topk_weights, dst_slot, recv_psum,
+                          recv_base, expand_pos, y, s, t, acc, out + ((size_t)s * T + t) * H);
+    free(acc);
+    return 0;
+}
+
+int epo_combine_tokens(int S, int T, int H, int K, int E, int R, int Nmax, int expand,
+                       const int64_t *topk_idx, const float *topk_weights,
+                       const int32_t *dst_slot, const int32_t *recv_psum,
+                       const int32_t *recv_base, const int32_t *expand_pos,
+                       const uint16_t *y, int n_sel, const int64_t *sel, uint16_t *out) {
+    if (!sizes_ok(S, T, K, E, R, Nmax) || H < 1 || n_sel < 0) return -1;
+    double *acc = (double *)malloc(sizeof(double) * (size_t)H);
+    for (int i = 0; i < n_sel; ++i) {
+        if (sel[i] < 0 || sel[i] >= (int64_t)S * T) { free(acc); return -1; }
+        int s = (int)(sel[i] / T), t = (int)(sel[i] % T);
+        combine_token(S, T, H, K, E, R, Nmax, expand, topk_idx, topk_weights, dst_slot, recv_psum,
+                      recv_base, expand_pos, y, s, t, acc, out + (size_t)i * H);
+    }
     free(acc);
     return 0;
 }

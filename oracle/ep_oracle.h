@@ -82,6 +82,14 @@ int epo_combine(int S, int T, int H, int K, int E, int R, int Nmax, int expand,
                 const int32_t *recv_base, const int32_t *expand_pos,
                 const uint16_t *y, uint16_t *out);
 
+/* Combine restricted to the n_sel global token indices sel[i] = s*T + t;
+ * out is [n_sel][H].  Same definition as epo_combine. */
+int epo_combine_tokens(int S, int T, int H, int K, int E, int R, int Nmax, int expand,
+                       const int64_t *topk_idx, const float *topk_weights,
+                       const int32_t *dst_slot, const int32_t *recv_psum,
+                       const int32_t *recv_base, const int32_t *expand_pos,
+                       const uint16_t *y, int n_sel, const int64_t *sel, uint16_t *out);
+
 /* Round a double to bf16 bits, nearest with ties to even (exposed for pins). */
 uint16_t epo_bf16_from_double(double v);
 
