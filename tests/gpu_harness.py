@@ -20,7 +20,7 @@ def say(msg: str) -> None:
 
 def upload(w, inputs: Dict[str, np.ndarray], device="cuda"):
     d = dict(
-        x=torch.from_numpy(inputs["x"].reshape(w.S * w.T, -1)).to(device),
+        x=torch.from_numpy(inputs["x"].reshape(w.S * w.T, inputs["x"].shape[-1])).to(device),
         topk_idx=torch.from_numpy(inputs["topk_idx"]).to(device),
         topk_weights=torch.from_numpy(inputs["topk_weights"]).to(device),
         x_sf=torch.from_numpy(inputs["x_sf"]).to(device) if w.dtype == "fp8" else None,
