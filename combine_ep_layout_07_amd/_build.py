@@ -25,10 +25,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-ta
          "-I", CSRC]
 
 
-def _compile(src: str) -> str:
-    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, obj_dir: str = OBJ, defines=()) -> str:
+    out = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC] + FLAGS + [f"-D{d}" for d in defines] + lang + ["-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -39,17 +39,18 @@ def _compile(src: str) -> str:
     return out
 
 
-def build_library() -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build_library(lib: str = LIB, obj_dir: str = OBJ, defines=()) -> str:
+    """Compile and link; ``defines`` (NAME=VALUE) override the kernels' tuning constants."""
+    os.makedirs(obj_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, obj_dir, defines), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "--hip-link", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -3,16 +3,18 @@
 // kernels for transports without ordered delivery" (PR #732), section
 // Changes).
 //
-// out[s][t] = bf16(sum over valid lanes k, ascending, of w[s][t][k] * Y),
-// accumulated in fp32 with fused multiply-adds and rounded to nearest-even
-// once.  In the compact layout Y is the receive row that the owner lane of the
-// lane's rank was given (recv_base[d] + recv_psum[d][s] + slot - s*Nmax), so
-// lanes sharing a rank weight the same row; in the expand layout Y is the
-// lane's own row expand_pos[s][t][k].
+// out[s][t] = bf16(sum over valid lanes k of w[s][t][k] * Y), accumulated in
+// fp32 and rounded to nearest-even once.  In the compact layout Y is the
+// receive row that the owner lane of the lane's rank was given
+// (recv_base[d] + recv_psum[d][s] + slot - s*Nmax), so lanes sharing a rank
+// weight the same row: the kernel reads that row once and applies the fp32
+// sum of those lanes' weights (taken in lane order).  In the expand layout Y
+// is the lane's own row expand_pos[s][t][k].
 //
 // The work is an HBM stream with about one FMA per 2 bytes read, far below
-// the MFMA ridge, so it runs on the vector ALUs: one wavefront per token,
-// 16-byte loads of 8 bf16 per lane, two expert rows in flight per step.
+// the MFMA ridge, so it runs on the vector ALUs: one wavefront per token; per
+// pass every lane loads CPL 16-byte chunks (8 bf16) of each of up to G
+// distinct rows before any FMA, so G*CPL loads per lane are in flight.
 #include "ep_device.h"
 #include "ep_kernels.h"
 
@@ -21,8 +23,31 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
+#ifndef EP_COMBINE_ROWS
+#define EP_COMBINE_ROWS 8  // G: distinct rows loaded together
+#endif
+#ifndef EP_COMBINE_CPL
+#define EP_COMBINE_CPL 2  // 16-byte chunks per lane per row per pass
+#endif
+#ifndef EP_COMBINE_NT_LOAD
+#define EP_COMBINE_NT_LOAD 1  // each expert-output row is read once
+#endif
+#ifndef EP_COMBINE_NT_STORE
+#define EP_COMBINE_NT_STORE 0
+#endif
+#ifndef EP_COMBINE_TOKENS_PER_WAVE
+#define EP_COMBINE_TOKENS_PER_WAVE 1  // consecutive tokens one wave reduces in turn
+#endif
+constexpr int kRowsPerGroup = EP_COMBINE_ROWS;
 
-__device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ u32x4 ld16(const uint16_t *p) {
+    const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+#if EP_COMBINE_NT_LOAD
+    return __builtin_nontemporal_load(q);
+#else
+    return *q;
+#endif
+}
 
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -31,7 +56,7 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 
 template <int CPL>
-__device__ __forceinline__ void fma_rows(float (&acc)[CPL][8], const u32x4 (&v)[CPL], float w) {
+__device__ __forceinline__ void fma_row(float (&acc)[CPL][8], const u32x4 (&v)[CPL], float w) {
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
 #pragma unroll
@@ -45,13 +70,16 @@ __device__ __forceinline__ void fma_rows(float (&acc)[CPL][8], const u32x4 (&v)[
 
 template <int CPL>
 __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
+    constexpr int G = kRowsPerGroup;
     const Shape &sh = a.sh;
     const int lane = lane_id();
     const int64_t n_tok = (int64_t)sh.S * sh.T;
     const int nchunks = sh.H / 8;  // 16-byte chunks of a bf16 row
+    constexpr int TPW = EP_COMBINE_TOKENS_PER_WAVE;
     const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t g = wave0; g < n_tok; g += nwaves) {
+    for (int64_t gi = wave0 * TPW; gi < n_tok; gi += nwaves * TPW)
+    for (int64_t g = gi; g < gi + TPW && g < n_tok; ++g) {
         const int s = (int)(g / sh.T);
         bool valid = false;
         float w = 0.0f;
@@ -65,20 +93,30 @@ __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
             else slot = a.dst_slot[g * sh.K + lane];
         }
         const uint64_t vmask = ballot(valid);
+        // Distinct rows, one per "row lane": every valid lane in the expand
+        // layout; the owner (lowest valid lane) of each rank otherwise, whose
+        // weight becomes the lane-ordered fp32 sum over the lanes of its rank.
         int row = -1;
+        float wrow = 0.0f;
         if (sh.expand) {
             row = valid ? pos : -1;
+            wrow = w;
         } else {
-            // The owner of a rank is its lowest valid lane; its slot names the row.
             const int d = valid ? e / sh.El : 0;
             const uint64_t peers = match_key((uint32_t)d, sh.bits_R, vmask);
             const int owner = peers ? __builtin_ctzll(peers) : 0;
-            const int owner_slot = shfl(slot, owner);
-            if (valid) row = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s] + (owner_slot - s * sh.Nmax);
+            const bool is_owner = valid && owner == lane;
+            if (is_owner) row = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s] + (slot - s * sh.Nmax);
+            for (uint64_t m = vmask; m; m &= m - 1) {
+                const int k = __builtin_ctzll(m);
+                const float wk = __int_as_float(read_lane(__float_as_int(w), k));
+                const int ok = read_lane(owner, k);
+                if (lane == ok) wrow += wk;
+            }
         }
         // Rows outside y never occur for a layout of this topk_idx; drop them.
-        const uint64_t use = vmask & ballot(row >= 0 && (int64_t)row < a.y_rows);
-        const int wbits = __float_as_int(w);
+        const uint64_t rows_mask = ballot(row >= 0 && (int64_t)row < a.y_rows);
+        const int wbits = __float_as_int(wrow);
         uint16_t *out = a.out + g * sh.H;
         for (int c0 = 0; c0 < nchunks; c0 += CPL * kWave) {
             float acc[CPL][8];
@@ -86,37 +124,38 @@ __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
             for (int i = 0; i < CPL; ++i)
 #pragma unroll
                 for (int q = 0; q < 8; ++q) acc[i][q] = 0.0f;
-            uint64_t m = use;
-            while (m) {
-                const int k0 = __builtin_ctzll(m);
-                m &= m - 1;
-                const int r0 = read_lane(row, k0);
-                const float w0 = __int_as_float(read_lane(wbits, k0));
-                const uint16_t *y0 = a.y + (int64_t)r0 * sh.H;
-                u32x4 v0[CPL], v1[CPL];
+            for (uint64_t m = rows_mask; m;) {
+                // Up to G rows: issue every load, then the FMAs in row order.
+                int rr[G];
+                float ww[G];
+                int n = 0;
 #pragma unroll
-                for (int i = 0; i < CPL; ++i) {
-                    const int c = c0 + i * kWave + lane;
-                    if (c < nchunks) v0[i] = ld16(y0 + (int64_t)c * 8);
-                    else v0[i] = u32x4{0u, 0u, 0u, 0u};
-                }
-                if (m) {
-                    const int k1 = __builtin_ctzll(m);
-                    m &= m - 1;
-                    const int r1 = read_lane(row, k1);
-                    const float w1 = __int_as_float(read_lane(wbits, k1));
-                    const uint16_t *y1 = a.y + (int64_t)r1 * sh.H;
-#pragma unroll
-                    for (int i = 0; i < CPL; ++i) {
-                        const int c = c0 + i * kWave + lane;
-                        if (c < nchunks) v1[i] = ld16(y1 + (int64_t)c * 8);
-                        else v1[i] = u32x4{0u, 0u, 0u, 0u};
+                for (int j = 0; j < G; ++j) {
+                    rr[j] = -1;
+                    ww[j] = 0.0f;
+                    if (m) {
+                        const int k = __builtin_ctzll(m);
+                        m &= m - 1;
+                        rr[j] = read_lane(row, k);
+                        ww[j] = __int_as_float(read_lane(wbits, k));
+                        n = j + 1;
                     }
-                    fma_rows<CPL>(acc, v0, w0);
-                    fma_rows<CPL>(acc, v1, w1);
-                } else {
-                    fma_rows<CPL>(acc, v0, w0);
                 }
+                u32x4 v[G][CPL];
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    if (j < n) {
+                        const uint16_t *yr = a.y + (int64_t)rr[j] * sh.H;
+#pragma unroll
+                        for (int i = 0; i < CPL; ++i) {
+                            const int c = c0 + i * kWave + lane;
+                            v[j][i] = c < nchunks ? ld16(yr + (int64_t)c * 8) : u32x4{0u, 0u, 0u, 0u};
+                        }
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < G; ++j)
+                    if (j < n) fma_row<CPL>(acc, v[j], ww[j]);
             }
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
@@ -125,7 +164,12 @@ __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
                     u32x4 o;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) o[q] = bf16_rne(acc[i][2 * q]) | (bf16_rne(acc[i][2 * q + 1]) << 16);
-                    *reinterpret_cast<u32x4 *>(out + (int64_t)c * 8) = o;
+                    u32x4 *dst = reinterpret_cast<u32x4 *>(out + (int64_t)c * 8);
+#if EP_COMBINE_NT_STORE
+                    __builtin_nontemporal_store(o, dst);
+#else
+                    *dst = o;
+#endif
                 }
             }
         }
@@ -135,8 +179,9 @@ __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
 template <int CPL>
 hipError_t run(const CombineArgs &a, hipStream_t st) {
     const int64_t n_tok = (int64_t)a.sh.S * a.sh.T;
-    int64_t blocks = (n_tok + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (blocks > 2048) blocks = 2048;
+    const int64_t per_block = (int64_t)kWavesPerBlock * EP_COMBINE_TOKENS_PER_WAVE;
+    int64_t blocks = (n_tok + per_block - 1) / per_block;
+    if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(k_combine<CPL>, dim3((int)blocks), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
@@ -146,12 +191,9 @@ hipError_t run(const CombineArgs &a, hipStream_t st) {
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream) {
     if ((int64_t)a.sh.S * a.sh.T == 0) return hipSuccess;
     const int need = (a.sh.H / 8 + kWave - 1) / kWave;  // chunks per lane for the whole row
-    // At most 8 chunks (64 fp32 accumulators) per lane per pass.
+    // Two chunks per lane per pass keeps G*CPL*4 = 64 VGPRs of loads in flight.
     if (need <= 1) return run<1>(a, stream);
-    if (need <= 2) return run<2>(a, stream);
-    if (need <= 4) return run<4>(a, stream);
-    if (need <= 7 || need == 14) return run<7>(a, stream);
-    return run<8>(a, stream);
+    return run<EP_COMBINE_CPL>(a, stream);
 }
 
 }  // namespace ep

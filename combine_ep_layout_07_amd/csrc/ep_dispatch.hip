@@ -22,8 +22,40 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
 
-__device__ __forceinline__ u32x4 ld16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
-__device__ __forceinline__ void st16(uint8_t *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+// Cache hints of the streamed rows (1 = non-temporal: the row is touched once
+// by this kernel and not again soon).  Measured on MI355X at T=4096, H=7168:
+// non-temporal loads and stores in the copy epilogue keep its 770 MB stream
+// from leaving dirty or useless lines in L2 and the Infinity Cache, which
+// speeds up both the epilogue and the combine that follows; non-temporal
+// staging stores in the scatter slow the scatter down more than they help.
+#ifndef EP_SCATTER_NT_LOAD
+#define EP_SCATTER_NT_LOAD 0
+#endif
+#ifndef EP_SCATTER_NT_STORE
+#define EP_SCATTER_NT_STORE 0
+#endif
+#ifndef EP_EPILOGUE_NT_LOAD
+#define EP_EPILOGUE_NT_LOAD 1
+#endif
+#ifndef EP_EPILOGUE_NT_STORE
+#define EP_EPILOGUE_NT_STORE 1
+#endif
+#ifndef EP_COPY_BLOCKS
+#define EP_COPY_BLOCKS 2048
+#endif
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const uint8_t *p) {
+    const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+    if constexpr (NT) return __builtin_nontemporal_load(q);
+    else return *q;
+}
+template <bool NT>
+__device__ __forceinline__ void st16(uint8_t *p, u32x4 v) {
+    u32x4 *q = reinterpret_cast<u32x4 *>(p);
+    if constexpr (NT) __builtin_nontemporal_store(v, q);
+    else *q = v;
+}
 
 // ----------------------------------------------------------------- scatter
 // One wave per token (s, t): load the row once, store it to the staging row
@@ -53,7 +85,7 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const int c = c0 + i * kWave + lane;
-                if (c < nchunks) v[i] = ld16(src + (int64_t)c * 16);
+                if (c < nchunks) v[i] = ld16<EP_SCATTER_NT_LOAD>(src + (int64_t)c * 16);
             }
             for (uint64_t m = owners; m; m &= m - 1) {
                 const int k = __builtin_ctzll(m);
@@ -64,7 +96,7 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
                     const int c = c0 + i * kWave + lane;
-                    if (c < nchunks) st16(dst + (int64_t)c * 16, v[i]);
+                    if (c < nchunks) st16<EP_SCATTER_NT_STORE>(dst + (int64_t)c * 16, v[i]);
                 }
             }
         }
@@ -92,24 +124,25 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
 }
 
 // Which (destination, source, row) a compact receive row i comes from:
-// d = last d with recv_base[d] <= i, s = last s with recv_psum[d][s] <= i - base.
+// d = last d with recv_base[d] <= i, s = last s with recv_psum[d][s] <= i -
+// recv_base[d], j the rest.  Both tables are non-decreasing, so each index is
+// the count of entries <= the key minus one: one ballot per 64 entries.
 __device__ __forceinline__ void locate_row(const int32_t *recv_base, const int32_t *recv_psum, int R, int S,
-                                           int i, int &d, int &s, int &j) {
-    int lo = 0, hi = R;  // invariant: recv_base[lo] <= i < recv_base[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (recv_base[mid] <= i) lo = mid; else hi = mid;
+                                           int i, int lane, int &d, int &s, int &j) {
+    int cnt = 0;
+    for (int l0 = 0; l0 < R; l0 += kWave) {
+        const int l = l0 + lane;
+        cnt += popc(ballot(l < R && recv_base[l] <= i));
     }
-    d = lo;
+    d = cnt - 1;
     const int off = i - recv_base[d];
     const int32_t *ps = recv_psum + (int64_t)d * (S + 1);
-    lo = 0;
-    hi = S;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (ps[mid] <= off) lo = mid; else hi = mid;
+    cnt = 0;
+    for (int l0 = 0; l0 < S; l0 += kWave) {
+        const int l = l0 + lane;
+        cnt += popc(ballot(l < S && ps[l] <= off));
     }
-    s = lo;
+    s = cnt - 1;
     j = off - ps[s];
 }
 
@@ -139,7 +172,7 @@ __global__ void __launch_bounds__(kThreads) k_epilogue(DispatchArgs a, int table
     const int nwaves = gridDim.x * kWavesPerBlock;
     for (int i = wave0; i < n_rows; i += nwaves) {
         int d, s, j;
-        locate_row(rbase, rpsum, sh.R, sh.S, i, d, s, j);
+        locate_row(rbase, rpsum, sh.R, sh.S, i, lane, d, s, j);
         if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for tables of one layout
         const int64_t row = ((int64_t)d * sh.S + s) * sh.Nmax + j;
         const uint8_t *src = a.staging_x + row * sh.row_bytes;
@@ -149,12 +182,12 @@ __global__ void __launch_bounds__(kThreads) k_epilogue(DispatchArgs a, int table
 #pragma unroll
             for (int q = 0; q < CPL; ++q) {
                 const int c = c0 + q * kWave + lane;
-                if (c < nchunks) v[q] = ld16(src + (int64_t)c * 16);
+                if (c < nchunks) v[q] = ld16<EP_EPILOGUE_NT_LOAD>(src + (int64_t)c * 16);
             }
 #pragma unroll
             for (int q = 0; q < CPL; ++q) {
                 const int c = c0 + q * kWave + lane;
-                if (c < nchunks) st16(dst + (int64_t)c * 16, v[q]);
+                if (c < nchunks) st16<EP_EPILOGUE_NT_STORE>(dst + (int64_t)c * 16, v[q]);
             }
         }
         for (int q = lane; q < sh.sf_per_row; q += kWave)
@@ -189,7 +222,7 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_expand(DispatchArgs a, in
     const int nwaves = gridDim.x * kWavesPerBlock;
     for (int i = wave0; i < n_rows; i += nwaves) {
         int d, s, j;
-        locate_row(rbase, rpsum, sh.R, sh.S, i, d, s, j);
+        locate_row(rbase, rpsum, sh.R, sh.S, i, lane, d, s, j);
         if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for tables of one layout
         const int64_t row = ((int64_t)d * sh.S + s) * sh.Nmax + j;
         const int32_t *meta = a.staging_meta + row * sh.meta_words;
@@ -209,7 +242,7 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_expand(DispatchArgs a, in
 #pragma unroll
             for (int q = 0; q < CPL; ++q) {
                 const int c = c0 + q * kWave + lane;
-                if (c < nchunks) v[q] = ld16(src + (int64_t)c * 16);
+                if (c < nchunks) v[q] = ld16<EP_EPILOGUE_NT_LOAD>(src + (int64_t)c * 16);
             }
             for (uint64_t m = lanes_on_d; m; m &= m - 1) {
                 const int r = read_lane(pos, __builtin_ctzll(m));
@@ -218,7 +251,7 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_expand(DispatchArgs a, in
 #pragma unroll
                 for (int q = 0; q < CPL; ++q) {
                     const int c = c0 + q * kWave + lane;
-                    if (c < nchunks) st16(dst + (int64_t)c * 16, v[q]);
+                    if (c < nchunks) st16<EP_EPILOGUE_NT_STORE>(dst + (int64_t)c * 16, v[q]);
                 }
             }
         }
@@ -249,7 +282,7 @@ __global__ void __launch_bounds__(kThreads) k_expand_padding(DispatchArgs a) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     for (int r = r0; r < r1; ++r) {
         uint8_t *dst = a.recv_x + (int64_t)r * sh.row_bytes;
-        for (int c = threadIdx.x; c < nchunks; c += kThreads) st16(dst + (int64_t)c * 16, zero);
+        for (int c = threadIdx.x; c < nchunks; c += kThreads) st16<false>(dst + (int64_t)c * 16, zero);
         for (int q = threadIdx.x; q < sh.sf_per_row; q += kThreads) a.recv_sf[(int64_t)r * sh.sf_per_row + q] = 0.0f;
         if (threadIdx.x == 0) {
             a.recv_src_idx[r] = -1;
@@ -274,7 +307,7 @@ hipError_t dispatch_cpl(int need, Args &&...args) {
 int grid_for(int64_t work_waves) {
     // Enough waves to fill 256 CUs several times over; extra work is strided.
     int64_t blocks = (work_waves + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (blocks > 2048) blocks = 2048;
+    if (blocks > EP_COPY_BLOCKS) blocks = EP_COPY_BLOCKS;
     if (blocks < 1) blocks = 1;
     return (int)blocks;
 }

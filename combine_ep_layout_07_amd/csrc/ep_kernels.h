@@ -38,6 +38,7 @@ struct LayoutArgs {
     int32_t *blk_cnt_rank;    // scratch [S*B][R]
     int32_t *blk_cnt_expert;  // scratch [S*B][E]
     int32_t *blk_flags;       // scratch [S*B]
+    int32_t *blk_base_expert; // scratch [S*B][E], expand only
 };
 
 struct DispatchArgs {

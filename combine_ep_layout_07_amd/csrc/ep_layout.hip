@@ -11,19 +11,23 @@
 // Design on CDNA4.  Work is cut into "units" of consecutive tokens of one
 // source: one workgroup of 4 wavefronts per unit, each wave owning a quarter.
 // A wave walks its tokens in steps of floor(64/K) tokens, one (token, lane)
-// item per SIMD lane, items in (t, k) order.  Equal destinations (or experts)
-// inside a step are found with one ballot per key bit; the exclusive rank of
-// an item among equal keys is a masked popcount (mbcnt), and the highest lane
-// of each key group advances a per-wave running counter in LDS.  Nothing is
-// decided by atomics, so the result never depends on scheduling.
+// item per SIMD lane, items in (t, k) order; the items of up to kBatch steps
+// are loaded with one batch of independent loads, so a wave pays about one
+// memory latency per pass.  Equal destinations (or experts) inside a step are
+// found with one ballot per key bit; the exclusive rank of an item among equal
+// keys is a masked popcount (mbcnt), and the highest lane of each key group
+// advances a per-wave running counter in LDS.  Nothing is decided by atomics
+// on memory, so the result never depends on scheduling.
 //
-//   pass 1 (k_layout_count): per-unit counts of owner lanes per destination
-//     and of valid lanes per expert, plus an invalid-id flag, into scratch;
-//   pass 2 (k_layout_slot): each unit reduces the counts of the units before
-//     it (its exclusive base), recounts per wave for the wave bases, then
-//     ranks every item and writes dst_slot (and expand_pos); the first unit
-//     of each source writes that source's counts, unit (0,0) the receiver
-//     tables (recv_psum, recv_base, expert_base, error_flags).
+//   k_layout_count: per-unit counts of owner lanes per destination and of
+//     valid lanes per expert, plus an invalid-id flag, into scratch;
+//   k_layout_expert_scan (expand only): per-expert segment bases (padded to
+//     A) and each unit's first row in every expert segment;
+//   k_layout_slot: each unit reduces the counts of the earlier units of its
+//     source (its base per destination), recounts per wave for the wave
+//     bases, then ranks every item and writes dst_slot (and expand_pos); the
+//     units also share out the per-source counts, and unit (0,0) writes the
+//     receiver tables (recv_psum, recv_base, error_flags).
 #include "ep_device.h"
 #include "ep_kernels.h"
 
@@ -31,14 +35,26 @@ namespace ep {
 
 constexpr int kLayoutThreads = 256;
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
+constexpr int kBatch = 8;  // steps whose items a wave loads together
+constexpr int kScanThreads = 1024;
 
 LayoutGeom layout_geometry(const Shape &sh, int num_layout_cus) {
     LayoutGeom g;
     const int T = sh.T;
-    int B = num_layout_cus > 0 ? (num_layout_cus + sh.S - 1) / sh.S : (T + 255) / 256;
-    const int max_b = T > 4 ? (T + 3) / 4 : 1;  // at least 4 tokens (one per wave) per unit
-    if (B < 1) B = 1;
+    const int tps = kWave / sh.K;                  // tokens per step
+    const int min_chunk = 2 * kLayoutWaves * tps;  // two steps per wave
+    const int max_b = T > 4 ? (T + 3) / 4 : 1;     // at least one token per wave
+    int B;
+    if (num_layout_cus > 0) {
+        B = (num_layout_cus + sh.S - 1) / sh.S;
+    } else {
+        const int target_units = sh.expand ? 128 : 256;
+        const int by_size = (T + min_chunk - 1) / min_chunk;
+        const int by_units = (target_units + sh.S - 1) / sh.S;
+        B = by_size < by_units ? by_size : by_units;
+    }
     if (B > max_b) B = max_b;
+    if (B < 1) B = 1;
     int chunk = T > 0 ? (T + B - 1) / B : 4;
     chunk = (chunk + 3) / 4 * 4;
     B = T > 0 ? (T + chunk - 1) / chunk : 1;
@@ -49,7 +65,7 @@ LayoutGeom layout_geometry(const Shape &sh, int num_layout_cus) {
 
 uint64_t layout_scratch_bytes(const Shape &sh, const LayoutGeom &g) {
     const uint64_t units = (uint64_t)sh.S * g.blocks_per_src;
-    return units * (uint64_t)(sh.R + sh.E + 1) * sizeof(int32_t);
+    return units * (uint64_t)(sh.R + sh.E + 1 + (sh.expand ? sh.E : 0)) * sizeof(int32_t);
 }
 
 namespace {
@@ -67,9 +83,9 @@ struct Item {
 
 struct StepCtx {
     int lane, l_tok, l_k;
-    bool used;          // lane holds an item slot in every step (l < tps*K)
-    uint64_t seg;       // lanes of the same token
-    int tps;            // tokens per step
+    bool used;     // lane holds an item slot in every step (l < tps*K)
+    uint64_t seg;  // lanes of the same token
+    int tps;       // tokens per step
 };
 
 __device__ __forceinline__ StepCtx make_ctx(int K) {
@@ -84,13 +100,23 @@ __device__ __forceinline__ StepCtx make_ctx(int K) {
     return c;
 }
 
-__device__ __forceinline__ Item load_item(const Shape &sh, const int64_t *topk_src, int t_step, int t_end,
-                                          const StepCtx &c, bool need_e) {
+// Load the expert ids of `n` consecutive steps starting at token ts (ids of
+// lanes without an item are returned as -1; n <= kBatch).
+__device__ __forceinline__ void load_batch(const Shape &sh, const int64_t *topk_src, int ts, int t_end,
+                                           const StepCtx &c, int64_t (&buf)[kBatch]) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+        const int t = ts + i * c.tps + c.l_tok;
+        buf[i] = (c.used && t < t_end) ? topk_src[(int64_t)t * sh.K + c.l_k] : (int64_t)-1;
+    }
+}
+
+__device__ __forceinline__ Item make_item(const Shape &sh, int64_t e64, int t_step, int t_end, const StepCtx &c,
+                                          bool need_e) {
     Item it;
     it.t = t_step + c.l_tok;
     it.k = c.l_k;
     it.in = c.used && it.t < t_end;
-    const int64_t e64 = it.in ? __builtin_nontemporal_load(topk_src + (int64_t)it.t * sh.K + c.l_k) : -1;
     it.invalid = it.in && e64 >= sh.E;
     it.valid = it.in && e64 >= 0 && e64 < sh.E;
     it.e = it.valid ? (int)e64 : 0;
@@ -114,38 +140,56 @@ __device__ __forceinline__ Item load_item(const Shape &sh, const int64_t *topk_s
     return it;
 }
 
+__device__ __forceinline__ void count_item(const Item &it, int *cnt_d, int *cnt_e, bool need_e, bool &bad) {
+    if (it.last_d) cnt_d[it.d] += it.cnt_d;
+    if (need_e && it.last_e) cnt_e[it.e] += it.cnt_e;
+    bad |= it.invalid;
+}
+
 // Count owner lanes per destination (and valid lanes per expert) over tokens
 // [t0, t1) of one source into this wave's LDS rows; returns the invalid flag.
+// When the range fits one batch, the ids stay in `buf` for the ranking pass.
 __device__ bool wave_count(const Shape &sh, const int64_t *topk_src, int t0, int t1, int *cnt_d, int *cnt_e,
-                           bool need_e) {
-    const StepCtx c = make_ctx(sh.K);
+                           bool need_e, const StepCtx &c, int64_t (&buf)[kBatch], bool single) {
     bool bad = false;
-    for (int ts = t0; ts < t1; ts += c.tps) {
-        const Item it = load_item(sh, topk_src, ts, t1, c, need_e);
-        if (it.last_d) cnt_d[it.d] += it.cnt_d;
-        if (need_e && it.last_e) cnt_e[it.e] += it.cnt_e;
-        bad |= it.invalid;
+    if (single) {
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int ts = t0 + i * c.tps;
+            if (ts < t1) count_item(make_item(sh, buf[i], ts, t1, c, need_e), cnt_d, cnt_e, need_e, bad);
+        }
+    } else {
+        for (int tb = t0; tb < t1; tb += kBatch * c.tps) {
+            int64_t b2[kBatch];
+            load_batch(sh, topk_src, tb, t1, c, b2);
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const int ts = tb + i * c.tps;
+                if (ts < t1) count_item(make_item(sh, b2[i], ts, t1, c, need_e), cnt_d, cnt_e, need_e, bad);
+            }
+        }
     }
     return ballot(bad) != 0;
 }
 
 // Exclusive scan of a[0..n) in LDS by the whole workgroup; returns the total.
+template <int NT>
 __device__ int block_exclusive_scan(int *a, int n, int *part) {
     const int tid = threadIdx.x;
-    const int per = (n + kLayoutThreads - 1) / kLayoutThreads;
+    const int per = (n + NT - 1) / NT;
     const int lo = min(tid * per, n), hi = min(lo + per, n);
     int sum = 0;
     for (int i = lo; i < hi; ++i) sum += a[i];
     part[tid] = sum;
     __syncthreads();
-    for (int off = 1; off < kLayoutThreads; off <<= 1) {
+    for (int off = 1; off < NT; off <<= 1) {
         const int v = tid >= off ? part[tid - off] : 0;
         __syncthreads();
         part[tid] += v;
         __syncthreads();
     }
     int run = part[tid] - sum;
-    const int total = part[kLayoutThreads - 1];
+    const int total = part[NT - 1];
     for (int i = lo; i < hi; ++i) {
         const int v = a[i];
         a[i] = run;
@@ -155,21 +199,32 @@ __device__ int block_exclusive_scan(int *a, int n, int *part) {
     return total;
 }
 
+__device__ __forceinline__ void wave_range(const LayoutArgs &a, int b, int w, int &t0, int &t1) {
+    const int cw = a.g.chunk / kLayoutWaves;
+    t0 = min(b * a.g.chunk + w * cw, a.sh.T);
+    t1 = min(t0 + cw, a.sh.T);
+}
+
 __global__ void __launch_bounds__(kLayoutThreads) k_layout_count(LayoutArgs a) {
     const Shape &sh = a.sh;
     const int b = blockIdx.x, s = blockIdx.y, B = a.g.blocks_per_src;
     const int w = threadIdx.x / kWave, tid = threadIdx.x;
     extern __shared__ int lds[];
-    int *cnt_d = lds;                               // [4][R]
-    int *cnt_e = cnt_d + kLayoutWaves * sh.R;       // [4][E]
-    int *flag = cnt_e + kLayoutWaves * sh.E;        // [4]
+    int *cnt_d = lds;                          // [4][R]
+    int *cnt_e = cnt_d + kLayoutWaves * sh.R;  // [4][E]
+    int *flag = cnt_e + kLayoutWaves * sh.E;   // [4]
+
+    int t0, t1;
+    wave_range(a, b, w, t0, t1);
+    const StepCtx c = make_ctx(sh.K);
+    const bool single = t1 - t0 <= kBatch * c.tps;
+    const int64_t *topk_src = a.topk_idx + (int64_t)s * sh.T * sh.K;
+    int64_t buf[kBatch];
+    if (single) load_batch(sh, topk_src, t0, t1, c, buf);  // in flight while LDS is cleared
     for (int i = tid; i < kLayoutWaves * (sh.R + sh.E); i += kLayoutThreads) lds[i] = 0;
     __syncthreads();
 
-    const int cw = a.g.chunk / kLayoutWaves;
-    const int t0 = min(b * a.g.chunk + w * cw, sh.T), t1 = min(t0 + cw, sh.T);
-    const int64_t *topk_src = a.topk_idx + (int64_t)s * sh.T * sh.K;
-    const bool bad = wave_count(sh, topk_src, t0, t1, cnt_d + w * sh.R, cnt_e + w * sh.E, true);
+    const bool bad = wave_count(sh, topk_src, t0, t1, cnt_d + w * sh.R, cnt_e + w * sh.E, true, c, buf, single);
     if (lane_id() == 0) flag[w] = bad ? 1 : 0;
     __syncthreads();
 
@@ -187,6 +242,46 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_count(LayoutArgs a) {
     if (tid == 0) a.blk_flags[u] = flag[0] | flag[1] | flag[2] | flag[3];
 }
 
+// Expand layout only.  One workgroup: thread (seg, e) owns expert column e
+// over a contiguous segment of units.  Writes expert_base [E+1] (segments of
+// the valid-lane counts, padded to A) and blk_base_expert[u][e], the first row
+// of unit u inside expert e's segment (units in (s, t) order).
+__global__ void __launch_bounds__(kScanThreads) k_layout_expert_scan(LayoutArgs a) {
+    const Shape &sh = a.sh;
+    const int E = sh.E, tid = threadIdx.x;
+    const int64_t U = (int64_t)sh.S * a.g.blocks_per_src;
+    const int nseg = kScanThreads / E;  // E <= 1024
+    const int e = tid % E, seg = tid / E;
+    const bool active = seg < nseg;
+    const int64_t u0 = active ? U * seg / nseg : 0, u1 = active ? U * (seg + 1) / nseg : 0;
+    extern __shared__ int lds[];
+    int *part = lds;                     // [nseg][E]
+    int *base = part + nseg * E;         // [E+1]
+    int *scan_part = base + E + 1;       // [kScanThreads]
+    int sum = 0;
+    for (int64_t u = u0; u < u1; ++u) sum += a.blk_cnt_expert[u * E + e];
+    if (active) part[seg * E + e] = sum;
+    __syncthreads();
+    if (tid < E) {
+        int tot = 0;
+        for (int q = 0; q < nseg; ++q) tot += part[q * E + tid];
+        base[tid] = (tot + sh.A - 1) / sh.A * sh.A;
+    }
+    __syncthreads();
+    const int total = block_exclusive_scan<kScanThreads>(base, E, scan_part);
+    if (tid == 0) base[E] = total;
+    __syncthreads();
+    for (int i = tid; i <= E; i += kScanThreads) a.expert_base[i] = base[i];
+    if (active) {
+        int run = base[e];
+        for (int q = 0; q < seg; ++q) run += part[q * E + e];
+        for (int64_t u = u0; u < u1; ++u) {
+            a.blk_base_expert[u * E + e] = run;
+            run += a.blk_cnt_expert[u * E + e];
+        }
+    }
+}
+
 __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
     const Shape &sh = a.sh;
     const int b = blockIdx.x, s = blockIdx.y, B = a.g.blocks_per_src;
@@ -196,46 +291,46 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
     const int64_t U = (int64_t)S * B, me = (int64_t)s * B + b;
 
     extern __shared__ int lds[];
-    int *cnt_d = lds;                          // [4][R] per-wave counts, then running bases
-    int *cnt_e = cnt_d + kLayoutWaves * R;     // [4][E]
-    int *base_d = cnt_e + kLayoutWaves * E;    // [R]   this unit's base per destination
-    int *base_e = base_d + R;                  // [E+1] expert_base, then this unit's base per expert
-    int *part = base_e + E + 1;                // [256] scan workspace
-    for (int i = tid; i < kLayoutWaves * (R + E); i += kLayoutThreads) lds[i] = 0;
+    int *cnt_d = lds;                       // [4][R] per-wave counts, then running bases
+    int *cnt_e = cnt_d + kLayoutWaves * R;  // [4][E]
+    int *base_d = cnt_e + kLayoutWaves * E; // [R]   this unit's base per destination
+    int *base_e = base_d + R;               // [E]   expand: this unit's first row per expert
+    int *col = base_e + E;                  // [R+E] per-source totals of this unit's share of columns
+    int *part = col + R + E;                // [256] scratch for unit (0,0)
 
+    int t0, t1;
+    wave_range(a, b, w, t0, t1);
+    const StepCtx c = make_ctx(sh.K);
+    const bool single = t1 - t0 <= kBatch * c.tps;
+    const int64_t *topk_src = a.topk_idx + (int64_t)s * sh.T * sh.K;
+    int64_t buf[kBatch];
+    if (single) load_batch(sh, topk_src, t0, t1, c, buf);
+
+    for (int i = tid; i < kLayoutWaves * (R + E) + R + E + (R + E); i += kLayoutThreads) lds[i] = 0;
+    __syncthreads();
     // Unit base per destination: what the earlier units of this source send there.
-    for (int d = tid; d < R; d += kLayoutThreads) {
-        int v = 0;
-        for (int q = 0; q < b; ++q) v += a.blk_cnt_rank[((int64_t)s * B + q) * R + d];
-        base_d[d] = v;
-    }
-    if (expand) {
-        // Expert segments ([E+1] bases, padded to A) and this unit's offset in
-        // each: the valid lanes of every unit before it in (s, t) order.
-        for (int e = tid; e < E; e += kLayoutThreads) {
-            int tot = 0;
-            for (int64_t q = 0; q < U; ++q) tot += a.blk_cnt_expert[q * E + e];
-            base_e[e] = (tot + sh.A - 1) / sh.A * sh.A;
-        }
-        __syncthreads();
-        const int total = block_exclusive_scan(base_e, E, part);
-        if (tid == 0) base_e[E] = total;
-        __syncthreads();
-        if (me == 0)
-            for (int e = tid; e <= E; e += kLayoutThreads) a.expert_base[e] = base_e[e];
-        for (int e = tid; e < E; e += kLayoutThreads) {
-            int pre = 0;
-            for (int64_t q = 0; q < me; ++q) pre += a.blk_cnt_expert[q * E + e];
-            base_e[e] += pre;
-        }
+    for (int i = tid; i < b * R; i += kLayoutThreads)
+        atomicAdd(&base_d[i % R], a.blk_cnt_rank[((int64_t)s * B) * R + i]);
+    if (expand)
+        for (int e = tid; e < E; e += kLayoutThreads) base_e[e] = a.blk_base_expert[me * E + e];
+    // This unit's share of the per-source totals: columns c = b, b+B, ...
+    // (destinations first, then experts), each summed over the source's units.
+    const int ncol = b < R + E ? (R + E - b + B - 1) / B : 0;
+    for (int i = tid; i < ncol * B; i += kLayoutThreads) {
+        const int j = i / B, q = i - j * B;
+        const int cidx = b + j * B;
+        const int v = cidx < R ? a.blk_cnt_rank[((int64_t)s * B + q) * R + cidx]
+                               : a.blk_cnt_expert[((int64_t)s * B + q) * E + (cidx - R)];
+        atomicAdd(&col[cidx], v);
     }
     __syncthreads();
+    for (int cidx = b + tid * B; cidx < R + E; cidx += kLayoutThreads * B) {
+        if (cidx < R) a.tokens_per_rank[(int64_t)s * R + cidx] = col[cidx];
+        else a.tokens_per_expert[(int64_t)s * E + cidx - R] = col[cidx];
+    }
 
     // Per-wave counts of this unit, then each wave's running base.
-    const int cw = a.g.chunk / kLayoutWaves;
-    const int t0 = min(b * a.g.chunk + w * cw, sh.T), t1 = min(t0 + cw, sh.T);
-    const int64_t *topk_src = a.topk_idx + (int64_t)s * sh.T * sh.K;
-    wave_count(sh, topk_src, t0, t1, cnt_d + w * R, cnt_e + w * E, expand);
+    wave_count(sh, topk_src, t0, t1, cnt_d + w * R, cnt_e + w * E, expand, c, buf, single);
     __syncthreads();
     for (int d = tid; d < R; d += kLayoutThreads) {
         int run = base_d[d];
@@ -259,12 +354,10 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
 
     // Ranking: every item of the wave's range gets its slot / expand row.
     {
-        const StepCtx c = make_ctx(sh.K);
         int *run_d = cnt_d + w * R;
         int *run_e = cnt_e + w * E;
         const int32_t row_base = s * sh.Nmax;  // direct path: one Nmax-row region per source
-        for (int ts = t0; ts < t1; ts += c.tps) {
-            const Item it = load_item(sh, topk_src, ts, t1, c, expand);
+        auto rank = [&](const Item &it) {
             const int rd = it.owner ? run_d[it.d] : 0;
             const int re = (expand && it.valid) ? run_e[it.e] : 0;
             if (it.in) {
@@ -274,26 +367,29 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
             }
             if (it.last_d) run_d[it.d] = rd + it.rank_d + 1;
             if (expand && it.last_e) run_e[it.e] = re + it.rank_e + 1;
+        };
+        if (single) {
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const int ts = t0 + i * c.tps;
+                if (ts < t1) rank(make_item(sh, buf[i], ts, t1, c, expand));
+            }
+        } else {
+            for (int tb = t0; tb < t1; tb += kBatch * c.tps) {
+                int64_t b2[kBatch];
+                load_batch(sh, topk_src, tb, t1, c, b2);
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) {
+                    const int ts = tb + i * c.tps;
+                    if (ts < t1) rank(make_item(sh, b2[i], ts, t1, c, expand));
+                }
+            }
         }
     }
 
-    // Per-source counts (first unit of each source).
-    if (b == 0) {
-        for (int d = tid; d < R; d += kLayoutThreads) {
-            int v = 0;
-            for (int q = 0; q < B; ++q) v += a.blk_cnt_rank[((int64_t)s * B + q) * R + d];
-            a.tokens_per_rank[(int64_t)s * R + d] = v;
-        }
-        for (int e = tid; e < E; e += kLayoutThreads) {
-            int v = 0;
-            for (int q = 0; q < B; ++q) v += a.blk_cnt_expert[((int64_t)s * B + q) * E + e];
-            a.tokens_per_expert[(int64_t)s * E + e] = v;
-        }
-    }
     // Receiver tables (unit 0 only): recv_psum, recv_base, error flags.
     if (me == 0) {
-        __syncthreads();
-        int *tot_d = part;  // reuse: [R] totals per destination (R <= 64 < 256)
+        int *tot_d = part;  // [R] totals per destination (R <= 64)
         for (int d = tid; d < R; d += kLayoutThreads) {
             int run = 0;
             for (int q = 0; q < S; ++q) {
@@ -316,17 +412,21 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
             a.recv_base[R] = run;
         }
         __syncthreads();
-        if (lane_id() == 0) part[w] = bad;
+        if (lane_id() == 0) part[64 + w] = bad;
         __syncthreads();
-        if (tid == 0) a.error_flags[0] = (part[0] | part[1] | part[2] | part[3]) ? 1 : 0;
+        if (tid == 0) a.error_flags[0] = (part[64] | part[65] | part[66] | part[67]) ? 1 : 0;
     }
 }
 
 size_t count_lds_bytes(const Shape &sh) {
     return sizeof(int) * ((size_t)kLayoutWaves * (sh.R + sh.E) + kLayoutWaves);
 }
+size_t scan_lds_bytes(const Shape &sh) {
+    const int nseg = kScanThreads / sh.E;
+    return sizeof(int) * ((size_t)nseg * sh.E + sh.E + 1 + kScanThreads);
+}
 size_t slot_lds_bytes(const Shape &sh) {
-    return sizeof(int) * ((size_t)kLayoutWaves * (sh.R + sh.E) + sh.R + sh.E + 1 + kLayoutThreads);
+    return sizeof(int) * ((size_t)kLayoutWaves * (sh.R + sh.E) + sh.R + sh.E + (sh.R + sh.E) + kLayoutThreads);
 }
 
 }  // namespace
@@ -336,6 +436,11 @@ hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(k_layout_count, grid, dim3(kLayoutThreads), count_lds_bytes(a.sh), stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (a.sh.expand) {
+        hipLaunchKernelGGL(k_layout_expert_scan, dim3(1), dim3(kScanThreads), scan_lds_bytes(a.sh), stream, a);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
     hipLaunchKernelGGL(k_layout_slot, grid, dim3(kLayoutThreads), slot_lds_bytes(a.sh), stream, a);
     return hipGetLastError();
 }

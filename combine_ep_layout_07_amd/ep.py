@@ -19,7 +19,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libep.so")
+# EP_LIBRARY selects another build of the same library (e.g. one compiled with
+# different tuning constants); the default is the in-tree build.
+LIB_PATH = os.environ.get("EP_LIBRARY") or os.path.join(_HERE, "libep.so")
 
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_CAPACITY, EP_ERR_UNSUPPORTED, EP_ERR_HIP = 0, -1, -2, -3, -4
 EP_DTYPE_BF16, EP_DTYPE_FP8_E4M3FN = 0, 1
