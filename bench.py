@@ -77,8 +77,9 @@ def read_traffic(per_launch_alg: float):
         return None
 
 
-def cpu_baseline(w, inputs, n_rows, v_rows, passes=2):
-    """The oracle as it stands, single-threaded, on the same workload."""
+def cpu_baseline(w, inputs, n_rows, v_rows, max_passes=30, budget_s=12.0):
+    """The oracle as it stands, single-threaded, on the same workload: whole
+    passes (layout + dispatch + combine) until about budget_s of CPU time."""
     import numpy as np
     import oracle
     from combine_ep_layout_07_amd.workloads import draw_expert_outputs
@@ -87,7 +88,7 @@ def cpu_baseline(w, inputs, n_rows, v_rows, passes=2):
     times = []
     rows = n_rows if not w.expand else v_rows
     y = draw_expert_outputs(rows, w.H, 99)
-    for _ in range(passes):
+    while len(times) < max_passes and (len(times) < 3 or sum(times) < budget_s):
         t0 = time.perf_counter()
         lay = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment)
         disp = oracle.dispatch(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.dtype == "fp8", w.expand, w.alignment,
@@ -100,8 +101,84 @@ def cpu_baseline(w, inputs, n_rows, v_rows, passes=2):
     b = alg_bytes(w, n_rows, v_rows)["total"]
     return {"value": round(b / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"full {w.name} workload (S={w.S} T={w.T} H={w.H} K={w.K}), layout+dispatch+combine, "
-                      f"median of {passes} passes of {t:.2f} s, single thread",
+                      f"median of {len(times)} passes of {t:.2f} s, single thread",
             "seconds_per_step": round(t, 3), "tokens_per_s": round(w.S * w.T / t, 1)}
+
+
+COPY_CAL_BYTES = 256 * 2**20
+
+
+def copy_calibration(reps=5):
+    """A plain device-to-device copy of COPY_CAL_BYTES, the reference the HBM
+    byte counters are scaled by (it reads and writes exactly that many bytes)."""
+    import torch
+    src = torch.ones(COPY_CAL_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _counter_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, out_md: str, command: str) -> None:
+    """Turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) into the traffic summary read by read_traffic()."""
+    import numpy as np
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in _counter_rows(path):
+            if r.get("Counter_Name") != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return acc
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(acc, key, largest=False):
+        vals = [v for k, vs in acc.items() if key in k for v in vs]
+        if not vals:
+            return float("nan")
+        return float(max(vals)) if largest else float(np.median(vals))
+
+    # The calibration copy (torch's device-to-device copy runs the runtime's
+    # copyBuffer kernel) is the largest copy dispatch of the run.
+    cf, cw = pick(fetch, "copyBuffer", True), pick(write, "copyBuffer", True)
+    ef, ew = pick(fetch, "k_epilogue"), pick(write, "k_epilogue")
+    # counters are KiB per dispatch; a copy of COPY_CAL_BYTES must read and write that many bytes
+    f_scale = COPY_CAL_BYTES / (cf * 1024.0)
+    w_scale = COPY_CAL_BYTES / (cw * 1024.0)
+    traffic = ef * 1024.0 * f_scale + ew * 1024.0 * w_scale
+    lines = [
+        "# Copy-epilogue HBM traffic (dsv3_share: T=4096 H=7168 bf16 K=8 E=256 R=16)",
+        "",
+        "Counters from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE), KiB per dispatch, median over",
+        "dispatches; scaled by what the same counters read for a plain device copy of 256 MiB.",
+        "",
+        "command: " + command,
+        "",
+        f"copy_fetch_kib_per_dispatch: {cf:.1f}",
+        f"copy_write_kib_per_dispatch: {cw:.1f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"epilogue_fetch_kib_per_dispatch: {ef:.1f}",
+        f"epilogue_write_kib_per_dispatch: {ew:.1f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        f"kernel_source_sha256_16: {source_digest(EPILOGUE_SOURCES)}",
+        "",
+        "Other kernels (median KiB per dispatch, fetch / write):",
+    ]
+    for k in sorted(set(fetch) | set(write)):
+        if "ep::" in k or "copy" in k:
+            lines.append(f"- {k[:90]}: {np.median(fetch.get(k, [np.nan])):.1f} / {np.median(write.get(k, [np.nan])):.1f}")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main():
@@ -111,7 +188,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (the reference for the byte counters)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
+                    help="write the traffic summary from two rocprofv3 --pmc CSVs and exit (no GPU use)")
+    ap.add_argument("--command", default="", help="profiling command recorded in the summary")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, command=args.command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs one GPU's share only (--gpus {args.gpus}, WORLD_SIZE {world}): the ranks of this "
@@ -218,6 +303,8 @@ def main():
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(epi_gbps / PEAK_HBM_GBPS, 4),
                      "alg_bytes_per_launch": epi_alg, "traffic": traffic},
     }
+    if args.copy_calibration:
+        copy_calibration()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, inputs, n_rows, v_rows)
