@@ -12,9 +12,11 @@
 // is the lane's own row expand_pos[s][t][k].
 //
 // The work is an HBM stream with about one FMA per 2 bytes read, far below
-// the MFMA ridge, so it runs on the vector ALUs: one wavefront per token; per
-// pass every lane loads CPL 16-byte chunks (8 bf16) of each of up to G
-// distinct rows before any FMA, so G*CPL loads per lane are in flight.
+// the MFMA ridge, so it runs on the vector ALUs.  A work unit is one column
+// slice of one token (by default one pass: 64 lanes x CPL 16-byte chunks);
+// every lane loads its chunks of each of up to G distinct rows before any
+// FMA, so G*CPL loads per lane are in flight.  Many small units balance the
+// uneven number of rows per token across the resident waves.
 #include "ep_device.h"
 #include "ep_kernels.h"
 
@@ -35,8 +37,10 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #ifndef EP_COMBINE_NT_STORE
 #define EP_COMBINE_NT_STORE 0
 #endif
-#ifndef EP_COMBINE_TOKENS_PER_WAVE
-#define EP_COMBINE_TOKENS_PER_WAVE 1  // consecutive tokens one wave reduces in turn
+#ifndef EP_COMBINE_SLICES
+// Column slices of a token's row, each a separate work unit; 0 = one pass
+// (64 lanes x CPL chunks) per unit, measured best on MI355X at H = 7168.
+#define EP_COMBINE_SLICES 0
 #endif
 constexpr int kRowsPerGroup = EP_COMBINE_ROWS;
 
@@ -75,11 +79,20 @@ __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
     const int lane = lane_id();
     const int64_t n_tok = (int64_t)sh.S * sh.T;
     const int nchunks = sh.H / 8;  // 16-byte chunks of a bf16 row
-    constexpr int TPW = EP_COMBINE_TOKENS_PER_WAVE;
+    // Work unit = (token, column slice); slices of one token are adjacent so
+    // neighbouring waves read neighbouring pieces of the same rows.  More
+    // units than resident waves lets early finishers pick up new work instead
+    // of idling behind tokens with many rows.
+    const int slices = a.slices;
+    const int cps = ((nchunks + slices - 1) / slices + kWave - 1) / kWave * kWave;  // chunks per slice
+    const int64_t n_units = n_tok * slices;
     const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t gi = wave0 * TPW; gi < n_tok; gi += nwaves * TPW)
-    for (int64_t g = gi; g < gi + TPW && g < n_tok; ++g) {
+    for (int64_t unit = wave0; unit < n_units; unit += nwaves) {
+        const int64_t g = unit / slices;
+        const int c_lo = (int)(unit - g * slices) * cps;
+        const int c_hi = min(c_lo + cps, nchunks);
+        if (c_lo >= c_hi) continue;
         const int s = (int)(g / sh.T);
         bool valid = false;
         float w = 0.0f;
@@ -118,7 +131,7 @@ __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
         const uint64_t rows_mask = ballot(row >= 0 && (int64_t)row < a.y_rows);
         const int wbits = __float_as_int(wrow);
         uint16_t *out = a.out + g * sh.H;
-        for (int c0 = 0; c0 < nchunks; c0 += CPL * kWave) {
+        for (int c0 = c_lo; c0 < c_hi; c0 += CPL * kWave) {
             float acc[CPL][8];
 #pragma unroll
             for (int i = 0; i < CPL; ++i)
@@ -149,7 +162,7 @@ __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
 #pragma unroll
                         for (int i = 0; i < CPL; ++i) {
                             const int c = c0 + i * kWave + lane;
-                            v[j][i] = c < nchunks ? ld16(yr + (int64_t)c * 8) : u32x4{0u, 0u, 0u, 0u};
+                            v[j][i] = c < c_hi ? ld16(yr + (int64_t)c * 8) : u32x4{0u, 0u, 0u, 0u};
                         }
                     }
                 }
@@ -160,7 +173,7 @@ __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const int c = c0 + i * kWave + lane;
-                if (c < nchunks) {
+                if (c < c_hi) {
                     u32x4 o;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) o[q] = bf16_rne(acc[i][2 * q]) | (bf16_rne(acc[i][2 * q + 1]) << 16);
@@ -178,18 +191,23 @@ __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
 
 template <int CPL>
 hipError_t run(const CombineArgs &a, hipStream_t st) {
-    const int64_t n_tok = (int64_t)a.sh.S * a.sh.T;
-    const int64_t per_block = (int64_t)kWavesPerBlock * EP_COMBINE_TOKENS_PER_WAVE;
-    int64_t blocks = (n_tok + per_block - 1) / per_block;
-    if (blocks > 4096) blocks = 4096;
+    const int64_t units = (int64_t)a.sh.S * a.sh.T * a.slices;
+    int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (blocks > 16384) blocks = 16384;
     hipLaunchKernelGGL(k_combine<CPL>, dim3((int)blocks), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_combine(const CombineArgs &a, hipStream_t stream) {
-    if ((int64_t)a.sh.S * a.sh.T == 0) return hipSuccess;
+hipError_t launch_combine(const CombineArgs &args, hipStream_t stream) {
+    if ((int64_t)args.sh.S * args.sh.T == 0) return hipSuccess;
+    CombineArgs a = args;
+    const int nchunks = a.sh.H / 8;
+    const int cpl = (nchunks + kWave - 1) / kWave <= 1 ? 1 : EP_COMBINE_CPL;
+    a.slices = EP_COMBINE_SLICES > 0 ? EP_COMBINE_SLICES : (nchunks + cpl * kWave - 1) / (cpl * kWave);
+    if (a.slices > (nchunks + kWave - 1) / kWave) a.slices = (nchunks + kWave - 1) / kWave;
+    if (a.slices < 1) a.slices = 1;
     const int need = (a.sh.H / 8 + kWave - 1) / kWave;  // chunks per lane for the whole row
     // Two chunks per lane per pass keeps G*CPL*4 = 64 VGPRs of loads in flight.
     if (need <= 1) return run<1>(a, stream);

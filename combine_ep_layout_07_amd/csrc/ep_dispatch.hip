@@ -40,6 +40,9 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #ifndef EP_EPILOGUE_NT_STORE
 #define EP_EPILOGUE_NT_STORE 1
 #endif
+#ifndef EP_SCATTER_SLICES
+#define EP_SCATTER_SLICES 1  // column slices of a token's row, each a separate work unit
+#endif
 #ifndef EP_COPY_BLOCKS
 #define EP_COPY_BLOCKS 2048
 #endif
@@ -67,9 +70,17 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
     const int lane = lane_id();
     const int64_t n_tok = (int64_t)sh.S * sh.T;
     const int nchunks = sh.row_bytes / 16;
+    // Work unit = (token, column slice of its row); slice 0 also writes the
+    // scales and the metadata.
+    const int slices = a.slices;
+    const int cps = ((nchunks + slices - 1) / slices + kWave - 1) / kWave * kWave;  // chunks per slice
+    const int64_t n_units = n_tok * slices;
     const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t g = wave0; g < n_tok; g += nwaves) {
+    for (int64_t unit = wave0; unit < n_units; unit += nwaves) {
+        const int64_t g = unit / slices;
+        const int slice = (int)(unit - g * slices);
+        const int c_lo = slice * cps, c_hi = min(c_lo + cps, nchunks);
         const int s = (int)(g / sh.T), t = (int)(g - (int64_t)s * sh.T);
         int e = -1, slot = -1, wbits = 0;
         if (lane < sh.K) {
@@ -80,12 +91,12 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
         }
         const uint64_t owners = ballot(lane < sh.K && slot >= 0);
         const uint8_t *src = a.x + g * sh.row_bytes;
-        for (int c0 = 0; c0 < nchunks; c0 += CPL * kWave) {
+        for (int c0 = c_lo; c0 < c_hi; c0 += CPL * kWave) {
             u32x4 v[CPL];
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const int c = c0 + i * kWave + lane;
-                if (c < nchunks) v[i] = ld16<EP_SCATTER_NT_LOAD>(src + (int64_t)c * 16);
+                if (c < c_hi) v[i] = ld16<EP_SCATTER_NT_LOAD>(src + (int64_t)c * 16);
             }
             for (uint64_t m = owners; m; m &= m - 1) {
                 const int k = __builtin_ctzll(m);
@@ -96,10 +107,11 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
                     const int c = c0 + i * kWave + lane;
-                    if (c < nchunks) st16<EP_SCATTER_NT_STORE>(dst + (int64_t)c * 16, v[i]);
+                    if (c < c_hi) st16<EP_SCATTER_NT_STORE>(dst + (int64_t)c * 16, v[i]);
                 }
             }
         }
+        if (slice != 0) continue;
         // Metadata words i = lane and i = lane + 64 (K = 32 needs 65 words):
         // word 0 = t, words 1..K = expert ids, words K+1..2K = weight bits.
         // Shuffled with every lane active, before any divergent store.
@@ -291,7 +303,14 @@ __global__ void __launch_bounds__(kThreads) k_expand_padding(DispatchArgs a) {
     }
 }
 
-int chunks_per_lane(const Shape &sh) { return (sh.row_bytes / 16 + kWave - 1) / kWave; }
+int chunks_per_lane(const Shape &sh) {
+    const int nchunks = sh.row_bytes / 16;
+    int slices = EP_SCATTER_SLICES < 1 ? 1 : EP_SCATTER_SLICES;
+    if (slices > (nchunks + kWave - 1) / kWave) slices = (nchunks + kWave - 1) / kWave;
+    const int cps = ((nchunks + slices - 1) / slices + kWave - 1) / kWave * kWave;
+    return cps / kWave;
+}
+int epilogue_chunks_per_lane(const Shape &sh) { return (sh.row_bytes / 16 + kWave - 1) / kWave; }
 
 template <template <int> class Launcher, typename... Args>
 hipError_t dispatch_cpl(int need, Args &&...args) {
@@ -314,9 +333,13 @@ int grid_for(int64_t work_waves) {
 
 template <int CPL>
 struct ScatterL {
-    static hipError_t run(const DispatchArgs &a, hipStream_t st) {
-        const int64_t n_tok = (int64_t)a.sh.S * a.sh.T;
-        hipLaunchKernelGGL(k_scatter<CPL>, dim3(grid_for(n_tok)), dim3(kThreads), 0, st, a);
+    static hipError_t run(const DispatchArgs &args, hipStream_t st) {
+        DispatchArgs a = args;
+        const int nchunks = a.sh.row_bytes / 16;
+        a.slices = EP_SCATTER_SLICES < 1 ? 1 : EP_SCATTER_SLICES;
+        if (a.slices > (nchunks + kWave - 1) / kWave) a.slices = (nchunks + kWave - 1) / kWave;
+        const int64_t units = (int64_t)a.sh.S * a.sh.T * a.slices;
+        hipLaunchKernelGGL(k_scatter<CPL>, dim3(grid_for(units)), dim3(kThreads), 0, st, a);
         return hipGetLastError();
     }
 };
@@ -347,7 +370,7 @@ hipError_t launch_scatter(const DispatchArgs &a, hipStream_t stream) {
 
 hipError_t launch_epilogue(const DispatchArgs &a, hipStream_t stream) {
     hipError_t err = hipSuccess;
-    if ((int64_t)a.sh.S * a.sh.T > 0) err = dispatch_cpl<EpilogueL>(chunks_per_lane(a.sh), a, stream);
+    if ((int64_t)a.sh.S * a.sh.T > 0) err = dispatch_cpl<EpilogueL>(epilogue_chunks_per_lane(a.sh), a, stream);
     if (err != hipSuccess) return err;
     if (a.sh.expand && a.sh.A > 1) {
         hipLaunchKernelGGL(k_expand_padding, dim3(a.sh.E), dim3(kThreads), 0, stream, a);

@@ -56,6 +56,7 @@ struct DispatchArgs {
     int32_t *recv_src_idx, *recv_topk_idx;
     float *recv_topk_weights;
     int64_t recv_capacity_rows;
+    int slices;  // scatter: column slices per token (set by the launcher)
 };
 
 struct CombineArgs {
@@ -66,6 +67,7 @@ struct CombineArgs {
     const uint16_t *y;
     uint16_t *out;
     int64_t y_rows;  // rows of y (the receive capacity)
+    int slices;      // column slices per token (set by the launcher)
 };
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream);

@@ -387,14 +387,33 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
         }
     }
 
-    // Receiver tables (unit 0 only): recv_psum, recv_base, error flags.
+    // Receiver tables (unit 0 only): recv_psum, recv_base, error flags.  The
+    // per-(source, destination) totals are reduced with every thread (LDS
+    // integer adds), then prefixed over sources and destinations.
     if (me == 0) {
+        __syncthreads();
+        int *tot = cnt_d;  // reuse the (finished) per-wave rows: [S][R] if it fits, else global loads per d
+        const bool fits = (int64_t)S * R <= (int64_t)kLayoutWaves * (R + E);
+        if (fits) {
+            for (int i = tid; i < S * R; i += kLayoutThreads) tot[i] = 0;
+            __syncthreads();
+            for (int64_t i = tid; i < U * R; i += kLayoutThreads) {
+                const int64_t uu = i / R;
+                const int d = (int)(i - uu * R);
+                atomicAdd(&tot[(uu / B) * R + d], a.blk_cnt_rank[i]);
+            }
+            __syncthreads();
+        }
         int *tot_d = part;  // [R] totals per destination (R <= 64)
         for (int d = tid; d < R; d += kLayoutThreads) {
             int run = 0;
             for (int q = 0; q < S; ++q) {
                 a.recv_psum[(int64_t)d * (S + 1) + q] = run;
-                for (int bb = 0; bb < B; ++bb) run += a.blk_cnt_rank[((int64_t)q * B + bb) * R + d];
+                if (fits) {
+                    run += tot[q * R + d];
+                } else {
+                    for (int bb = 0; bb < B; ++bb) run += a.blk_cnt_rank[((int64_t)q * B + bb) * R + d];
+                }
             }
             a.recv_psum[(int64_t)d * (S + 1) + S] = run;
             tot_d[d] = run;
