@@ -31,11 +31,13 @@ EPILOGUE_SOURCES = [os.path.join(ROOT, "combine_ep_layout_07_amd", "csrc", f)
                     for f in ("ep_dispatch.hip", "ep_device.h", "ep_kernels.h")]
 
 
-def alg_bytes(w, n_rows: int, v_rows: int) -> dict:
+def alg_bytes(w, n_rows: int, v_rows: int, direct: bool = False) -> dict:
     """Algorithmic bytes per stage: each mandatory input read and output write once.
 
     Rw row bytes, F scale bytes per row, M = 4(1+2K) staging metadata bytes,
-    Y = 2H expert-output row bytes; N deduplicated rows, V valid lanes."""
+    Y = 2H expert-output row bytes; N deduplicated rows, V valid lanes.  With
+    Direct Recv X the scatter writes the hidden rows to recv_x (same bytes) and
+    the epilogue moves only scales and metadata."""
     S, T, K, H = w.S, w.T, w.K, w.H
     Rw = H if w.dtype == "fp8" else 2 * H
     F = (H // 128) * 4 if w.dtype == "fp8" else 0
@@ -44,7 +46,10 @@ def alg_bytes(w, n_rows: int, v_rows: int) -> dict:
     lanes = S * T * K
     layout = lanes * (8 + 4) + (lanes * 4 if w.expand else 0)
     scatter = S * T * (Rw + F) + lanes * 16 + n_rows * (Rw + F + M)
-    epilogue = n_rows * (Rw + F + M) + (v_rows * (Rw + F + 8) if w.expand else n_rows * (Rw + F + 4 + 8 * K))
+    if direct:
+        epilogue = n_rows * (F + M) + n_rows * (F + 4 + 8 * K)
+    else:
+        epilogue = n_rows * (Rw + F + M) + (v_rows * (Rw + F + 8) if w.expand else n_rows * (Rw + F + 4 + 8 * K))
     combine = lanes * 16 + (v_rows if w.expand else n_rows) * Y + S * T * Y
     return dict(layout=layout, scatter=scatter, epilogue=epilogue, combine=combine,
                 total=layout + scatter + epilogue + combine)
@@ -188,6 +193,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-direct", action="store_true", help="skip the Direct Recv X variant")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (the reference for the byte counters)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
@@ -226,52 +232,53 @@ def main():
     out = torch.empty((w.S * w.T, w.H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(phased=False, ev=None):
+    def step(c, recv, phased=False, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        ep.ep_layout(cfg, topk, L, stream)
+        ep.ep_layout(c, topk, L, stream)
         if ev is not None:
             ev[1].record(stream)
         if phased:
-            ep.ep_dispatch(cfg, x, x_sf, topk, wts, L, R, ep.EP_PHASE_SCATTER, stream)
+            ep.ep_dispatch(c, x, x_sf, topk, wts, L, recv, ep.EP_PHASE_SCATTER, stream)
             if ev is not None:
                 ev[2].record(stream)
-            ep.ep_dispatch(cfg, x, x_sf, topk, wts, L, R, ep.EP_PHASE_EPILOGUE, stream)
+            ep.ep_dispatch(c, x, x_sf, topk, wts, L, recv, ep.EP_PHASE_EPILOGUE, stream)
         else:
-            ep.ep_dispatch(cfg, x, x_sf, topk, wts, L, R, ep.EP_PHASE_ALL, stream)
+            ep.ep_dispatch(c, x, x_sf, topk, wts, L, recv, ep.EP_PHASE_ALL, stream)
         if ev is not None:
             ev[3].record(stream)
-        ep.ep_combine(cfg, L, topk, wts, y, out, stream)
+        ep.ep_combine(c, L, topk, wts, y, out, stream)
         if ev is not None:
             ev[4].record(stream)
 
-    print(f"[bench] {w.name}: warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    names = ["layout", "scatter", "epilogue", "combine"]
+
+    def measure(c, recv):
+        """K back-to-back steps between two events (synchronised on both sides),
+        then the same steps again with an event between stages."""
+        for _ in range(args.warmup):
+            step(c, recv)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            step(c, recv)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(c, recv, phased=True, ev=evs[i])
+        torch.cuda.synchronize()
+        stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+        return ms, stage_ms
+
+    print(f"[bench] {w.name}: warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
+    ms, stage_ms = measure(cfg, R)
     n_rows = int(L.recv_base[-1].item())
     v_rows = int(((topk >= 0) & (topk < w.E)).sum().item())
     b = alg_bytes(w, n_rows, v_rows)
-
-    # Headline: K back-to-back steps between two events, synchronised on both sides.
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
-
-    # Per-stage durations: the same steps with an event between stages.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(phased=True, ev=evs[i])
-    torch.cuda.synchronize()
-    names = ["layout", "scatter", "epilogue", "combine"]
-    stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
 
     value = b["total"] / (ms * 1e-3) / 1e9
     epi_alg = b["epilogue"]
@@ -303,6 +310,20 @@ def main():
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(epi_gbps / PEAK_HBM_GBPS, 4),
                      "alg_bytes_per_launch": epi_alg, "traffic": traffic},
     }
+    if not w.expand and not args.no_direct:
+        # Direct Recv X (the scatter writes hidden rows straight into recv_x):
+        # a different byte count, reported beside the headline, never as it.
+        cfg_d = ep.config_for(w, direct_recv_x=True)
+        del R
+        R_d = ep.alloc_recv(cfg_d, dev)
+        print("[bench] direct recv_x variant", file=sys.stderr, flush=True)
+        ms_d, stage_d = measure(cfg_d, R_d)
+        bd = alg_bytes(w, n_rows, v_rows, direct=True)
+        res["direct_recv_x"] = {
+            "value": round(bd["total"] / (ms_d * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "ms_per_step": round(ms_d, 5), "tokens_per_s": round(w.S * w.T / (ms_d * 1e-3), 1),
+            "alg_bytes_per_step": bd, "stage_us": {k: round(v * 1e3, 2) for k, v in stage_d.items()},
+            "speedup_vs_staging": round(ms / ms_d, 3)}
     if args.copy_calibration:
         copy_calibration()
     if not args.no_cpu_baseline:

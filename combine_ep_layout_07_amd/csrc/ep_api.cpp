@@ -26,7 +26,8 @@ int bits_for(int n) {
 // Validate a configuration and derive the kernel shape.
 int make_shape(const ep_config_t *c, ep::Shape *sh) {
     if (!c || !sh) return EP_ERR_INVALID_ARG;
-    if (c->reserved != 0) return EP_ERR_INVALID_ARG;
+    if ((c->flags & ~EP_FLAG_DIRECT_RECV_X) != 0) return EP_ERR_INVALID_ARG;
+    if ((c->flags & EP_FLAG_DIRECT_RECV_X) && c->expand) return EP_ERR_UNSUPPORTED;
     if (c->num_src_ranks < 1 || c->num_tokens < 0 || c->hidden < 1 || c->num_topk < 1 || c->num_experts < 1 ||
         c->num_ranks < 1 || c->num_max_tokens_per_rank < 0 || c->num_layout_cus < 0 || c->expert_alignment < 1)
         return EP_ERR_INVALID_ARG;
@@ -59,6 +60,7 @@ int make_shape(const ep_config_t *c, ep::Shape *sh) {
     sh->meta_words = 1 + 2 * c->num_topk;
     sh->bits_R = bits_for(c->num_ranks);
     sh->bits_E = bits_for(c->num_experts);
+    sh->direct = (c->flags & EP_FLAG_DIRECT_RECV_X) ? 1 : 0;
     return EP_OK;
 }
 
@@ -119,7 +121,7 @@ int ep_query_sizes(const ep_config_t *cfg, ep_sizes_t *sz) {
     sz->error_flags = i4;
     sz->layout_scratch = ep::layout_scratch_bytes(sh, ep::layout_geometry(sh, cfg->num_layout_cus));
     const uint64_t staging_rows = R * S * Nmax;
-    sz->staging_x = staging_rows * (uint64_t)sh.row_bytes;
+    sz->staging_x = sh.direct ? 0 : staging_rows * (uint64_t)sh.row_bytes;
     sz->staging_sf = staging_rows * (uint64_t)sh.sf_per_row * sizeof(float);
     sz->staging_meta = staging_rows * (uint64_t)sh.meta_words * i4;
     const uint64_t rows = (uint64_t)recv_rows(sh);
@@ -173,7 +175,7 @@ int ep_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev
         if (!x_dev || !aligned(x_dev, 16) || !topk_idx_dev || !aligned(topk_idx_dev, 8) || !topk_weights_dev ||
             !aligned(topk_weights_dev, 4))
             return EP_ERR_INVALID_ARG;
-        if (!recv->staging_x_dev || !aligned(recv->staging_x_dev, 16) || !recv->staging_meta_dev ||
+        if ((!sh.direct && (!recv->staging_x_dev || !aligned(recv->staging_x_dev, 16))) || !recv->staging_meta_dev ||
             !aligned(recv->staging_meta_dev, 4) || !recv->recv_x_dev || !aligned(recv->recv_x_dev, 16) ||
             !recv->recv_src_idx_dev || !aligned(recv->recv_src_idx_dev, 4) || !recv->recv_topk_weights_dev ||
             !aligned(recv->recv_topk_weights_dev, 4))

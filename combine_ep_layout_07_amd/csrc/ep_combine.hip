@@ -35,7 +35,7 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #define EP_COMBINE_NT_LOAD 1  // each expert-output row is read once
 #endif
 #ifndef EP_COMBINE_NT_STORE
-#define EP_COMBINE_NT_STORE 0
+#define EP_COMBINE_NT_STORE 1  // each output row is written once
 #endif
 #ifndef EP_COMBINE_SLICES
 // Column slices of a token's row, each a separate work unit; 0 = one pass

@@ -34,6 +34,9 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #ifndef EP_SCATTER_NT_STORE
 #define EP_SCATTER_NT_STORE 0
 #endif
+#ifndef EP_DIRECT_NT_STORE
+#define EP_DIRECT_NT_STORE 1  // Direct Recv X rows: written once, read by the next stage at the earliest
+#endif
 #ifndef EP_EPILOGUE_NT_LOAD
 #define EP_EPILOGUE_NT_LOAD 1
 #endif
@@ -90,6 +93,14 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
             wbits = __float_as_int(a.topk_weights[g * sh.K + lane]);
         }
         const uint64_t owners = ballot(lane < sh.K && slot >= 0);
+        // Direct Recv X: every owner lane fetches its destination's compact
+        // base recv_base[d] + recv_psum[d][s] at once (one gather, not a
+        // dependent scalar load per owner row).
+        int recv_row0 = 0;
+        if (sh.direct && lane < sh.K && slot >= 0) {
+            const int d = e / sh.El;
+            recv_row0 = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s];
+        }
         const uint8_t *src = a.x + g * sh.row_bytes;
         for (int c0 = c_lo; c0 < c_hi; c0 += CPL * kWave) {
             u32x4 v[CPL];
@@ -103,11 +114,23 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
                 const int d = read_lane(e, k) / sh.El;
                 const int j = read_lane(slot, k) - s * sh.Nmax;
                 if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for a layout of this topk_idx
-                uint8_t *dst = a.staging_x + (((int64_t)d * sh.S + s) * sh.Nmax + j) * sh.row_bytes;
+                if (sh.direct) {
+                    // Direct Recv X: the compact receive row of (d, s, j).
+                    const int64_t i = (int64_t)read_lane(recv_row0, k) + j;
+                    if (i >= a.recv_capacity_rows) continue;
+                    uint8_t *dst = a.recv_x + i * sh.row_bytes;
 #pragma unroll
-                for (int i = 0; i < CPL; ++i) {
-                    const int c = c0 + i * kWave + lane;
-                    if (c < c_hi) st16<EP_SCATTER_NT_STORE>(dst + (int64_t)c * 16, v[i]);
+                    for (int q = 0; q < CPL; ++q) {
+                        const int c = c0 + q * kWave + lane;
+                        if (c < c_hi) st16<EP_DIRECT_NT_STORE>(dst + (int64_t)c * 16, v[q]);
+                    }
+                } else {
+                    uint8_t *dst = a.staging_x + (((int64_t)d * sh.S + s) * sh.Nmax + j) * sh.row_bytes;
+#pragma unroll
+                    for (int q = 0; q < CPL; ++q) {
+                        const int c = c0 + q * kWave + lane;
+                        if (c < c_hi) st16<EP_SCATTER_NT_STORE>(dst + (int64_t)c * 16, v[q]);
+                    }
                 }
             }
         }
@@ -189,7 +212,8 @@ __global__ void __launch_bounds__(kThreads) k_epilogue(DispatchArgs a, int table
         const int64_t row = ((int64_t)d * sh.S + s) * sh.Nmax + j;
         const uint8_t *src = a.staging_x + row * sh.row_bytes;
         uint8_t *dst = a.recv_x + (int64_t)i * sh.row_bytes;
-        for (int c0 = 0; c0 < nchunks; c0 += CPL * kWave) {
+        // Direct Recv X: the scatter already wrote the hidden row in place.
+        for (int c0 = 0; c0 < (sh.direct ? 0 : nchunks); c0 += CPL * kWave) {
             u32x4 v[CPL];
 #pragma unroll
             for (int q = 0; q < CPL; ++q) {

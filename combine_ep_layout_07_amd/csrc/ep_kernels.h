@@ -17,6 +17,7 @@ struct Shape {
     int sf_per_row;  // fp32 scales per row (fp8), else 0
     int meta_words;  // 1 + 2K
     int bits_R, bits_E;  // key widths for ballot matching of ranks / experts
+    int direct;          // Direct Recv X: hidden rows go straight to recv_x
 };
 
 // Layout pass geometry: B workgroups per source, each owning `chunk` tokens

@@ -26,6 +26,7 @@ LIB_PATH = os.environ.get("EP_LIBRARY") or os.path.join(_HERE, "libep.so")
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_CAPACITY, EP_ERR_UNSUPPORTED, EP_ERR_HIP = 0, -1, -2, -3, -4
 EP_DTYPE_BF16, EP_DTYPE_FP8_E4M3FN = 0, 1
 EP_PHASE_SCATTER, EP_PHASE_EPILOGUE, EP_PHASE_ALL = 1, 2, 3
+EP_FLAG_DIRECT_RECV_X = 1
 
 
 class EpError(RuntimeError):
@@ -37,7 +38,7 @@ class EpError(RuntimeError):
 class EpConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_src_ranks", "num_tokens", "hidden", "num_topk", "num_experts", "num_ranks",
-        "num_max_tokens_per_rank", "x_dtype", "expand", "expert_alignment", "num_layout_cus", "reserved")]
+        "num_max_tokens_per_rank", "x_dtype", "expand", "expert_alignment", "num_layout_cus", "flags")]
 
 
 class EpSizes(ctypes.Structure):
@@ -89,14 +90,16 @@ def ep_version() -> int:
 
 
 def make_config(S: int, T: int, H: int, K: int, E: int, R: int, Nmax: int, dtype: str = "bf16",
-                expand: bool = False, alignment: int = 1, num_layout_cus: int = 0) -> EpConfig:
+                expand: bool = False, alignment: int = 1, num_layout_cus: int = 0,
+                direct_recv_x: bool = False) -> EpConfig:
     return EpConfig(S, T, H, K, E, R, Nmax, EP_DTYPE_FP8_E4M3FN if dtype == "fp8" else EP_DTYPE_BF16,
-                    int(bool(expand)), alignment, num_layout_cus, 0)
+                    int(bool(expand)), alignment, num_layout_cus, EP_FLAG_DIRECT_RECV_X if direct_recv_x else 0)
 
 
-def config_for(w, num_layout_cus: int = 0) -> EpConfig:
+def config_for(w, num_layout_cus: int = 0, direct_recv_x: bool = False) -> EpConfig:
     """EpConfig of a ``workloads.Workload``."""
-    return make_config(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.dtype, w.expand, w.alignment, num_layout_cus)
+    return make_config(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.dtype, w.expand, w.alignment, num_layout_cus,
+                       direct_recv_x)
 
 
 def ep_query_sizes(cfg: EpConfig) -> EpSizes:
@@ -178,7 +181,8 @@ class RecvBuffers:
         F = H // 128 if fp8 else 0
         rows = int(sz.recv_rows)
         self.rows = rows
-        self.staging_x = torch.empty((R, S, Nmax, rw), dtype=torch.uint8, device=device)
+        direct = bool(cfg.flags & EP_FLAG_DIRECT_RECV_X)
+        self.staging_x = None if direct else torch.empty((R, S, Nmax, rw), dtype=torch.uint8, device=device)
         self.staging_sf = torch.empty((R, S, Nmax, F), dtype=torch.float32, device=device) if fp8 else None
         self.staging_meta = torch.empty((R, S, Nmax, 1 + 2 * K), dtype=torch.int32, device=device)
         self.recv_x = torch.empty((rows, rw), dtype=torch.uint8, device=device)

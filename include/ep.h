@@ -66,6 +66,17 @@ enum ep_phase {
     EP_PHASE_ALL = 3
 };
 
+/* Option bits of ep_config_t.flags. */
+enum ep_flags {
+    /* Direct Recv X ([DRX] Direct Recv X design): the scatter writes each hidden
+     * row straight into its compact receive row recv_base[d] + recv_psum[d][s]
+     * + j instead of the staging row; staging keeps the scales and metadata,
+     * and the epilogue produces recv_sf and the metadata tensors but copies no
+     * hidden bytes.  staging_x is not used (may be NULL).  Compact layout only
+     * (EP_ERR_UNSUPPORTED with expand), as on the page. */
+    EP_FLAG_DIRECT_RECV_X = 1
+};
+
 /* Limits (checked on the host): 1 <= R <= 64, 1 <= K <= 32, E % R == 0,
  * E <= 1024, S * Nmax < 2^31, S * T * K < 2^31, H * element size a multiple of
  * 16 bytes, fp8 needs H % 128 == 0. */
@@ -92,7 +103,7 @@ typedef struct ep_config {
     int32_t num_layout_cus;           /* workgroups of the layout pass; 0 = auto
                                          (the pages' num_prologue_sms, [DET] New
                                          API); never changes any result          */
-    int32_t reserved;                 /* must be 0                               */
+    int32_t flags;                    /* enum ep_flags bits; others must be 0    */
 } ep_config_t;
 
 /* Byte sizes of every caller-allocated buffer for a configuration (0 = not

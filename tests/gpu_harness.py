@@ -28,8 +28,8 @@ def upload(w, inputs: Dict[str, np.ndarray], device="cuda"):
     return d
 
 
-def run_layout(w, dev, num_layout_cus=0):
-    cfg = ep.config_for(w, num_layout_cus)
+def run_layout(w, dev, num_layout_cus=0, direct=False):
+    cfg = ep.config_for(w, num_layout_cus, direct)
     L = ep.alloc_layout(cfg)
     ep.ep_layout(cfg, dev["topk_idx"], L)
     torch.cuda.synchronize()
@@ -56,12 +56,14 @@ def filled_staging_mask(w, lay) -> np.ndarray:
     return j < tpr.T[:, :, None]
 
 
-def compare_dispatch(w, lay, gpu: "ep.RecvBuffers", want: Dict[str, np.ndarray]):
-    """Bit-exact comparison of staging (filled rows) and receive buffers (filled rows)."""
+def compare_dispatch(w, lay, gpu: "ep.RecvBuffers", want: Dict[str, np.ndarray], direct: bool = False):
+    """Bit-exact comparison of staging (filled rows) and receive buffers (filled
+    rows).  With Direct Recv X the staging rows hold no hidden bytes."""
     mask = filled_staging_mask(w, lay)
-    sx = gpu.staging_x.cpu().numpy()
-    assert (sx[mask] == want["staging_x"][mask]).all(), "staging_x differs"
-    del sx
+    if not direct:
+        sx = gpu.staging_x.cpu().numpy()
+        assert (sx[mask] == want["staging_x"][mask]).all(), "staging_x differs"
+        del sx
     sm = gpu.staging_meta.cpu().numpy()
     assert (sm[mask] == want["staging_meta"][mask]).all(), "staging_meta differs"
     if w.dtype == "fp8":

@@ -87,10 +87,16 @@ def test_validation_codes(kw, code):
     assert ep.ep_status_string(code)
 
 
-def test_reserved_field_must_be_zero():
+def test_flags_validation():
     cfg = ep.make_config(1, 16, 64, 2, 8, 4, 16)
-    cfg.reserved = 1
+    cfg.flags = 2  # unknown option bit
     assert _rc(cfg) == ep.EP_ERR_INVALID_ARG
+    # Direct Recv X supports the compact layout only (as on the direct recv_x page)
+    assert _rc(ep.make_config(1, 16, 64, 2, 8, 4, 16, expand=True, direct_recv_x=True)) == ep.EP_ERR_UNSUPPORTED
+    d = ep.ep_query_sizes(ep.make_config(1, 4096, 7168, 8, 256, 16, 4096, direct_recv_x=True))
+    n = ep.ep_query_sizes(ep.make_config(1, 4096, 7168, 8, 256, 16, 4096))
+    assert d.staging_x == 0 and n.staging_x > 0
+    assert (d.staging_meta, d.recv_x, d.recv_rows) == (n.staging_meta, n.recv_x, n.recv_rows)
 
 
 def test_calls_reject_bad_arguments_before_any_launch():

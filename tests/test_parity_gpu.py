@@ -23,15 +23,15 @@ from tests.gpu_harness import (compare_combine, compare_dispatch, compare_tables
                                say, seeded_y, upload)
 
 
-def _full_case(w, seed, edge=None, num_layout_cus=0, check_combine=True, combine_sample=None):
+def _full_case(w, seed, edge=None, num_layout_cus=0, check_combine=True, combine_sample=None, direct=False):
     edge = edge or {}
     say(f"[case] {w.name} S={w.S} T={w.T} H={w.H} K={w.K} E={w.E} R={w.R} Nmax={w.Nmax} {w.dtype} "
-        f"expand={w.expand} A={w.alignment} seed={seed} edge={edge} cus={num_layout_cus}")
+        f"expand={w.expand} A={w.alignment} seed={seed} edge={edge} cus={num_layout_cus} direct={direct}")
     inputs = generate(w, seed, **edge)
     lay_o = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment)
     dev = upload(w, inputs)
     say("  ep_layout")
-    cfg, L = run_layout(w, dev, num_layout_cus)
+    cfg, L = run_layout(w, dev, num_layout_cus, direct)
     compare_tables(layout_host(L), lay_o)
     say("  ep_dispatch")
     R = ep.alloc_recv(cfg)
@@ -39,7 +39,7 @@ def _full_case(w, seed, edge=None, num_layout_cus=0, check_combine=True, combine
     torch.cuda.synchronize()
     want = oracle.dispatch(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.dtype == "fp8", w.expand, w.alignment,
                            inputs["x"], inputs.get("x_sf"), inputs["topk_idx"], inputs["topk_weights"], lay_o)
-    compare_dispatch(w, lay_o, R, want)
+    compare_dispatch(w, lay_o, R, want, direct)
     del want
     if not check_combine:
         return
@@ -100,6 +100,17 @@ SMALL = [
 @pytest.mark.parametrize("edge", [False, True], ids=["clean", "edge_lanes"])
 def test_small_cases(w, edge):
     _full_case(w, 7, EDGE if edge else None)
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2, 3, 4])
+def test_direct_recv_x_full_size(cfg_id):
+    """Direct Recv X writes the same receive rows, scales and metadata."""
+    _full_case(WORKLOADS[cfg_id], seed_for(cfg_id, 1), direct=True, check_combine=(cfg_id == 1))
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[3], SMALL[4], SMALL[7], SMALL[11]], ids=lambda w: w.name)
+def test_direct_recv_x_small(w):
+    _full_case(w, 11, EDGE, direct=True)
 
 
 def test_error_flag_for_out_of_range_ids():
