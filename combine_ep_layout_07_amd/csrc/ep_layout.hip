@@ -199,6 +199,27 @@ __device__ int block_exclusive_scan(int *a, int n, int *part) {
     return total;
 }
 
+// lds[col(i)] += src(i) for i in [0, n), with every thread issuing up to 8
+// global loads before its first LDS add, so a reduction of up to 2048 terms
+// costs one memory latency.
+template <typename Src, typename Col>
+__device__ __forceinline__ void gather_add(int64_t n, int *lds, Src src, Col col) {
+    constexpr int U = 8;
+    for (int64_t i0 = 0; i0 < n; i0 += (int64_t)U * kLayoutThreads) {
+        int v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t i = i0 + (int64_t)k * kLayoutThreads + threadIdx.x;
+            v[k] = i < n ? src(i) : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t i = i0 + (int64_t)k * kLayoutThreads + threadIdx.x;
+            if (i < n && v[k] != 0) atomicAdd(&lds[col(i)], v[k]);
+        }
+    }
+}
+
 __device__ __forceinline__ void wave_range(const LayoutArgs &a, int b, int w, int &t0, int &t1) {
     const int cw = a.g.chunk / kLayoutWaves;
     t0 = min(b * a.g.chunk + w * cw, a.sh.T);
@@ -309,20 +330,23 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
     for (int i = tid; i < kLayoutWaves * (R + E) + R + E + (R + E); i += kLayoutThreads) lds[i] = 0;
     __syncthreads();
     // Unit base per destination: what the earlier units of this source send there.
-    for (int i = tid; i < b * R; i += kLayoutThreads)
-        atomicAdd(&base_d[i % R], a.blk_cnt_rank[((int64_t)s * B) * R + i]);
+    const int32_t *src_rank = a.blk_cnt_rank + (int64_t)s * B * R;
+    gather_add((int64_t)b * R, base_d, [&](int64_t i) { return src_rank[i]; },
+               [&](int64_t i) { return (int)(i % R); });
     if (expand)
         for (int e = tid; e < E; e += kLayoutThreads) base_e[e] = a.blk_base_expert[me * E + e];
     // This unit's share of the per-source totals: columns c = b, b+B, ...
     // (destinations first, then experts), each summed over the source's units.
     const int ncol = b < R + E ? (R + E - b + B - 1) / B : 0;
-    for (int i = tid; i < ncol * B; i += kLayoutThreads) {
-        const int j = i / B, q = i - j * B;
-        const int cidx = b + j * B;
-        const int v = cidx < R ? a.blk_cnt_rank[((int64_t)s * B + q) * R + cidx]
-                               : a.blk_cnt_expert[((int64_t)s * B + q) * E + (cidx - R)];
-        atomicAdd(&col[cidx], v);
-    }
+    gather_add(
+        (int64_t)ncol * B, col,
+        [&](int64_t i) {
+            const int j = (int)(i / B), q = (int)(i - (int64_t)j * B);
+            const int cidx = b + j * B;
+            return cidx < R ? a.blk_cnt_rank[((int64_t)s * B + q) * R + cidx]
+                            : a.blk_cnt_expert[((int64_t)s * B + q) * E + (cidx - R)];
+        },
+        [&](int64_t i) { return b + (int)(i / B) * B; });
     __syncthreads();
     for (int cidx = b + tid * B; cidx < R + E; cidx += kLayoutThreads * B) {
         if (cidx < R) a.tokens_per_rank[(int64_t)s * R + cidx] = col[cidx];
@@ -397,11 +421,8 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
         if (fits) {
             for (int i = tid; i < S * R; i += kLayoutThreads) tot[i] = 0;
             __syncthreads();
-            for (int64_t i = tid; i < U * R; i += kLayoutThreads) {
-                const int64_t uu = i / R;
-                const int d = (int)(i - uu * R);
-                atomicAdd(&tot[(uu / B) * R + d], a.blk_cnt_rank[i]);
-            }
+            gather_add(U * R, tot, [&](int64_t i) { return a.blk_cnt_rank[i]; },
+                       [&](int64_t i) { return (int)((i / R) / B * R + i % R); });
             __syncthreads();
         }
         int *tot_d = part;  // [R] totals per destination (R <= 64)
