@@ -51,6 +51,8 @@ def _open(path: str) -> ctypes.CDLL:
     lib.epo_dispatch.restype = I
     lib.epo_combine.argtypes = [I] * 8 + [P] * 8
     lib.epo_combine.restype = I
+    lib.epo_combine_bias.argtypes = [I] * 8 + [P] * 10
+    lib.epo_combine_bias.restype = I
     lib.epo_combine_tokens.argtypes = [I] * 8 + [P] * 7 + [I, P, P]
     lib.epo_combine_tokens.restype = I
     lib.epo_bf16_from_double.argtypes = [ctypes.c_double]
@@ -168,6 +170,25 @@ def combine(S, T, H, K, E, R, Nmax, expand: bool, topk_idx: np.ndarray, topk_wei
                          _p(lay.get("expand_pos")), _p(yy), _p(out))
     if rc != 0:
         raise ValueError(f"epo_combine rejected the sizes (rc={rc})")
+    return out
+
+
+def combine_bias(S, T, H, K, E, R, Nmax, expand: bool, topk_idx: np.ndarray, topk_weights: np.ndarray,
+                 lay: Dict[str, np.ndarray], y: np.ndarray, bias0: Optional[np.ndarray],
+                 bias1: Optional[np.ndarray]) -> np.ndarray:
+    """Combine plus up to two bf16 bias tensors (uint16 [S][T][H] or None)."""
+    lib = _load()
+    out = np.empty((S, T, H), np.uint16)
+    b0 = None if bias0 is None else np.ascontiguousarray(bias0, dtype=np.uint16)
+    b1 = None if bias1 is None else np.ascontiguousarray(bias1, dtype=np.uint16)
+    rc = lib.epo_combine_bias(S, T, H, K, E, R, Nmax, int(expand),
+                              _p(np.ascontiguousarray(topk_idx, dtype=np.int64)),
+                              _p(np.ascontiguousarray(topk_weights, dtype=np.float32)),
+                              _p(lay["dst_slot"]), _p(lay["recv_psum"]), _p(lay["recv_base"]),
+                              _p(lay.get("expand_pos")), _p(np.ascontiguousarray(y, dtype=np.uint16)),
+                              _p(b0), _p(b1), _p(out))
+    if rc != 0:
+        raise ValueError(f"epo_combine_bias rejected the sizes (rc={rc})")
     return out
 
 

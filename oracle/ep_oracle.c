@@ -279,7 +279,8 @@ static void combine_token(int S, int T, int H, int K, int E, int R, int Nmax, in
                           const int64_t *topk_idx, const float *topk_weights,
                           const int32_t *dst_slot, const int32_t *recv_psum,
                           const int32_t *recv_base, const int32_t *expand_pos,
-                          const uint16_t *y, int s, int t, double *acc, uint16_t *o) {
+                          const uint16_t *y, const uint16_t *bias0, const uint16_t *bias1,
+                          int s, int t, double *acc, uint16_t *o) {
     const int El = E / R;
     const int64_t *tok = topk_idx + ((size_t)s * T + t) * K;
     const float *w = topk_weights + ((size_t)s * T + t) * K;
@@ -302,6 +303,15 @@ static void combine_token(int S, int T, int H, int K, int E, int R, int Nmax, in
         const uint16_t *yr = y + row * (size_t)H;
         for (int h = 0; h < H; ++h) acc[h] += (double)w[k] * bf16_to_double(yr[h]);
     }
+    /* Bias rows of the token (the benchmark of [DET] Performance runs the
+     * combine with num_bias = 2): added to the reduced sum before the one
+     * rounding. */
+    const uint16_t *biases[2] = {bias0, bias1};
+    for (int b = 0; b < 2; ++b) {
+        if (!biases[b]) continue;
+        const uint16_t *br = biases[b] + ((size_t)s * T + t) * H;
+        for (int h = 0; h < H; ++h) acc[h] += bf16_to_double(br[h]);
+    }
     for (int h = 0; h < H; ++h) o[h] = epo_bf16_from_double(acc[h]);
 }
 
@@ -315,7 +325,22 @@ int epo_combine(int S, int T, int H, int K, int E, int R, int Nmax, int expand,
     for (int s = 0; s < S; ++s)
         for (int t = 0; t < T; ++t)
             combine_token(S, T, H, K, E, R, Nmax, expand, topk_idx, topk_weights, dst_slot, recv_psum,
-                          recv_base, expand_pos, y, s, t, acc, out + ((size_t)s * T + t) * H);
+                          recv_base, expand_pos, y, NULL, NULL, s, t, acc, out + ((size_t)s * T + t) * H);
+    free(acc);
+    return 0;
+}
+
+int epo_combine_bias(int S, int T, int H, int K, int E, int R, int Nmax, int expand,
+                     const int64_t *topk_idx, const float *topk_weights,
+                     const int32_t *dst_slot, const int32_t *recv_psum,
+                     const int32_t *recv_base, const int32_t *expand_pos,
+                     const uint16_t *y, const uint16_t *bias0, const uint16_t *bias1, uint16_t *out) {
+    if (!sizes_ok(S, T, K, E, R, Nmax) || H < 1) return -1;
+    double *acc = (double *)malloc(sizeof(double) * (size_t)H);
+    for (int s = 0; s < S; ++s)
+        for (int t = 0; t < T; ++t)
+            combine_token(S, T, H, K, E, R, Nmax, expand, topk_idx, topk_weights, dst_slot, recv_psum,
+                          recv_base, expand_pos, y, bias0, bias1, s, t, acc, out + ((size_t)s * T + t) * H);
     free(acc);
     return 0;
 }
@@ -331,7 +356,7 @@ int epo_combine_tokens(int S, int T, int H, int K, int E, int R, int Nmax, int e
         if (sel[i] < 0 || sel[i] >= (int64_t)S * T) { free(acc); return -1; }
         int s = (int)(sel[i] / T), t = (int)(sel[i] % T);
         combine_token(S, T, H, K, E, R, Nmax, expand, topk_idx, topk_weights, dst_slot, recv_psum,
-                      recv_base, expand_pos, y, s, t, acc, out + (size_t)i * H);
+                      recv_base, expand_pos, y, NULL, NULL, s, t, acc, out + (size_t)i * H);
     }
     free(acc);
     return 0;

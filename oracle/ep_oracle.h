@@ -82,6 +82,15 @@ int epo_combine(int S, int T, int H, int K, int E, int R, int Nmax, int expand,
                 const int32_t *recv_base, const int32_t *expand_pos,
                 const uint16_t *y, uint16_t *out);
 
+/* Combine plus up to two bias tensors bias0/bias1 (bf16 bits [S][T][H], NULL
+ * when absent): out = bf16(sum_k w*Y + bias0 + bias1), summed in double and
+ * rounded once. */
+int epo_combine_bias(int S, int T, int H, int K, int E, int R, int Nmax, int expand,
+                     const int64_t *topk_idx, const float *topk_weights,
+                     const int32_t *dst_slot, const int32_t *recv_psum,
+                     const int32_t *recv_base, const int32_t *expand_pos,
+                     const uint16_t *y, const uint16_t *bias0, const uint16_t *bias1, uint16_t *out);
+
 /* Combine restricted to the n_sel global token indices sel[i] = s*T + t;
  * out is [n_sel][H].  Same definition as epo_combine. */
 int epo_combine_tokens(int S, int T, int H, int K, int E, int R, int Nmax, int expand,

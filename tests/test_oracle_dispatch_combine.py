@@ -85,6 +85,46 @@ def test_combine_exact_rational(w):
             assert (out[s, t] == want).all(), f"token ({s},{t})"
 
 
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[1]], ids=lambda w: w.name)
+@pytest.mark.parametrize("nb", [1, 2])
+def test_combine_bias_exact_rational(w, nb):
+    """Bias rows are added to the reduced sum before the single rounding."""
+    from fractions import Fraction
+    d, lay, disp = _run(w, 13, masked_frac=0.2, dup_frac=0.2)
+    rows = oracle.recv_rows(w.S, w.T, w.K, w.E, w.R, lay, w.expand)
+    H = 24
+    y = draw_expert_outputs(max(rows, 1), H, 31)
+    biases = [draw_expert_outputs(w.S * w.T, H, 40 + i).reshape(w.S, w.T, H) for i in range(nb)]
+    out = oracle.combine_bias(w.S, w.T, H, w.K, w.E, w.R, w.Nmax, w.expand, d["topk_idx"], d["topk_weights"],
+                              lay, y, biases[0], biases[1] if nb > 1 else None)
+    for s in range(w.S):
+        for t in range(w.T):
+            pairs = combine_rows_for_token(w.S, w.T, w.K, w.E, w.R, w.Nmax, d["topk_idx"], lay, s, t, w.expand)
+            want = []
+            for h in range(H):
+                acc = sum((f32_to_fraction(d["topk_weights"][s, t, k]) * bf16_bits_to_fraction(int(y[r, h]))
+                           for r, k in pairs), Fraction(0))
+                acc += sum((bf16_bits_to_fraction(int(bb[s, t, h])) for bb in biases), Fraction(0))
+                want.append(fraction_to_bf16_bits(acc))
+            assert (out[s, t] == np.array(want, np.uint16)).all(), f"token ({s},{t})"
+
+
+def test_combine_bias_alone_when_no_lane_is_valid():
+    w = Workload("nb", S=1, T=5, H=16, K=2, E=4, R=2, Nmax=5)
+    topk = np.full((1, 5, 2), -1, np.int64)
+    wts = np.full((1, 5, 2), 0.5, np.float32)
+    lay = oracle.layout(1, 5, 2, 4, 2, 5, topk)
+    y = draw_expert_outputs(1, 16, 1)
+    b0 = draw_expert_outputs(5, 16, 2).reshape(1, 5, 16)
+    b1 = draw_expert_outputs(5, 16, 3).reshape(1, 5, 16)
+    out = oracle.combine_bias(1, 5, 16, 2, 4, 2, 5, False, topk, wts, lay, y, b0, b1)
+    f0 = torch.from_numpy(b0.view(np.int16).copy()).view(torch.bfloat16).double()
+    f1 = torch.from_numpy(b1.view(np.int16).copy()).view(torch.bfloat16).double()
+    want = (f0 + f1).float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)  # b0+b1 exact in fp32
+    assert (out == want).all()
+    assert (oracle.combine_bias(1, 5, 16, 2, 4, 2, 5, False, topk, wts, lay, y, b0, None) == b0).all()
+
+
 def test_combine_one_hot_returns_row_bitwise():
     w = Workload("oh", S=2, T=20, H=64, K=4, E=16, R=4, Nmax=20, expand=False)
     rng = np.random.default_rng(1)

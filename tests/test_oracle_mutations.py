@@ -45,6 +45,10 @@ MUTANTS = {
     "expand_weight_from_owner": ("recv_topk_weights[r] = topk_weights[((size_t)s * T + t) * K + k];",
                                  "recv_topk_weights[r] = topk_weights[((size_t)s * T + t) * K + k0];"),
     "padding_src_zero": ("recv_src_idx[r] = -1;", "recv_src_idx[r] = 0;"),
+    "bias_dropped": ("for (int h = 0; h < H; ++h) acc[h] += bf16_to_double(br[h]);",
+                     "for (int h = 0; h < H; ++h) acc[h] += 0.0 * bf16_to_double(br[h]);"),
+    "bias_wrong_token": ("const uint16_t *br = biases[b] + ((size_t)s * T + t) * H;",
+                         "const uint16_t *br = biases[b] + ((size_t)t) * H;"),
 }
 
 SMALL = [
@@ -83,6 +87,19 @@ def pin_suite():
                 want = exact_combine_row([y[r] for r, _ in pairs], [d["topk_weights"][s, t, k] for _, k in pairs]) \
                     if pairs else np.zeros(16, np.uint16)
                 assert (out[s, t] == want).all()
+    wb = SMALL[0]
+    d = generate(wb, 4, masked_frac=0.2)
+    lay = oracle.layout(wb.S, wb.T, wb.K, wb.E, wb.R, wb.Nmax, d["topk_idx"])
+    y = draw_expert_outputs(int(lay["recv_base"][-1]), 8, 5)
+    bias = draw_expert_outputs(wb.S * wb.T, 8, 6).reshape(wb.S, wb.T, 8)
+    out = oracle.combine_bias(wb.S, wb.T, 8, wb.K, wb.E, wb.R, wb.Nmax, False, d["topk_idx"], d["topk_weights"],
+                              lay, y, bias, None)
+    for s in range(wb.S):
+        for t in range(wb.T):
+            pairs = combine_rows_for_token(wb.S, wb.T, wb.K, wb.E, wb.R, wb.Nmax, d["topk_idx"], lay, s, t, False)
+            ext_rows = [y[r] for r, _ in pairs] + [bias[s, t]]
+            ext_w = [d["topk_weights"][s, t, k] for _, k in pairs] + [np.float32(1.0)]
+            assert (out[s, t] == exact_combine_row(ext_rows, ext_w)).all()
     one, q = Fraction(1), Fraction(1, 128)
     for c in (one + q / 2, one + 3 * q / 2, Fraction(3, 2) * Fraction(2) ** -133, Fraction(2) ** -130):
         assert oracle.bf16_from_double(float(c)) == fraction_to_bf16_bits(c)
