@@ -216,6 +216,12 @@ int ep_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev
 
 int ep_combine(const ep_config_t *cfg, const ep_layout_t *layout, const int64_t *topk_idx_dev,
                const float *topk_weights_dev, const void *y_dev, void *out_dev, void *stream) {
+    return ep_combine_bias(cfg, layout, topk_idx_dev, topk_weights_dev, y_dev, nullptr, nullptr, out_dev, stream);
+}
+
+int ep_combine_bias(const ep_config_t *cfg, const ep_layout_t *layout, const int64_t *topk_idx_dev,
+                    const float *topk_weights_dev, const void *y_dev, const void *bias0_dev,
+                    const void *bias1_dev, void *out_dev, void *stream) {
     ep::Shape sh;
     int rc = make_shape(cfg, &sh);
     if (rc != EP_OK) return rc;
@@ -223,6 +229,8 @@ int ep_combine(const ep_config_t *cfg, const ep_layout_t *layout, const int64_t 
     if ((int64_t)sh.S * sh.T > 0) {
         if (!topk_idx_dev || !aligned(topk_idx_dev, 8) || !topk_weights_dev || !aligned(topk_weights_dev, 4) ||
             !y_dev || !aligned(y_dev, 16) || !out_dev || !aligned(out_dev, 16))
+            return EP_ERR_INVALID_ARG;
+        if ((bias0_dev && !aligned(bias0_dev, 16)) || (bias1_dev && !aligned(bias1_dev, 16)))
             return EP_ERR_INVALID_ARG;
     }
     ep::CombineArgs a;
@@ -234,6 +242,8 @@ int ep_combine(const ep_config_t *cfg, const ep_layout_t *layout, const int64_t 
     a.recv_base = layout->recv_base_dev;
     a.expand_pos = layout->expand_pos_dev;
     a.y = static_cast<const uint16_t *>(y_dev);
+    a.bias0 = static_cast<const uint16_t *>(bias0_dev);
+    a.bias1 = static_cast<const uint16_t *>(bias1_dev);
     a.out = static_cast<uint16_t *>(out_dev);
     a.y_rows = recv_rows(sh);
     return ep::launch_combine(a, (hipStream_t)stream) == hipSuccess ? EP_OK : EP_ERR_HIP;

@@ -170,6 +170,18 @@ __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
                 for (int j = 0; j < G; ++j)
                     if (j < n) fma_row<CPL>(acc, v[j], ww[j]);
             }
+            // Bias rows of this token, added in fp32 before the rounding.
+            for (int bi = 0; bi < 2; ++bi) {
+                const uint16_t *bias = bi == 0 ? a.bias0 : a.bias1;
+                if (!bias) continue;
+                u32x4 bv[CPL];
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
+                    const int c = c0 + i * kWave + lane;
+                    bv[i] = c < c_hi ? ld16(bias + g * sh.H + (int64_t)c * 8) : u32x4{0u, 0u, 0u, 0u};
+                }
+                fma_row<CPL>(acc, bv, 1.0f);
+            }
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const int c = c0 + i * kWave + lane;

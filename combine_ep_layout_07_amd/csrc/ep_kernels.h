@@ -66,6 +66,7 @@ struct CombineArgs {
     const float *topk_weights;
     const int32_t *dst_slot, *recv_psum, *recv_base, *expand_pos;
     const uint16_t *y;
+    const uint16_t *bias0, *bias1;  // optional [S][T][H] rows added before rounding
     uint16_t *out;
     int64_t y_rows;  // rows of y (the receive capacity)
     int slices;      // column slices per token (set by the launcher)

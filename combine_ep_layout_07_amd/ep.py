@@ -71,7 +71,8 @@ def _load():
     lib.ep_dispatch.argtypes = [ctypes.POINTER(EpConfig), P, P, P, P, ctypes.POINTER(EpLayoutT),
                                 ctypes.POINTER(EpRecvT), ctypes.c_int32, P]
     lib.ep_combine.argtypes = [ctypes.POINTER(EpConfig), ctypes.POINTER(EpLayoutT), P, P, P, P, P]
-    for f in ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_combine", "ep_version"):
+    lib.ep_combine_bias.argtypes = [ctypes.POINTER(EpConfig), ctypes.POINTER(EpLayoutT), P, P, P, P, P, P, P]
+    for f in ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_combine", "ep_combine_bias", "ep_version"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ep_status_string.argtypes = [ctypes.c_int]
     lib.ep_status_string.restype = ctypes.c_char_p
@@ -246,3 +247,21 @@ def ep_combine(cfg: EpConfig, layout: LayoutBuffers, topk_idx: torch.Tensor, top
                          _ptr(out, "out", S * T * H * 2), _stream(stream))
     if rc != EP_OK:
         raise EpError(rc, "ep_combine")
+
+
+def ep_combine_bias(cfg: EpConfig, layout: LayoutBuffers, topk_idx: torch.Tensor, topk_weights: torch.Tensor,
+                    y: torch.Tensor, bias0: Optional[torch.Tensor], bias1: Optional[torch.Tensor],
+                    out: torch.Tensor, stream=None) -> None:
+    """Combine plus up to two bf16 [S][T][H] bias tensors added before the rounding."""
+    S, T, K, H = cfg.num_src_ranks, cfg.num_tokens, cfg.num_topk, cfg.hidden
+    rows = int(ep_query_sizes(cfg).recv_rows)
+    if topk_weights.dtype != torch.float32 or topk_idx.dtype != torch.int64:
+        raise ValueError("topk_idx must be int64 and topk_weights float32")
+    nb = S * T * H * 2
+    rc = _lib.ep_combine_bias(ctypes.byref(cfg), ctypes.byref(layout.struct), _ptr(topk_idx, "topk_idx", S * T * K * 8),
+                              _ptr(topk_weights, "topk_weights", S * T * K * 4), _ptr(y, "y", rows * H * 2),
+                              _ptr(bias0, "bias0", nb if bias0 is not None else 0),
+                              _ptr(bias1, "bias1", nb if bias1 is not None else 0),
+                              _ptr(out, "out", S * T * H * 2), _stream(stream))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_combine_bias")

@@ -216,6 +216,15 @@ int ep_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev
 int ep_combine(const ep_config_t *cfg, const ep_layout_t *layout, const int64_t *topk_idx_dev,
                const float *topk_weights_dev, const void *y_dev, void *out_dev, void *stream);
 
+/* Combine plus bias ([DET] Performance runs the combine with num_bias = 2):
+ * out[s][t] = bf16(sum over valid lanes of w * Y + bias0[s][t] + bias1[s][t]),
+ * the bias rows added in fp32 before the one rounding.  bias0_dev / bias1_dev
+ * are bf16 [S][T][H] (16-byte aligned), either may be NULL; with both NULL
+ * this is ep_combine. */
+int ep_combine_bias(const ep_config_t *cfg, const ep_layout_t *layout, const int64_t *topk_idx_dev,
+                    const float *topk_weights_dev, const void *y_dev, const void *bias0_dev,
+                    const void *bias1_dev, void *out_dev, void *stream);
+
 /* Static description of a status code. */
 const char *ep_status_string(int status);
 

@@ -33,7 +33,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_combine", "ep_status_string"):
+    for required in ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_combine", "ep_combine_bias",
+                     "ep_status_string"):
         assert required in names
 
 

@@ -113,6 +113,52 @@ def test_direct_recv_x_small(w):
     _full_case(w, 11, EDGE, direct=True)
 
 
+@pytest.mark.parametrize("case", ["tiny", "dsv3_share", "expand_small", "expand_a4_fp8"])
+@pytest.mark.parametrize("nb", [1, 2])
+def test_combine_bias(case, nb):
+    """ep_combine_bias: bias rows added before the single rounding."""
+    w = {x.name: x for x in list(WORKLOADS.values()) + SMALL}[case]
+    inputs = generate(w, 23, masked_frac=0.1)
+    lay_o = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment)
+    dev = upload(w, inputs)
+    say(f"[case] {w.name} ep_combine_bias nb={nb}")
+    cfg, L = run_layout(w, dev)
+    rows = int(ep.ep_query_sizes(cfg).recv_rows)
+    y = seeded_y(rows, w.H, 5)
+    biases = [seeded_y(w.S * w.T, w.H, 6 + i) for i in range(nb)]
+    out = torch.empty((w.S * w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    ep.ep_combine_bias(cfg, L, dev["topk_idx"], dev["topk_weights"], y, biases[0], biases[1] if nb > 1 else None,
+                       out)
+    torch.cuda.synchronize()
+    hb = [b.view(torch.int16).cpu().numpy().view(np.uint16).reshape(w.S, w.T, w.H) for b in biases]
+    ref = oracle.combine_bias(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.expand, inputs["topk_idx"],
+                              inputs["topk_weights"], lay_o, y.view(torch.int16).cpu().numpy().view(np.uint16),
+                              hb[0], hb[1] if nb > 1 else None)
+    share = compare_combine(out.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+    assert share > 0.99
+
+
+def test_cached_layout_replay():
+    """One layout (the pages' handle) serves several dispatches of different
+    hidden states with the same routing."""
+    w = WORKLOADS[3]
+    inputs = generate(w, seed_for(3, 1))
+    other = generate(w, seed_for(3, 2))
+    say("[case] dsv3_share_fp8 cached layout replay")
+    lay_o = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment)
+    dev = upload(w, inputs)
+    cfg, L = run_layout(w, dev)
+    for x_np, sf_np in ((inputs["x"], inputs["x_sf"]), (other["x"], other["x_sf"]), (inputs["x"], inputs["x_sf"])):
+        x = torch.from_numpy(x_np.reshape(w.S * w.T, -1)).cuda()
+        sf = torch.from_numpy(sf_np).cuda()
+        R = ep.alloc_recv(cfg)
+        ep.ep_dispatch(cfg, x, sf, dev["topk_idx"], dev["topk_weights"], L, R)
+        torch.cuda.synchronize()
+        want = oracle.dispatch(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, True, False, 1, x_np, sf_np,
+                               inputs["topk_idx"], inputs["topk_weights"], lay_o)
+        compare_dispatch(w, lay_o, R, want)
+
+
 def test_error_flag_for_out_of_range_ids():
     w = Workload("bad_ids", S=1, T=64, H=64, K=4, E=16, R=4, Nmax=64)
     inputs = generate(w, 3, invalid_frac=0.2)
