@@ -46,6 +46,7 @@ class Workload:
     alignment: int = 1
     routing: str = "uniform"      # "uniform" distinct experts, or "zipf"
     zipf_s: float = 1.2
+    n_out: int = 1                # num_scaleout_ranks: > 1 = hybrid row form, S = n_out * n_up
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)

@@ -45,15 +45,15 @@ def _open(path: str) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I = ctypes.c_int
-    lib.epo_layout.argtypes = [I] * 8 + [P] * 9
+    lib.epo_layout.argtypes = [I] * 9 + [P] * 10
     lib.epo_layout.restype = I
-    lib.epo_dispatch.argtypes = [I] * 10 + [P] * 19
+    lib.epo_dispatch.argtypes = [I] * 11 + [P] * 19
     lib.epo_dispatch.restype = I
-    lib.epo_combine.argtypes = [I] * 8 + [P] * 8
+    lib.epo_combine.argtypes = [I] * 9 + [P] * 8
     lib.epo_combine.restype = I
-    lib.epo_combine_bias.argtypes = [I] * 8 + [P] * 10
+    lib.epo_combine_bias.argtypes = [I] * 9 + [P] * 10
     lib.epo_combine_bias.restype = I
-    lib.epo_combine_tokens.argtypes = [I] * 8 + [P] * 7 + [I, P, P]
+    lib.epo_combine_tokens.argtypes = [I] * 9 + [P] * 7 + [I, P, P]
     lib.epo_combine_tokens.restype = I
     lib.epo_bf16_from_double.argtypes = [ctypes.c_double]
     lib.epo_bf16_from_double.restype = ctypes.c_uint16
@@ -88,8 +88,10 @@ def bf16_from_double(v: float) -> int:
     return int(_load().epo_bf16_from_double(float(v)))
 
 
-def layout(S, T, K, E, R, Nmax, topk_idx: np.ndarray, expand: bool = False, A: int = 1) -> Dict[str, np.ndarray]:
-    """Run the oracle layout; returns the tables as numpy int32 arrays."""
+def layout(S, T, K, E, R, Nmax, topk_idx: np.ndarray, expand: bool = False, A: int = 1,
+           n_out: int = 1) -> Dict[str, np.ndarray]:
+    """Run the oracle layout; returns the tables as numpy int32 arrays
+    (``n_out`` = num_scaleout_ranks; > 1 selects the hybrid row form)."""
     lib = _load()
     topk = np.ascontiguousarray(topk_idx, dtype=np.int64).reshape(S, T, K)
     out = {
@@ -103,10 +105,12 @@ def layout(S, T, K, E, R, Nmax, topk_idx: np.ndarray, expand: bool = False, A: i
     if expand:
         out["expert_base"] = np.empty((E + 1,), np.int32)
         out["expand_pos"] = np.empty((S, T, K), np.int32)
-    rc = lib.epo_layout(S, T, K, E, R, Nmax, int(expand), A, _p(topk), _p(out["dst_slot"]),
+    if n_out > 1:
+        out["recv_psum_scaleup"] = np.empty((R, S // n_out + 1), np.int32)
+    rc = lib.epo_layout(S, T, K, E, R, Nmax, int(expand), A, n_out, _p(topk), _p(out["dst_slot"]),
                         _p(out["tokens_per_rank"]), _p(out["tokens_per_expert"]), _p(out["recv_psum"]),
                         _p(out["recv_base"]), _p(out.get("expert_base")), _p(out.get("expand_pos")),
-                        _p(out["error_flags"]))
+                        _p(out.get("recv_psum_scaleup")), _p(out["error_flags"]))
     if rc != 0:
         raise ValueError(f"epo_layout rejected the sizes (rc={rc})")
     return out
@@ -119,7 +123,7 @@ def recv_rows(S, T, K, E, R, lay: Dict[str, np.ndarray], expand: bool) -> int:
 
 def dispatch(S, T, H, K, E, R, Nmax, is_fp8: bool, expand: bool, A: int, x: np.ndarray,
              x_sf: Optional[np.ndarray], topk_idx: np.ndarray, topk_weights: np.ndarray,
-             lay: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+             lay: Dict[str, np.ndarray], n_out: int = 1) -> Dict[str, np.ndarray]:
     """Run the oracle scatter + copy epilogue; returns staging and receive arrays.
 
     Staging rows that no lane fills keep the value 0 here; they are unspecified
@@ -144,7 +148,7 @@ def dispatch(S, T, H, K, E, R, Nmax, is_fp8: bool, expand: bool, A: int, x: np.n
         out["recv_topk_weights"] = np.zeros((rows, K), np.float32)
     xs = np.ascontiguousarray(x, dtype=np.uint8).reshape(S, T, Rw)
     sf = np.ascontiguousarray(x_sf, dtype=np.float32).reshape(S, T, F) if is_fp8 else None
-    rc = lib.epo_dispatch(S, T, H, K, E, R, Nmax, int(is_fp8), int(expand), A, _p(xs), _p(sf),
+    rc = lib.epo_dispatch(S, T, H, K, E, R, Nmax, int(is_fp8), int(expand), A, n_out, _p(xs), _p(sf),
                           _p(np.ascontiguousarray(topk_idx, dtype=np.int64)),
                           _p(np.ascontiguousarray(topk_weights, dtype=np.float32)),
                           _p(lay["dst_slot"]), _p(lay["tokens_per_rank"]), _p(lay["tokens_per_expert"]),
@@ -158,12 +162,12 @@ def dispatch(S, T, H, K, E, R, Nmax, is_fp8: bool, expand: bool, A: int, x: np.n
 
 
 def combine(S, T, H, K, E, R, Nmax, expand: bool, topk_idx: np.ndarray, topk_weights: np.ndarray,
-            lay: Dict[str, np.ndarray], y: np.ndarray) -> np.ndarray:
+            lay: Dict[str, np.ndarray], y: np.ndarray, n_out: int = 1) -> np.ndarray:
     """Run the oracle combine; ``y`` is bf16 bits (uint16) [rows][H]; returns uint16 [S][T][H]."""
     lib = _load()
     out = np.empty((S, T, H), np.uint16)
     yy = np.ascontiguousarray(y, dtype=np.uint16)
-    rc = lib.epo_combine(S, T, H, K, E, R, Nmax, int(expand),
+    rc = lib.epo_combine(S, T, H, K, E, R, Nmax, int(expand), n_out,
                          _p(np.ascontiguousarray(topk_idx, dtype=np.int64)),
                          _p(np.ascontiguousarray(topk_weights, dtype=np.float32)),
                          _p(lay["dst_slot"]), _p(lay["recv_psum"]), _p(lay["recv_base"]),
@@ -175,13 +179,13 @@ def combine(S, T, H, K, E, R, Nmax, expand: bool, topk_idx: np.ndarray, topk_wei
 
 def combine_bias(S, T, H, K, E, R, Nmax, expand: bool, topk_idx: np.ndarray, topk_weights: np.ndarray,
                  lay: Dict[str, np.ndarray], y: np.ndarray, bias0: Optional[np.ndarray],
-                 bias1: Optional[np.ndarray]) -> np.ndarray:
+                 bias1: Optional[np.ndarray], n_out: int = 1) -> np.ndarray:
     """Combine plus up to two bf16 bias tensors (uint16 [S][T][H] or None)."""
     lib = _load()
     out = np.empty((S, T, H), np.uint16)
     b0 = None if bias0 is None else np.ascontiguousarray(bias0, dtype=np.uint16)
     b1 = None if bias1 is None else np.ascontiguousarray(bias1, dtype=np.uint16)
-    rc = lib.epo_combine_bias(S, T, H, K, E, R, Nmax, int(expand),
+    rc = lib.epo_combine_bias(S, T, H, K, E, R, Nmax, int(expand), n_out,
                               _p(np.ascontiguousarray(topk_idx, dtype=np.int64)),
                               _p(np.ascontiguousarray(topk_weights, dtype=np.float32)),
                               _p(lay["dst_slot"]), _p(lay["recv_psum"]), _p(lay["recv_base"]),
@@ -193,13 +197,13 @@ def combine_bias(S, T, H, K, E, R, Nmax, expand: bool, topk_idx: np.ndarray, top
 
 
 def combine_tokens(S, T, H, K, E, R, Nmax, expand: bool, topk_idx: np.ndarray, topk_weights: np.ndarray,
-                   lay: Dict[str, np.ndarray], y: np.ndarray, sel: np.ndarray) -> np.ndarray:
+                   lay: Dict[str, np.ndarray], y: np.ndarray, sel: np.ndarray, n_out: int = 1) -> np.ndarray:
     """Combine for the global token indices ``sel`` only; returns uint16 [len(sel)][H]."""
     lib = _load()
     sel = np.ascontiguousarray(sel, dtype=np.int64)
     out = np.empty((sel.size, H), np.uint16)
     yy = np.ascontiguousarray(y, dtype=np.uint16)
-    rc = lib.epo_combine_tokens(S, T, H, K, E, R, Nmax, int(expand),
+    rc = lib.epo_combine_tokens(S, T, H, K, E, R, Nmax, int(expand), n_out,
                                 _p(np.ascontiguousarray(topk_idx, dtype=np.int64)),
                                 _p(np.ascontiguousarray(topk_weights, dtype=np.float32)),
                                 _p(lay["dst_slot"]), _p(lay["recv_psum"]), _p(lay["recv_base"]),
@@ -211,12 +215,13 @@ def combine_tokens(S, T, H, K, E, R, Nmax, expand: bool, topk_idx: np.ndarray, t
 
 def run_workload(w, inputs: Dict[str, np.ndarray], y: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Layout + dispatch (+ combine when ``y`` is given) for a ``workloads.Workload``."""
-    lay = layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment)
+    lay = layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment, w.n_out)
     res = dict(lay)
     if "x" in inputs:
         res.update(dispatch(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.dtype == "fp8", w.expand, w.alignment,
-                            inputs["x"], inputs.get("x_sf"), inputs["topk_idx"], inputs["topk_weights"], lay))
+                            inputs["x"], inputs.get("x_sf"), inputs["topk_idx"], inputs["topk_weights"], lay,
+                            w.n_out))
     if y is not None:
         res["out"] = combine(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.expand, inputs["topk_idx"],
-                             inputs["topk_weights"], lay, y)
+                             inputs["topk_weights"], lay, y, w.n_out)
     return res

@@ -14,8 +14,9 @@
  *     is the "owner" and carries the slot, the other lanes of the same rank
  *     get -1;
  *   - the running count is exclusive, over tokens in ascending order;
- *   - the row base of source partition s is s (direct path: one receive row
- *     per source rank);
+ *   - the row base of source partition s is s on the direct path (one
+ *     receive row per source rank) and its scale-out index on the hybrid path,
+ *     whose receive buffer is segmented by the scale-up index (row form);
  *   - the compact receive order is destination-major, then source, then slot,
  *     which is the order a sort by global source token index (s*T + t) gives
  *     inside each destination;
@@ -60,11 +61,33 @@ static int sizes_ok(int S, int T, int K, int E, int R, int Nmax) {
     return 1;
 }
 
-int epo_layout(int S, int T, int K, int E, int R, int Nmax, int expand, int A,
+/* Topology of the S source ranks: n_out <= 1 is the direct path; n_out > 1
+ * is the hybrid path with S = n_out * n_up ranks, rank s having scale-out
+ * index s / n_up and scale-up index s % n_up. */
+static int topology_ok(int S, int n_out) { return n_out <= 1 || (S % n_out == 0); }
+
+/* Row base of source s ([DET] Direct vs hybrid dispatch): the source rank on
+ * the direct path, its scale-out index on the hybrid path. */
+static int64_t row_base(int s, int S, int n_out) { return n_out > 1 ? s / (S / n_out) : s; }
+
+/* Region (of Nmax rows) that source s fills in destination d's staging
+ * buffer: one region per source on the direct path (d*S + s); in the hybrid
+ * row form the buffer has one segment per scale-up index, and inside it one
+ * region per scale-out index ([DET] Direct vs hybrid dispatch). */
+static size_t staging_region(int d, int s, int S, int n_out) {
+    if (n_out > 1) {
+        const int n_up = S / n_out;
+        return ((size_t)d * n_up + (size_t)(s % n_up)) * (size_t)n_out + (size_t)(s / n_up);
+    }
+    return (size_t)d * S + (size_t)s;
+}
+
+int epo_layout(int S, int T, int K, int E, int R, int Nmax, int expand, int A, int n_out,
                const int64_t *topk_idx, int32_t *dst_slot, int32_t *tokens_per_rank,
                int32_t *tokens_per_expert, int32_t *recv_psum, int32_t *recv_base,
-               int32_t *expert_base, int32_t *expand_pos, int32_t *error_flags) {
-    if (!sizes_ok(S, T, K, E, R, Nmax) || (expand && A < 1)) return -1;
+               int32_t *expert_base, int32_t *expand_pos, int32_t *recv_psum_scaleup,
+               int32_t *error_flags) {
+    if (!sizes_ok(S, T, K, E, R, Nmax) || (expand && A < 1) || !topology_ok(S, n_out)) return -1;
     const int El = E / R;
     int32_t flags = 0;
     memset(tokens_per_rank, 0, sizeof(int32_t) * (size_t)S * R);
@@ -72,8 +95,7 @@ int epo_layout(int S, int T, int K, int E, int R, int Nmax, int expand, int A,
 
     /* Counts and slots ([DET] Approach): the slot of an owner lane is
      * row_base * Nmax + the number of earlier tokens of the same source that
-     * also go to that destination; row_base = s on the direct path ([DET]
-     * Direct vs hybrid dispatch). */
+     * also go to that destination. */
     int32_t *run = (int32_t *)calloc((size_t)R, sizeof(int32_t));
     for (int s = 0; s < S; ++s) {
         for (int d = 0; d < R; ++d) run[d] = 0;
@@ -85,7 +107,7 @@ int epo_layout(int S, int T, int K, int E, int R, int Nmax, int expand, int A,
                 int64_t e = lane_expert(tok[k], E);
                 if (e >= 0) tokens_per_expert[(size_t)s * E + e] += 1;
                 if (lane_is_owner(tok, k, E, El))
-                    slot[k] = (int32_t)((int64_t)s * Nmax + run[e / El]);
+                    slot[k] = (int32_t)(row_base(s, S, n_out) * Nmax + run[e / El]);
                 else
                     slot[k] = -1;
             }
@@ -112,6 +134,23 @@ int epo_layout(int S, int T, int K, int E, int R, int Nmax, int expand, int A,
     }
     recv_base[0] = 0;
     for (int d = 0; d < R; ++d) recv_base[d + 1] = recv_base[d] + recv_psum[(size_t)d * (S + 1) + S];
+
+    /* Hybrid row form: per destination, also the exclusive prefix over
+     * scale-up segments of the rows each segment holds (the per-segment part
+     * of the extended psum, [DET] Direct vs hybrid dispatch). */
+    if (n_out > 1) {
+        const int n_up = S / n_out;
+        for (int d = 0; d < R; ++d) {
+            int32_t *ps = recv_psum_scaleup + (size_t)d * (n_up + 1);
+            ps[0] = 0;
+            for (int u = 0; u < n_up; ++u) {
+                int32_t seg = 0;
+                for (int s = 0; s < S; ++s)
+                    if (s % n_up == u) seg += tokens_per_rank[(size_t)s * R + d];
+                ps[u + 1] = ps[u] + seg;
+            }
+        }
+    }
 
     if (expand) {
         /* Expand layout: one receive row per valid lane, grouped by expert,
@@ -141,7 +180,7 @@ int epo_layout(int S, int T, int K, int E, int R, int Nmax, int expand, int A,
 }
 
 int epo_dispatch(int S, int T, int H, int K, int E, int R, int Nmax, int is_fp8,
-                 int expand, int A, const uint8_t *x, const float *x_sf,
+                 int expand, int A, int n_out, const uint8_t *x, const float *x_sf,
                  const int64_t *topk_idx, const float *topk_weights,
                  const int32_t *dst_slot, const int32_t *tokens_per_rank,
                  const int32_t *tokens_per_expert, const int32_t *recv_psum,
@@ -149,7 +188,7 @@ int epo_dispatch(int S, int T, int H, int K, int E, int R, int Nmax, int is_fp8,
                  const int32_t *expand_pos, uint8_t *staging_x, float *staging_sf,
                  int32_t *staging_meta, uint8_t *recv_x, float *recv_sf,
                  int32_t *recv_src_idx, int32_t *recv_topk_idx, float *recv_topk_weights) {
-    if (!sizes_ok(S, T, K, E, R, Nmax) || H < 1) return -1;
+    if (!sizes_ok(S, T, K, E, R, Nmax) || H < 1 || !topology_ok(S, n_out)) return -1;
     if (is_fp8 && H % 128 != 0) return -1;
     const int El = E / R;
     const size_t Rw = is_fp8 ? (size_t)H : (size_t)H * 2; /* row bytes */
@@ -157,9 +196,9 @@ int epo_dispatch(int S, int T, int H, int K, int E, int R, int Nmax, int is_fp8,
     const size_t M = 1 + 2 * (size_t)K;                     /* metadata words */
 
     /* Scatter: each owner lane copies the token's row, scales and metadata to
-     * row j = slot - s*Nmax of destination d's receive buffer for source s,
-     * a [R][S][Nmax] array of rows ([DET] Direct vs hybrid dispatch: the
-     * direct receive buffer has one Nmax-row region per source rank). */
+     * row j = slot - row_base*Nmax of source s's region in destination d's
+     * receive buffer, R buffers of S regions of Nmax rows ([DET] Direct vs
+     * hybrid dispatch). */
     for (int s = 0; s < S; ++s)
         for (int t = 0; t < T; ++t) {
             const int64_t *tok = topk_idx + ((size_t)s * T + t) * K;
@@ -167,8 +206,8 @@ int epo_dispatch(int S, int T, int H, int K, int E, int R, int Nmax, int is_fp8,
             for (int k = 0; k < K; ++k) {
                 if (!lane_is_owner(tok, k, E, El)) continue;
                 int d = (int)(tok[k] / El);
-                int64_t j = (int64_t)dst_slot[((size_t)s * T + t) * K + k] - (int64_t)s * Nmax;
-                size_t row = ((size_t)d * S + s) * Nmax + (size_t)j;
+                int64_t j = (int64_t)dst_slot[((size_t)s * T + t) * K + k] - row_base(s, S, n_out) * Nmax;
+                size_t row = staging_region(d, s, S, n_out) * Nmax + (size_t)j;
                 memcpy(staging_x + row * Rw, x + ((size_t)s * T + t) * Rw, Rw);
                 if (F) memcpy(staging_sf + row * F, x_sf + ((size_t)s * T + t) * F, F * sizeof(float));
                 int32_t *meta = staging_meta + row * M;
@@ -190,7 +229,7 @@ int epo_dispatch(int S, int T, int H, int K, int E, int R, int Nmax, int is_fp8,
             for (int s = 0; s < S; ++s)
                 for (int j = 0; j < tokens_per_rank[(size_t)s * R + d]; ++j) {
                     size_t i = (size_t)recv_base[d] + (size_t)recv_psum[(size_t)d * (S + 1) + s] + (size_t)j;
-                    size_t row = ((size_t)d * S + s) * Nmax + (size_t)j;
+                    size_t row = staging_region(d, s, S, n_out) * Nmax + (size_t)j;
                     memcpy(recv_x + i * Rw, staging_x + row * Rw, Rw);
                     if (F) memcpy(recv_sf + i * F, staging_sf + row * F, F * sizeof(float));
                     const int32_t *meta = staging_meta + row * M;
@@ -217,8 +256,8 @@ int epo_dispatch(int S, int T, int H, int K, int E, int R, int Nmax, int is_fp8,
                     if (e < 0) continue;
                     int d = (int)(e / El);
                     int k0 = owner_lane(tok, K, E, El, d);
-                    int64_t j = (int64_t)dst_slot[((size_t)s * T + t) * K + k0] - (int64_t)s * Nmax;
-                    size_t row = ((size_t)d * S + s) * Nmax + (size_t)j;
+                    int64_t j = (int64_t)dst_slot[((size_t)s * T + t) * K + k0] - row_base(s, S, n_out) * Nmax;
+                    size_t row = staging_region(d, s, S, n_out) * Nmax + (size_t)j;
                     size_t r = (size_t)expand_pos[((size_t)s * T + t) * K + k];
                     memcpy(recv_x + r * Rw, staging_x + row * Rw, Rw);
                     if (F) memcpy(recv_sf + r * F, staging_sf + row * F, F * sizeof(float));
@@ -275,7 +314,7 @@ uint16_t epo_bf16_from_double(double v) {
 
 /* One token's combine row: acc = sum over valid lanes k (ascending) of
  * w[k] * Y(k) in double, then one rounding to bf16 per element. */
-static void combine_token(int S, int T, int H, int K, int E, int R, int Nmax, int expand,
+static void combine_token(int S, int T, int H, int K, int E, int R, int Nmax, int expand, int n_out,
                           const int64_t *topk_idx, const float *topk_weights,
                           const int32_t *dst_slot, const int32_t *recv_psum,
                           const int32_t *recv_base, const int32_t *expand_pos,
@@ -297,7 +336,7 @@ static void combine_token(int S, int T, int H, int K, int E, int R, int Nmax, in
              * rank weights the same row. */
             int d = (int)(e / El);
             int k0 = owner_lane(tok, K, E, El, d);
-            int64_t j = (int64_t)dst_slot[((size_t)s * T + t) * K + k0] - (int64_t)s * Nmax;
+            int64_t j = (int64_t)dst_slot[((size_t)s * T + t) * K + k0] - row_base(s, S, n_out) * Nmax;
             row = (size_t)recv_base[d] + (size_t)recv_psum[(size_t)d * (S + 1) + s] + (size_t)j;
         }
         const uint16_t *yr = y + row * (size_t)H;
@@ -315,47 +354,47 @@ static void combine_token(int S, int T, int H, int K, int E, int R, int Nmax, in
     for (int h = 0; h < H; ++h) o[h] = epo_bf16_from_double(acc[h]);
 }
 
-int epo_combine(int S, int T, int H, int K, int E, int R, int Nmax, int expand,
+int epo_combine(int S, int T, int H, int K, int E, int R, int Nmax, int expand, int n_out,
                 const int64_t *topk_idx, const float *topk_weights,
                 const int32_t *dst_slot, const int32_t *recv_psum,
                 const int32_t *recv_base, const int32_t *expand_pos,
                 const uint16_t *y, uint16_t *out) {
-    if (!sizes_ok(S, T, K, E, R, Nmax) || H < 1) return -1;
+    if (!sizes_ok(S, T, K, E, R, Nmax) || H < 1 || !topology_ok(S, n_out)) return -1;
     double *acc = (double *)malloc(sizeof(double) * (size_t)H);
     for (int s = 0; s < S; ++s)
         for (int t = 0; t < T; ++t)
-            combine_token(S, T, H, K, E, R, Nmax, expand, topk_idx, topk_weights, dst_slot, recv_psum,
+            combine_token(S, T, H, K, E, R, Nmax, expand, n_out, topk_idx, topk_weights, dst_slot, recv_psum,
                           recv_base, expand_pos, y, NULL, NULL, s, t, acc, out + ((size_t)s * T + t) * H);
     free(acc);
     return 0;
 }
 
-int epo_combine_bias(int S, int T, int H, int K, int E, int R, int Nmax, int expand,
+int epo_combine_bias(int S, int T, int H, int K, int E, int R, int Nmax, int expand, int n_out,
                      const int64_t *topk_idx, const float *topk_weights,
                      const int32_t *dst_slot, const int32_t *recv_psum,
                      const int32_t *recv_base, const int32_t *expand_pos,
                      const uint16_t *y, const uint16_t *bias0, const uint16_t *bias1, uint16_t *out) {
-    if (!sizes_ok(S, T, K, E, R, Nmax) || H < 1) return -1;
+    if (!sizes_ok(S, T, K, E, R, Nmax) || H < 1 || !topology_ok(S, n_out)) return -1;
     double *acc = (double *)malloc(sizeof(double) * (size_t)H);
     for (int s = 0; s < S; ++s)
         for (int t = 0; t < T; ++t)
-            combine_token(S, T, H, K, E, R, Nmax, expand, topk_idx, topk_weights, dst_slot, recv_psum,
+            combine_token(S, T, H, K, E, R, Nmax, expand, n_out, topk_idx, topk_weights, dst_slot, recv_psum,
                           recv_base, expand_pos, y, bias0, bias1, s, t, acc, out + ((size_t)s * T + t) * H);
     free(acc);
     return 0;
 }
 
-int epo_combine_tokens(int S, int T, int H, int K, int E, int R, int Nmax, int expand,
+int epo_combine_tokens(int S, int T, int H, int K, int E, int R, int Nmax, int expand, int n_out,
                        const int64_t *topk_idx, const float *topk_weights,
                        const int32_t *dst_slot, const int32_t *recv_psum,
                        const int32_t *recv_base, const int32_t *expand_pos,
                        const uint16_t *y, int n_sel, const int64_t *sel, uint16_t *out) {
-    if (!sizes_ok(S, T, K, E, R, Nmax) || H < 1 || n_sel < 0) return -1;
+    if (!sizes_ok(S, T, K, E, R, Nmax) || H < 1 || n_sel < 0 || !topology_ok(S, n_out)) return -1;
     double *acc = (double *)malloc(sizeof(double) * (size_t)H);
     for (int i = 0; i < n_sel; ++i) {
         if (sel[i] < 0 || sel[i] >= (int64_t)S * T) { free(acc); return -1; }
         int s = (int)(sel[i] / T), t = (int)(sel[i] % T);
-        combine_token(S, T, H, K, E, R, Nmax, expand, topk_idx, topk_weights, dst_slot, recv_psum,
+        combine_token(S, T, H, K, E, R, Nmax, expand, n_out, topk_idx, topk_weights, dst_slot, recv_psum,
                       recv_base, expand_pos, y, NULL, NULL, s, t, acc, out + (size_t)i * H);
     }
     free(acc);

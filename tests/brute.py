@@ -31,7 +31,21 @@ def token_dests(topk, s, t, K, E, El):
     return {int(topk[s, t, k]) // El for k in range(K) if _valid(int(topk[s, t, k]), E)}
 
 
-def brute_layout(S, T, K, E, R, Nmax, topk, expand=False, A=1) -> Dict[str, np.ndarray]:
+def row_base(s, S, n_out):
+    """Row base of source s: s on the direct path, its scale-out index s // n_up on the hybrid path."""
+    return s // (S // n_out) if n_out > 1 else s
+
+
+def staging_region(d, s, S, n_out):
+    """Region of source s in destination d's staging buffer: d*S + s on the direct
+    path; on the hybrid path segment = scale-up index, then the scale-out index."""
+    if n_out > 1:
+        n_up = S // n_out
+        return (d * n_up + s % n_up) * n_out + s // n_up
+    return d * S + s
+
+
+def brute_layout(S, T, K, E, R, Nmax, topk, expand=False, A=1, n_out=1) -> Dict[str, np.ndarray]:
     """Each output restated literally, by counting (O(T^2), tiny sizes only)."""
     El = E // R
     topk = np.asarray(topk).reshape(S, T, K)
@@ -46,7 +60,7 @@ def brute_layout(S, T, K, E, R, Nmax, topk, expand=False, A=1) -> Dict[str, np.n
                 if any(_valid(int(topk[s, t, k2]), E) and int(topk[s, t, k2]) // El == d for k2 in range(k)):
                     continue  # a lower lane already carries this destination
                 earlier = sum(1 for t2 in range(t) if d in token_dests(topk, s, t2, K, E, El))
-                dst_slot[s, t, k] = s * Nmax + earlier
+                dst_slot[s, t, k] = row_base(s, S, n_out) * Nmax + earlier
     tpr = np.array([[sum(1 for t in range(T) if d in token_dests(topk, s, t, K, E, El)) for d in range(R)]
                     for s in range(S)], np.int64).reshape(S, R)
     tpe = np.array([[sum(1 for t in range(T) for k in range(K) if int(topk[s, t, k]) == e) for e in range(E)]
@@ -56,6 +70,11 @@ def brute_layout(S, T, K, E, R, Nmax, topk, expand=False, A=1) -> Dict[str, np.n
     recv_base = np.array([sum(tpr[s, d2] for s in range(S) for d2 in range(d)) for d in range(R + 1)], np.int64)
     out = dict(dst_slot=dst_slot, tokens_per_rank=tpr, tokens_per_expert=tpe, recv_psum=recv_psum,
                recv_base=recv_base, error_flags=np.array([1 if (topk >= E).any() else 0]))
+    if n_out > 1:
+        n_up = S // n_out
+        out["recv_psum_scaleup"] = np.array(
+            [[sum(tpr[s2, d] for s2 in range(S) if s2 % n_up < u) for u in range(n_up + 1)] for d in range(R)],
+            np.int64)
     if expand:
         cnt = [int(tpe[:, e].sum()) for e in range(E)]
         expert_base = np.array([sum(-(-cnt[e2] // A) * A for e2 in range(e)) for e in range(E + 1)], np.int64)
@@ -72,7 +91,7 @@ def brute_layout(S, T, K, E, R, Nmax, topk, expand=False, A=1) -> Dict[str, np.n
     return out
 
 
-def sorted_layout(S, T, K, E, R, Nmax, topk, expand=False, A=1) -> Dict[str, np.ndarray]:
+def sorted_layout(S, T, K, E, R, Nmax, topk, expand=False, A=1, n_out=1) -> Dict[str, np.ndarray]:
     """The same tables from stable sorts and bincounts (vectorised numpy)."""
     El = E // R
     topk = np.asarray(topk, np.int64).reshape(S, T, K)
@@ -92,7 +111,8 @@ def sorted_layout(S, T, K, E, R, Nmax, topk, expand=False, A=1) -> Dict[str, np.
     start = np.searchsorted(group, group, side="left")
     pos_in_group = np.arange(group.size) - start
     dst_slot = np.full((S, T, K), -1, np.int64)
-    dst_slot[s_idx[order], t_idx[order], k_idx[order]] = s_idx[order] * Nmax + pos_in_group
+    base = np.array([row_base(s, S, n_out) for s in range(S)], np.int64)
+    dst_slot[s_idx[order], t_idx[order], k_idx[order]] = base[s_idx[order]] * Nmax + pos_in_group
     tpr = np.bincount(s_idx * R + d_idx, minlength=S * R).reshape(S, R)
     vs, vt, vk = np.nonzero(valid)
     tpe = np.bincount(vs * E + topk[vs, vt, vk], minlength=S * E).reshape(S, E)
@@ -126,7 +146,7 @@ def assert_tables_equal(got: Dict[str, np.ndarray], want: Dict[str, np.ndarray],
         assert bad.size == 0, f"{key}: {bad.size} mismatches, first at {bad[0]}: got {g[bad[0]]} want {w[bad[0]]}"
 
 
-def check_layout_invariants(S, T, K, E, R, Nmax, topk, lay, expand=False, A=1):
+def check_layout_invariants(S, T, K, E, R, Nmax, topk, lay, expand=False, A=1, n_out=1):
     """Properties that hold at any size (each one a statement of the pages)."""
     El = E // R
     topk = np.asarray(topk, np.int64).reshape(S, T, K)
@@ -148,7 +168,7 @@ def check_layout_invariants(S, T, K, E, R, Nmax, topk, lay, expand=False, A=1):
     for s in range(S):
         for d in range(R):
             sl = np.sort(slot[s][has[s] & (rank[s] == d)])
-            assert (sl == s * Nmax + np.arange(tpr[s, d])).all(), f"(s={s}, d={d}) slots not dense"
+            assert (sl == row_base(s, S, n_out) * Nmax + np.arange(tpr[s, d])).all(), f"(s={s}, d={d}) not dense"
             assert tpr[s, d] <= min(T, Nmax), "a row overflows Nmax"
             # ascending token order inside a row
             ts = np.nonzero((has[s] & (rank[s] == d)).any(axis=1))[0]
@@ -177,7 +197,7 @@ def check_layout_invariants(S, T, K, E, R, Nmax, topk, lay, expand=False, A=1):
             assert (pe == eb[e] + np.arange(cnt[e])).all(), f"expert {e} rows not dense/ordered"
 
 
-def check_dispatch(S, T, H, K, E, R, Nmax, is_fp8, expand, A, inputs, lay, disp, rows_to_check=None):
+def check_dispatch(S, T, H, K, E, R, Nmax, is_fp8, expand, A, inputs, lay, disp, rows_to_check=None, n_out=1):
     """Staging and receive rows against the inputs at the positions the layout fixes."""
     El = E // R
     Rw = H if is_fp8 else 2 * H
@@ -190,14 +210,18 @@ def check_dispatch(S, T, H, K, E, R, Nmax, is_fp8, expand, A, inputs, lay, disp,
     rp = np.asarray(lay["recv_psum"]).reshape(R, S + 1)
     rb = np.asarray(lay["recv_base"]).reshape(R + 1)
     valid = (topk >= 0) & (topk < E)
-    # staging: owner lane (s,t,k) -> row (d, s, slot - s*Nmax)
+    # staging: owner lane (s,t,k) -> row j = slot - row_base*Nmax of source s's region in destination d
+    sx = disp["staging_x"].reshape(R * S, Nmax, disp["staging_x"].shape[-1])
+    ssf = disp["staging_sf"].reshape(R * S, Nmax, disp["staging_sf"].shape[-1])
+    smeta = disp["staging_meta"].reshape(R * S, Nmax, disp["staging_meta"].shape[-1])
     for s, t, k in zip(*np.nonzero(slot >= 0)):
         d = int(topk[s, t, k]) // El
-        j = int(slot[s, t, k]) - s * Nmax
-        assert (disp["staging_x"][d, s, j] == x[s, t]).all(), f"staging_x ({d},{s},{j}) != x[{s},{t}]"
+        j = int(slot[s, t, k]) - row_base(s, S, n_out) * Nmax
+        g = staging_region(d, s, S, n_out)
+        assert (sx[g, j] == x[s, t]).all(), f"staging_x ({d},{s},{j}) != x[{s},{t}]"
         if is_fp8:
-            assert (disp["staging_sf"][d, s, j] == sf[s, t]).all()
-        meta = disp["staging_meta"][d, s, j]
+            assert (ssf[g, j] == sf[s, t]).all()
+        meta = smeta[g, j]
         assert meta[0] == t
         assert (meta[1:1 + K] == np.where(valid[s, t], topk[s, t], -1)).all()
         assert (meta[1 + K:1 + 2 * K] == w[s, t].view(np.int32)).all()

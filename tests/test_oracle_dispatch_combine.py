@@ -235,3 +235,25 @@ def test_bf16_rounding_exact_rational_ties_and_limits():
     assert oracle.bf16_from_double(float("nan")) & 0x7FC0 == 0x7FC0
     assert oracle.bf16_from_double(float("-inf")) == 0xFF80
     assert bf16_bits_to_fraction(0x3F80) == 1 and f32_to_fraction(np.float32(0.5)) == Fraction(1, 2)
+
+
+@pytest.mark.parametrize("expand", [False, True])
+def test_hybrid_dispatch_rows_and_combine(expand):
+    """Hybrid row form: staging rows sit at segment = scale-up index, offset =
+    scale-out index * Nmax + slot; the receive rows and combine are unchanged."""
+    w = Workload("hyb", S=6, T=25, H=64, K=4, E=24, R=6, Nmax=27, n_out=2, expand=expand, alignment=2)
+    d = generate(w, 8, masked_frac=0.1, dup_frac=0.3)
+    lay = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, d["topk_idx"], expand, 2, 2)
+    disp = oracle.dispatch(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, False, expand, 2, d["x"], None, d["topk_idx"],
+                           d["topk_weights"], lay, 2)
+    check_dispatch(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, False, expand, 2, d, lay, disp, n_out=2)
+    dlay = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, d["topk_idx"], expand, 2)
+    ddisp = oracle.dispatch(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, False, expand, 2, d["x"], None, d["topk_idx"],
+                            d["topk_weights"], dlay)
+    rows = oracle.recv_rows(w.S, w.T, w.K, w.E, w.R, lay, expand)
+    assert (disp["recv_x"][:rows] == ddisp["recv_x"][:rows]).all()
+    assert (disp["recv_src_idx"][:rows] == ddisp["recv_src_idx"][:rows]).all()
+    y = draw_expert_outputs(rows, w.H, 3)
+    a = oracle.combine(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, expand, d["topk_idx"], d["topk_weights"], lay, y, 2)
+    b = oracle.combine(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, expand, d["topk_idx"], d["topk_weights"], dlay, y)
+    assert (a == b).all()

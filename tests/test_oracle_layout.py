@@ -177,3 +177,51 @@ def test_property_sweep(S, T, K, R, El, extra, A, seed, expand):
     topk = _rand_topk(rng, S, T, K, E)
     got = oracle.layout(S, T, K, E, R, T + extra, topk, expand, A)
     assert_tables_equal(got, brute_layout(S, T, K, E, R, T + extra, topk, expand, A))
+
+
+# ------------------------------------------------- hybrid row form (n_out > 1)
+
+@pytest.mark.parametrize("seed", range(12))
+def test_hybrid_brute_force(seed):
+    rng = np.random.default_rng(500 + seed)
+    n_out, n_up = int(rng.integers(2, 4)), int(rng.integers(1, 4))
+    S = n_out * n_up
+    R = int(rng.integers(1, 5))
+    E = R * int(rng.integers(1, 3))
+    K, T = int(rng.integers(1, 4)), int(rng.integers(0, 8))
+    topk = _rand_topk(rng, S, T, K, E)
+    got = oracle.layout(S, T, K, E, R, T + 1, topk, bool(seed % 2), 1 + seed % 3, n_out)
+    assert_tables_equal(got, brute_layout(S, T, K, E, R, T + 1, topk, bool(seed % 2), 1 + seed % 3, n_out))
+
+
+def test_hybrid_sort_characterisation_2x8():
+    # the pages' 2 x 8 topology: 16 ranks as 2 scale-out x 8 scale-up
+    w = WORKLOADS[2].with_(S=16, T=256, Nmax=256, n_out=2)
+    d = generate(w, 77, with_x=False)
+    got = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, d["topk_idx"], False, 1, 2)
+    assert_tables_equal(got, sorted_layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, d["topk_idx"], False, 1, 2))
+    check_layout_invariants(w.S, w.T, w.K, w.E, w.R, w.Nmax, d["topk_idx"], got, False, 1, 2)
+    # segment prefix: segment u holds the rows of the sources with scale-up index u
+    n_up = 8
+    tpr = got["tokens_per_rank"]
+    for dd in range(w.R):
+        seg = [tpr[[s for s in range(16) if s % n_up == u], dd].sum() for u in range(n_up)]
+        assert (got["recv_psum_scaleup"][dd] == np.concatenate([[0], np.cumsum(seg)])).all()
+
+
+def test_hybrid_with_one_scaleup_rank_is_the_direct_path():
+    # n_up = 1: the scale-out index is the rank and each segment holds one region,
+    # so slots and staging coincide with the direct path.
+    rng = np.random.default_rng(9)
+    S, T, K, E, R = 4, 30, 4, 16, 4
+    topk = _rand_topk(rng, S, T, K, E)
+    hyb = oracle.layout(S, T, K, E, R, T, topk, False, 1, S)
+    dire = oracle.layout(S, T, K, E, R, T, topk)
+    assert_tables_equal(hyb, dire)
+    assert (hyb["recv_psum_scaleup"][:, 1] == dire["recv_psum"][:, S]).all()
+
+
+def test_hybrid_rejects_indivisible_topology():
+    topk = np.zeros((3, 4, 2), np.int64)
+    with pytest.raises(ValueError):
+        oracle.layout(3, 4, 2, 8, 4, 4, topk, False, 1, 2)   # 3 ranks cannot form 2 scale-out groups

@@ -20,10 +20,16 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "ep_oracle.c")
 
 MUTANTS = {
     "dedup_by_expert_not_rank": ("if (e2 >= 0 && e2 / El == e / El) return 0;", "if (e2 >= 0 && e2 == e) return 0;"),
-    "row_base_uses_T": ("slot[k] = (int32_t)((int64_t)s * Nmax + run[e / El]);",
-                        "slot[k] = (int32_t)((int64_t)s * T + run[e / El]);"),
-    "inclusive_running_count": ("slot[k] = (int32_t)((int64_t)s * Nmax + run[e / El]);",
-                                "slot[k] = (int32_t)((int64_t)s * Nmax + run[e / El] + 1);"),
+    "row_base_uses_T": ("slot[k] = (int32_t)(row_base(s, S, n_out) * Nmax + run[e / El]);",
+                        "slot[k] = (int32_t)(row_base(s, S, n_out) * T + run[e / El]);"),
+    "inclusive_running_count": ("slot[k] = (int32_t)(row_base(s, S, n_out) * Nmax + run[e / El]);",
+                                "slot[k] = (int32_t)(row_base(s, S, n_out) * Nmax + run[e / El] + 1);"),
+    "hybrid_row_base_is_rank": ("return n_out > 1 ? s / (S / n_out) : s;", "return s;"),
+    "hybrid_segment_by_scaleout": (
+        "return ((size_t)d * n_up + (size_t)(s % n_up)) * (size_t)n_out + (size_t)(s / n_up);",
+        "return ((size_t)d * n_out + (size_t)(s / n_up)) * (size_t)n_up + (size_t)(s % n_up);"),
+    "hybrid_segment_psum_wrong_key": ("if (s % n_up == u) seg += tokens_per_rank[(size_t)s * R + d];",
+                                      "if (s / n_out == u) seg += tokens_per_rank[(size_t)s * R + d];"),
     "psum_drops_carry": ("ps[s + 1] = ps[s] + tokens_per_rank[(size_t)s * R + d];",
                          "ps[s + 1] = tokens_per_rank[(size_t)s * R + d];"),
     "recv_base_wrong_column": ("recv_base[d + 1] = recv_base[d] + recv_psum[(size_t)d * (S + 1) + S];",
@@ -67,6 +73,18 @@ def pin_suite():
         for expand, A in ((False, 1), (True, 1 + seed % 3)):
             got = oracle.layout(S, T, K, E, R, T + 2, topk, expand, A)
             assert_tables_equal(got, brute_layout(S, T, K, E, R, T + 2, topk, expand, A))
+    for n_out, n_up in ((2, 3), (3, 2)):
+        rng = np.random.default_rng(n_out)
+        S, T, K, E, R = n_out * n_up, 6, 3, 12, 6
+        topk = rng.integers(-1, E + 1, size=(S, T, K)).astype(np.int64)
+        got = oracle.layout(S, T, K, E, R, T + 1, topk, False, 1, n_out)
+        assert_tables_equal(got, brute_layout(S, T, K, E, R, T + 1, topk, False, 1, n_out))
+        wh = Workload("h", S=S, T=T, H=64, K=K, E=E, R=R, Nmax=T + 1, n_out=n_out)
+        d = generate(wh, 5, masked_frac=0.2, dup_frac=0.3)
+        lay = oracle.layout(S, T, K, E, R, T + 1, d["topk_idx"], False, 1, n_out)
+        disp = oracle.dispatch(S, T, 64, K, E, R, T + 1, False, False, 1, d["x"], None, d["topk_idx"],
+                               d["topk_weights"], lay, n_out)
+        check_dispatch(S, T, 64, K, E, R, T + 1, False, False, 1, d, lay, disp, n_out=n_out)
     rng = np.random.default_rng(99)
     topk = rng.integers(-1, 40, size=(2, 200, 6)).astype(np.int64)
     got = oracle.layout(2, 200, 6, 40, 8, 200, topk, True, 2)
