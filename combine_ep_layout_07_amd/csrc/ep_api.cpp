@@ -29,8 +29,10 @@ int make_shape(const ep_config_t *c, ep::Shape *sh) {
     if ((c->flags & ~EP_FLAG_DIRECT_RECV_X) != 0) return EP_ERR_INVALID_ARG;
     if ((c->flags & EP_FLAG_DIRECT_RECV_X) && c->expand) return EP_ERR_UNSUPPORTED;
     if (c->num_src_ranks < 1 || c->num_tokens < 0 || c->hidden < 1 || c->num_topk < 1 || c->num_experts < 1 ||
-        c->num_ranks < 1 || c->num_max_tokens_per_rank < 0 || c->num_layout_cus < 0 || c->expert_alignment < 1)
+        c->num_ranks < 1 || c->num_max_tokens_per_rank < 0 || c->num_layout_cus < 0 || c->expert_alignment < 1 ||
+        c->num_scaleout_ranks < 0)
         return EP_ERR_INVALID_ARG;
+    if (c->num_scaleout_ranks > 1 && c->num_src_ranks % c->num_scaleout_ranks != 0) return EP_ERR_INVALID_ARG;
     if (c->x_dtype != EP_DTYPE_BF16 && c->x_dtype != EP_DTYPE_FP8_E4M3FN) return EP_ERR_INVALID_ARG;
     if (c->expand != 0 && c->expand != 1) return EP_ERR_INVALID_ARG;
     if (c->num_experts % c->num_ranks != 0) return EP_ERR_INVALID_ARG;
@@ -61,6 +63,8 @@ int make_shape(const ep_config_t *c, ep::Shape *sh) {
     sh->bits_R = bits_for(c->num_ranks);
     sh->bits_E = bits_for(c->num_experts);
     sh->direct = (c->flags & EP_FLAG_DIRECT_RECV_X) ? 1 : 0;
+    sh->n_out = c->num_scaleout_ranks > 1 ? c->num_scaleout_ranks : 1;
+    sh->n_up = c->num_src_ranks / sh->n_out;
     return EP_OK;
 }
 
@@ -79,8 +83,10 @@ int check_layout_ptrs(const ep::Shape &sh, const ep_layout_t *L) {
         !L->recv_psum_dev || !L->recv_base_dev || !L->error_flags_dev || !L->scratch_dev)
         return EP_ERR_INVALID_ARG;
     if (sh.expand && (!L->expert_base_dev || (need_tok && !L->expand_pos_dev))) return EP_ERR_INVALID_ARG;
+    if (sh.n_out > 1 && !L->recv_psum_scaleup_dev) return EP_ERR_INVALID_ARG;
     const void *ps[] = {L->dst_slot_dev, L->tokens_per_rank_dev, L->tokens_per_expert_dev, L->recv_psum_dev,
-                        L->recv_base_dev, L->expert_base_dev, L->expand_pos_dev, L->error_flags_dev, L->scratch_dev};
+                        L->recv_base_dev, L->expert_base_dev, L->expand_pos_dev, L->error_flags_dev, L->scratch_dev,
+                        L->recv_psum_scaleup_dev};
     for (const void *p : ps)
         if (!aligned(p, 4)) return EP_ERR_INVALID_ARG;
     return EP_OK;
@@ -120,6 +126,7 @@ int ep_query_sizes(const ep_config_t *cfg, ep_sizes_t *sz) {
     sz->expand_pos = sh.expand ? S * T * K * i4 : 0;
     sz->error_flags = i4;
     sz->layout_scratch = ep::layout_scratch_bytes(sh, ep::layout_geometry(sh, cfg->num_layout_cus));
+    sz->recv_psum_scaleup = sh.n_out > 1 ? R * ((uint64_t)sh.n_up + 1) * i4 : 0;
     const uint64_t staging_rows = R * S * Nmax;
     sz->staging_x = sh.direct ? 0 : staging_rows * (uint64_t)sh.row_bytes;
     sz->staging_sf = staging_rows * (uint64_t)sh.sf_per_row * sizeof(float);
@@ -154,6 +161,7 @@ int ep_layout(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layo
     a.expert_base = layout->expert_base_dev;
     a.expand_pos = layout->expand_pos_dev;
     a.error_flags = layout->error_flags_dev;
+    a.recv_psum_scaleup = layout->recv_psum_scaleup_dev;
     const int64_t units = (int64_t)sh.S * a.g.blocks_per_src;
     a.blk_cnt_rank = static_cast<int32_t *>(layout->scratch_dev);
     a.blk_cnt_expert = a.blk_cnt_rank + units * sh.R;

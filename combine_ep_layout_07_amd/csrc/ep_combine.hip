@@ -119,7 +119,8 @@ __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
             const uint64_t peers = match_key((uint32_t)d, sh.bits_R, vmask);
             const int owner = peers ? __builtin_ctzll(peers) : 0;
             const bool is_owner = valid && owner == lane;
-            if (is_owner) row = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s] + (slot - s * sh.Nmax);
+            if (is_owner)
+                row = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s] + (slot - row_base(sh, s) * sh.Nmax);
             for (uint64_t m = vmask; m; m &= m - 1) {
                 const int k = __builtin_ctzll(m);
                 const float wk = __int_as_float(read_lane(__float_as_int(w), k));

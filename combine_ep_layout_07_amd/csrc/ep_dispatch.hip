@@ -112,7 +112,7 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
             for (uint64_t m = owners; m; m &= m - 1) {
                 const int k = __builtin_ctzll(m);
                 const int d = read_lane(e, k) / sh.El;
-                const int j = read_lane(slot, k) - s * sh.Nmax;
+                const int j = read_lane(slot, k) - row_base(sh, s) * sh.Nmax;
                 if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for a layout of this topk_idx
                 if (sh.direct) {
                     // Direct Recv X: the compact receive row of (d, s, j).
@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
                         if (c < c_hi) st16<EP_DIRECT_NT_STORE>(dst + (int64_t)c * 16, v[q]);
                     }
                 } else {
-                    uint8_t *dst = a.staging_x + (((int64_t)d * sh.S + s) * sh.Nmax + j) * sh.row_bytes;
+                    uint8_t *dst = a.staging_x + (staging_region(sh, d, s) * sh.Nmax + j) * sh.row_bytes;
 #pragma unroll
                     for (int q = 0; q < CPL; ++q) {
                         const int c = c0 + q * kWave + lane;
@@ -147,9 +147,9 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
         for (uint64_t m = owners; m; m &= m - 1) {
             const int k = __builtin_ctzll(m);
             const int d = read_lane(e, k) / sh.El;
-            const int j = read_lane(slot, k) - s * sh.Nmax;
+            const int j = read_lane(slot, k) - row_base(sh, s) * sh.Nmax;
             if ((unsigned)j >= (unsigned)sh.Nmax) continue;
-            const int64_t row = ((int64_t)d * sh.S + s) * sh.Nmax + j;
+            const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
             for (int i = lane; i < sh.sf_per_row; i += kWave)
                 a.staging_sf[row * sh.sf_per_row + i] = a.x_sf[g * sh.sf_per_row + i];
             if (lane < sh.meta_words) a.staging_meta[row * sh.meta_words + lane] = word0;
@@ -209,7 +209,7 @@ __global__ void __launch_bounds__(kThreads) k_epilogue(DispatchArgs a, int table
         int d, s, j;
         locate_row(rbase, rpsum, sh.R, sh.S, i, lane, d, s, j);
         if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for tables of one layout
-        const int64_t row = ((int64_t)d * sh.S + s) * sh.Nmax + j;
+        const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
         const uint8_t *src = a.staging_x + row * sh.row_bytes;
         uint8_t *dst = a.recv_x + (int64_t)i * sh.row_bytes;
         // Direct Recv X: the scatter already wrote the hidden row in place.
@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_expand(DispatchArgs a, in
         int d, s, j;
         locate_row(rbase, rpsum, sh.R, sh.S, i, lane, d, s, j);
         if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for tables of one layout
-        const int64_t row = ((int64_t)d * sh.S + s) * sh.Nmax + j;
+        const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
         const int32_t *meta = a.staging_meta + row * sh.meta_words;
         const int t = meta[0];
         int pos = -1, wbits = 0;

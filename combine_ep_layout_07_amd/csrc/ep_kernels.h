@@ -18,7 +18,20 @@ struct Shape {
     int meta_words;  // 1 + 2K
     int bits_R, bits_E;  // key widths for ballot matching of ranks / experts
     int direct;          // Direct Recv X: hidden rows go straight to recv_x
+    int n_out, n_up;     // hybrid row form when n_out > 1: rank s = (s / n_up, s % n_up)
 };
+
+// Row base of source s: the source itself on the direct path, its scale-out
+// index on the hybrid path.
+__host__ __device__ inline int row_base(const Shape &sh, int s) { return sh.n_out > 1 ? s / sh.n_up : s; }
+
+// Region (of Nmax rows) that source s fills in destination d's staging rows:
+// d*S + s on the direct path; in the hybrid row form, segment = scale-up
+// index, then the scale-out index inside the segment.
+__host__ __device__ inline int64_t staging_region(const Shape &sh, int d, int s) {
+    if (sh.n_out > 1) return ((int64_t)d * sh.n_up + s % sh.n_up) * sh.n_out + s / sh.n_up;
+    return (int64_t)d * sh.S + s;
+}
 
 // Layout pass geometry: B workgroups per source, each owning `chunk` tokens
 // (split into 4 equal wave ranges of chunk/4 tokens).
@@ -36,6 +49,7 @@ struct LayoutArgs {
     const int64_t *topk_idx;
     int32_t *dst_slot, *tokens_per_rank, *tokens_per_expert, *recv_psum, *recv_base;
     int32_t *expert_base, *expand_pos, *error_flags;
+    int32_t *recv_psum_scaleup;  // hybrid only
     int32_t *blk_cnt_rank;    // scratch [S*B][R]
     int32_t *blk_cnt_expert;  // scratch [S*B][E]
     int32_t *blk_flags;       // scratch [S*B]

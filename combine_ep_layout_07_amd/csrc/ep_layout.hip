@@ -380,13 +380,13 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
     {
         int *run_d = cnt_d + w * R;
         int *run_e = cnt_e + w * E;
-        const int32_t row_base = s * sh.Nmax;  // direct path: one Nmax-row region per source
+        const int32_t slot_base = row_base(sh, s) * sh.Nmax;  // row_base * Nmax ([DET] Approach)
         auto rank = [&](const Item &it) {
             const int rd = it.owner ? run_d[it.d] : 0;
             const int re = (expand && it.valid) ? run_e[it.e] : 0;
             if (it.in) {
                 const int64_t idx = ((int64_t)s * sh.T + it.t) * sh.K + it.k;
-                a.dst_slot[idx] = it.owner ? row_base + rd + it.rank_d : -1;
+                a.dst_slot[idx] = it.owner ? slot_base + rd + it.rank_d : -1;
                 if (expand) a.expand_pos[idx] = it.valid ? re + it.rank_e : -1;
             }
             if (it.last_d) run_d[it.d] = rd + it.rank_d + 1;
@@ -438,6 +438,20 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
             }
             a.recv_psum[(int64_t)d * (S + 1) + S] = run;
             tot_d[d] = run;
+            if (sh.n_out > 1) {
+                // Hybrid row form: prefix over scale-up segments; segment u
+                // holds the sources s with s % n_up == u.
+                int32_t *ps = a.recv_psum_scaleup + (int64_t)d * (sh.n_up + 1);
+                int seg_run = 0;
+                for (int u = 0; u < sh.n_up; ++u) {
+                    ps[u] = seg_run;
+                    for (int o = 0; o < sh.n_out; ++o) {
+                        const int q = o * sh.n_up + u;
+                        seg_run += a.recv_psum[(int64_t)d * (S + 1) + q + 1] - a.recv_psum[(int64_t)d * (S + 1) + q];
+                    }
+                }
+                ps[sh.n_up] = seg_run;
+            }
         }
         int bad = 0;
         for (int64_t q = tid; q < U; q += kLayoutThreads) bad |= a.blk_flags[q];

@@ -38,13 +38,14 @@ class EpError(RuntimeError):
 class EpConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_src_ranks", "num_tokens", "hidden", "num_topk", "num_experts", "num_ranks",
-        "num_max_tokens_per_rank", "x_dtype", "expand", "expert_alignment", "num_layout_cus", "flags")]
+        "num_max_tokens_per_rank", "x_dtype", "expand", "expert_alignment", "num_layout_cus", "flags",
+        "num_scaleout_ranks")]
 
 
 class EpSizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "dst_slot", "tokens_per_rank", "tokens_per_expert", "recv_psum", "recv_base",
-        "expert_base", "expand_pos", "error_flags", "layout_scratch",
+        "expert_base", "expand_pos", "error_flags", "layout_scratch", "recv_psum_scaleup",
         "staging_x", "staging_sf", "staging_meta", "recv_rows",
         "recv_x", "recv_sf", "recv_src_idx", "recv_topk_idx", "recv_topk_weights", "y", "out")]
 
@@ -52,7 +53,7 @@ class EpSizes(ctypes.Structure):
 class EpLayoutT(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "dst_slot_dev", "tokens_per_rank_dev", "tokens_per_expert_dev", "recv_psum_dev", "recv_base_dev",
-        "expert_base_dev", "expand_pos_dev", "error_flags_dev", "scratch_dev")]
+        "expert_base_dev", "expand_pos_dev", "error_flags_dev", "scratch_dev", "recv_psum_scaleup_dev")]
 
 
 class EpRecvT(ctypes.Structure):
@@ -92,15 +93,16 @@ def ep_version() -> int:
 
 def make_config(S: int, T: int, H: int, K: int, E: int, R: int, Nmax: int, dtype: str = "bf16",
                 expand: bool = False, alignment: int = 1, num_layout_cus: int = 0,
-                direct_recv_x: bool = False) -> EpConfig:
+                direct_recv_x: bool = False, num_scaleout_ranks: int = 1) -> EpConfig:
     return EpConfig(S, T, H, K, E, R, Nmax, EP_DTYPE_FP8_E4M3FN if dtype == "fp8" else EP_DTYPE_BF16,
-                    int(bool(expand)), alignment, num_layout_cus, EP_FLAG_DIRECT_RECV_X if direct_recv_x else 0)
+                    int(bool(expand)), alignment, num_layout_cus, EP_FLAG_DIRECT_RECV_X if direct_recv_x else 0,
+                    num_scaleout_ranks)
 
 
 def config_for(w, num_layout_cus: int = 0, direct_recv_x: bool = False) -> EpConfig:
     """EpConfig of a ``workloads.Workload``."""
     return make_config(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.dtype, w.expand, w.alignment, num_layout_cus,
-                       direct_recv_x)
+                       direct_recv_x, getattr(w, "n_out", 1))
 
 
 def ep_query_sizes(cfg: EpConfig) -> EpSizes:
@@ -155,12 +157,14 @@ class LayoutBuffers:
         self.expand_pos = torch.empty((S, T, K), **i32) if cfg.expand else None
         self.error_flags = torch.zeros((1,), **i32)
         self.scratch = _empty(sz.layout_scratch, torch.int32, device)
+        n_out = cfg.num_scaleout_ranks
+        self.recv_psum_scaleup = torch.empty((R, S // n_out + 1), **i32) if n_out > 1 else None
         self.struct = EpLayoutT(
             _ptr(self.dst_slot, "dst_slot"), _ptr(self.tokens_per_rank, "tokens_per_rank"),
             _ptr(self.tokens_per_expert, "tokens_per_expert"), _ptr(self.recv_psum, "recv_psum"),
             _ptr(self.recv_base, "recv_base"), _ptr(self.expert_base, "expert_base"),
             _ptr(self.expand_pos, "expand_pos"), _ptr(self.error_flags, "error_flags"),
-            _ptr(self.scratch, "scratch"))
+            _ptr(self.scratch, "scratch"), _ptr(self.recv_psum_scaleup, "recv_psum_scaleup"))
 
     def tables(self):
         out = dict(dst_slot=self.dst_slot, tokens_per_rank=self.tokens_per_rank,
@@ -168,6 +172,8 @@ class LayoutBuffers:
                    error_flags=self.error_flags)
         if self.expert_base is not None:
             out.update(expert_base=self.expert_base, expand_pos=self.expand_pos)
+        if self.recv_psum_scaleup is not None:
+            out.update(recv_psum_scaleup=self.recv_psum_scaleup)
         return out
 
 

@@ -104,6 +104,18 @@ typedef struct ep_config {
                                          (the pages' num_prologue_sms, [DET] New
                                          API); never changes any result          */
     int32_t flags;                    /* enum ep_flags bits; others must be 0    */
+    int32_t num_scaleout_ranks;       /* 0 or 1: direct path.  > 1: hybrid path
+                                         ([DET] Direct vs hybrid dispatch): the
+                                         S source ranks are num_scaleout_ranks x
+                                         num_scaleup_ranks, rank s = (s / n_up,
+                                         s % n_up); S must be a multiple.  The
+                                         row base of a slot is the sender's
+                                         scale-out index, and a destination's
+                                         staging buffer is read in row form:
+                                         segment = scale-up index, offset =
+                                         scale-out index * Nmax + row slot.
+                                         Receive rows are the same as on the
+                                         direct path.                            */
 } ep_config_t;
 
 /* Byte sizes of every caller-allocated buffer for a configuration (0 = not
@@ -112,7 +124,7 @@ typedef struct ep_config {
  * reach; S*T*K + E*(A-1) for expand. */
 typedef struct ep_sizes {
     uint64_t dst_slot, tokens_per_rank, tokens_per_expert, recv_psum, recv_base;
-    uint64_t expert_base, expand_pos, error_flags, layout_scratch;
+    uint64_t expert_base, expand_pos, error_flags, layout_scratch, recv_psum_scaleup;
     uint64_t staging_x, staging_sf, staging_meta;
     uint64_t recv_rows;
     uint64_t recv_x, recv_sf, recv_src_idx, recv_topk_idx, recv_topk_weights;
@@ -121,11 +133,12 @@ typedef struct ep_sizes {
 
 /* Layout tables ("handle"): written by ep_layout, read by ep_dispatch and
  * ep_combine.  All device pointers, int32:
- *   dst_slot          [S][T][K]  s*Nmax + the number of earlier tokens of
- *                                source s that reach the same destination,
+ *   dst_slot          [S][T][K]  row_base*Nmax + the number of earlier tokens
+ *                                of source s that reach the same destination,
  *                                on the lowest valid lane of each destination
  *                                of a token; -1 on every other lane
- *                                ([DET] Motivation and Approach)
+ *                                ([DET] Motivation and Approach); row_base is
+ *                                s (direct) or s / n_up (hybrid)
  *   tokens_per_rank   [S][R]     deduplicated tokens source s sends to rank d
  *   tokens_per_expert [S][E]     valid lanes of source s routed to expert e
  *   recv_psum         [R][S+1]   exclusive prefix over sources of
@@ -139,6 +152,10 @@ typedef struct ep_sizes {
  *                                padded to a multiple of A
  *   expand_pos        [S][T][K]  expand only: receive row of a valid lane
  *                                (ascending (s,t,k) inside the expert), else -1
+ *   recv_psum_scaleup [R][n_up+1] hybrid only: per destination, exclusive
+ *                                prefix over scale-up segments of the rows
+ *                                each segment holds (the per-segment part of
+ *                                the pages' extended psum)
  *   error_flags       [1]        bit 0: some top-k id was >= E
  *   scratch           bytes      ep_sizes_t.layout_scratch, private to the
  *                                library; contents need no initialisation  */
@@ -152,11 +169,13 @@ typedef struct ep_layout {
     int32_t *expand_pos_dev;    /* NULL unless expand */
     int32_t *error_flags_dev;
     void *scratch_dev;
+    int32_t *recv_psum_scaleup_dev; /* NULL unless hybrid */
 } ep_layout_t;
 
 /* Staging ([R][S][Nmax] rows: destination d's receive buffer holds one Nmax-row
  * region per source, [DET] Direct vs hybrid dispatch) and receive buffers.
- *   staging_x     [R][S][Nmax][row bytes]
+ *   staging_x     [R][S][Nmax][row bytes]; on the hybrid path the S regions
+ *                 of a destination are ordered [n_up segments][n_out]
  *   staging_sf    [R][S][Nmax][H/128] fp32 (fp8 only, else NULL)
  *   staging_meta  [R][S][Nmax][1+2K] int32: token index t, the token's K
  *                 expert ids (masked/invalid as -1), the K weights' fp32 bits

@@ -50,10 +50,16 @@ def compare_tables(got: Dict[str, np.ndarray], want: Dict[str, np.ndarray]):
 
 
 def filled_staging_mask(w, lay) -> np.ndarray:
-    """[R][S][Nmax] mask of the staging rows the layout fills (j < tokens_per_rank[s][d])."""
+    """[R][S][Nmax] mask of the staging rows the layout fills: j < tokens_per_rank
+    of the source whose region it is (regions reordered on the hybrid path)."""
+    from tests.brute import staging_region
     tpr = np.asarray(lay["tokens_per_rank"]).reshape(w.S, w.R)
+    cnt = np.zeros((w.R * w.S,), np.int64)
+    for d in range(w.R):
+        for s in range(w.S):
+            cnt[staging_region(d, s, w.S, w.n_out)] = tpr[s, d]
     j = np.arange(w.Nmax)[None, None, :]
-    return j < tpr.T[:, :, None]
+    return j < cnt.reshape(w.R, w.S)[:, :, None]
 
 
 def compare_dispatch(w, lay, gpu: "ep.RecvBuffers", want: Dict[str, np.ndarray], direct: bool = False):

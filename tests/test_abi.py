@@ -56,7 +56,7 @@ def test_struct_layouts_match_header():
     assert members("ep_sizes") == len(ep.EpSizes._fields_)
     assert members("ep_layout") == len(ep.EpLayoutT._fields_)
     assert members("ep_recv") == len(ep.EpRecvT._fields_)
-    assert ctypes.sizeof(ep.EpConfig) == 12 * 4
+    assert ctypes.sizeof(ep.EpConfig) == 13 * 4
 
 
 def _rc(cfg):
@@ -86,6 +86,17 @@ def test_validation_codes(kw, code):
                          False, A)
     assert _rc(cfg) == code
     assert ep.ep_status_string(code)
+
+
+def test_hybrid_topology_validation():
+    # S must be a multiple of num_scaleout_ranks; 0 and 1 both mean the direct path
+    assert _rc(ep.make_config(6, 16, 64, 2, 8, 4, 16, num_scaleout_ranks=4)) == ep.EP_ERR_INVALID_ARG
+    assert _rc(ep.make_config(6, 16, 64, 2, 8, 4, 16, num_scaleout_ranks=-1)) == ep.EP_ERR_INVALID_ARG
+    h = ep.ep_query_sizes(ep.make_config(16, 256, 7168, 8, 256, 16, 256, num_scaleout_ranks=2))
+    d = ep.ep_query_sizes(ep.make_config(16, 256, 7168, 8, 256, 16, 256, num_scaleout_ranks=1))
+    z = ep.ep_query_sizes(ep.make_config(16, 256, 7168, 8, 256, 16, 256, num_scaleout_ranks=0))
+    assert h.recv_psum_scaleup == 16 * (8 + 1) * 4 and d.recv_psum_scaleup == 0 and z.recv_psum_scaleup == 0
+    assert h.staging_x == d.staging_x and h.recv_rows == d.recv_rows
 
 
 def test_flags_validation():

@@ -28,7 +28,7 @@ def _full_case(w, seed, edge=None, num_layout_cus=0, check_combine=True, combine
     say(f"[case] {w.name} S={w.S} T={w.T} H={w.H} K={w.K} E={w.E} R={w.R} Nmax={w.Nmax} {w.dtype} "
         f"expand={w.expand} A={w.alignment} seed={seed} edge={edge} cus={num_layout_cus} direct={direct}")
     inputs = generate(w, seed, **edge)
-    lay_o = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment)
+    lay_o = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment, w.n_out)
     dev = upload(w, inputs)
     say("  ep_layout")
     cfg, L = run_layout(w, dev, num_layout_cus, direct)
@@ -38,7 +38,8 @@ def _full_case(w, seed, edge=None, num_layout_cus=0, check_combine=True, combine
     ep.ep_dispatch(cfg, dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_weights"], L, R)
     torch.cuda.synchronize()
     want = oracle.dispatch(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.dtype == "fp8", w.expand, w.alignment,
-                           inputs["x"], inputs.get("x_sf"), inputs["topk_idx"], inputs["topk_weights"], lay_o)
+                           inputs["x"], inputs.get("x_sf"), inputs["topk_idx"], inputs["topk_weights"], lay_o,
+                           w.n_out)
     compare_dispatch(w, lay_o, R, want, direct)
     del want
     if not check_combine:
@@ -53,13 +54,13 @@ def _full_case(w, seed, edge=None, num_layout_cus=0, check_combine=True, combine
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)
     if combine_sample is None:
         ref = oracle.combine(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.expand, inputs["topk_idx"],
-                             inputs["topk_weights"], lay_o, y_h).reshape(-1, w.H)
+                             inputs["topk_weights"], lay_o, y_h, w.n_out).reshape(-1, w.H)
         share = compare_combine(got, ref)
     else:
         rng = np.random.default_rng(seed)
         sel = np.sort(rng.choice(w.S * w.T, size=min(combine_sample, w.S * w.T), replace=False))
         ref = oracle.combine_tokens(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.expand, inputs["topk_idx"],
-                                    inputs["topk_weights"], lay_o, y_h, sel)
+                                    inputs["topk_weights"], lay_o, y_h, sel, w.n_out)
         share = compare_combine(got[sel], ref)
     say(f"  combine bit-equal share {share:.6f}")
     assert share > 0.99
@@ -157,6 +158,24 @@ def test_cached_layout_replay():
         want = oracle.dispatch(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, True, False, 1, x_np, sf_np,
                                inputs["topk_idx"], inputs["topk_weights"], lay_o)
         compare_dispatch(w, lay_o, R, want)
+
+
+HYBRID = [
+    # the deterministic-dispatch page's 2 x 8 topology (EP16 over two scale-out groups)
+    Workload("hybrid_2x8", S=16, T=512, H=7168, K=8, E=256, R=16, Nmax=512, n_out=2),
+    Workload("hybrid_3x2_edge", S=6, T=97, H=264, K=6, E=24, R=6, Nmax=100, n_out=3),
+    Workload("hybrid_2x2_fp8_expand", S=4, T=80, H=256, K=4, E=16, R=4, Nmax=80, n_out=2, dtype="fp8", expand=True,
+             alignment=4),
+]
+
+
+@pytest.mark.parametrize("w", HYBRID, ids=lambda w: w.name)
+def test_hybrid_row_form(w):
+    _full_case(w, 19, EDGE if "edge" in w.name else None)
+
+
+def test_hybrid_direct_recv_x():
+    _full_case(HYBRID[0], 21, direct=True, check_combine=False)
 
 
 def test_error_flag_for_out_of_range_ids():
