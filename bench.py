@@ -194,6 +194,7 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-direct", action="store_true", help="skip the Direct Recv X variant")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (the reference for the byte counters)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
@@ -310,6 +311,33 @@ def main():
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(epi_gbps / PEAK_HBM_GBPS, 4),
                      "alg_bytes_per_launch": epi_alg, "traffic": traffic},
     }
+    if not args.no_graph:
+        # The same step captured once in a HIP graph and replayed K times.
+        print("[bench] graph replay", file=sys.stderr, flush=True)
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs):
+            step_on = lambda: (ep.ep_layout(cfg, topk, L, gs),  # noqa: E731
+                               ep.ep_dispatch(cfg, x, x_sf, topk, wts, L, R, ep.EP_PHASE_ALL, gs),
+                               ep.ep_combine(cfg, L, topk, wts, y, out, gs))
+            step_on()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=gs):
+                step_on()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_g = g0.elapsed_time(g1) / args.steps
+        res["graph_replay"] = {"value": round(b["total"] / (ms_g * 1e-3) / 1e9, 2), "unit": "GB/s",
+                               "ms_per_step": round(ms_g, 5), "tokens_per_s": round(w.S * w.T / (ms_g * 1e-3), 1)}
     if not w.expand and not args.no_direct:
         # Direct Recv X (the scatter writes hidden rows straight into recv_x):
         # a different byte count, reported beside the headline, never as it.
