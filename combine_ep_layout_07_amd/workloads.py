@@ -73,6 +73,8 @@ def sf_per_row(w: Workload) -> int:
 
 def _route(w: Workload, rng: np.random.Generator) -> np.ndarray:
     n = w.S * w.T
+    if w.K > w.E:
+        raise ValueError(f"{w.K} distinct experts per token need E >= K (E = {w.E})")
     if w.routing == "uniform":
         # K distinct experts, uniform: the first K of a random permutation per token.
         keys = rng.random((n, w.E))

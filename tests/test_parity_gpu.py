@@ -317,3 +317,29 @@ def test_graph_replay_matches_eager(cfg_id):
         got = (L.dst_slot, R.recv_x[:n], R.recv_topk_weights[:n], out)
         for a_, b_ in zip(got, ref):
             assert torch.equal(a_, b_), f"replay {rep} differs from the eager step"
+
+
+def _random_workload(rng):
+    R = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
+    El = int(rng.choice([1, 2, 3, 4, 8]))
+    K = int(rng.integers(1, 9))
+    El = max(El, -(-K // R))  # distinct experts per token need K <= E
+    n_out = int(rng.choice([1, 1, 2, 3]))
+    S = n_out * int(rng.integers(1, 4))
+    T = int(rng.integers(0, 200))
+    dtype = "fp8" if rng.random() < 0.3 else "bf16"
+    H = int(rng.choice([128, 256, 384])) if dtype == "fp8" else int(rng.choice([8, 64, 136, 512, 1032]))
+    expand = bool(rng.random() < 0.3)
+    return Workload(f"rand", S=S, T=T, H=H, K=K, E=R * El, R=R, Nmax=T + int(rng.integers(0, 5)), dtype=dtype,
+                    expand=expand, alignment=int(rng.choice([1, 2, 8])) if expand else 1, n_out=n_out)
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_small_configurations(seed):
+    """Random shapes, dtypes, layouts, topologies and edge lanes against the oracle."""
+    rng = np.random.default_rng(9000 + seed)
+    w = _random_workload(rng)
+    direct = (not w.expand) and rng.random() < 0.4
+    edge = dict(masked_frac=float(rng.random() * 0.3), invalid_frac=float(rng.random() * 0.05),
+                dup_frac=float(rng.random() * 0.4))
+    _full_case(w, 100 + seed, edge, num_layout_cus=int(rng.choice([0, 0, 1, 5])), direct=direct)
