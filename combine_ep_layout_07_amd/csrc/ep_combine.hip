@@ -3,10 +3,10 @@
 // kernels for transports without ordered delivery" (PR #732), section
 // Changes).
 //
-// out[s][t] = bf16(sum over valid lanes k of w[s][t][k] * Y), accumulated in
-// fp32 and rounded to nearest-even once.  In the compact layout Y is the
-// receive row that the owner lane of the lane's rank was given
-// (recv_base[d] + recv_psum[d][s] + slot - s*Nmax), so lanes sharing a rank
+// out[s][t] = bf16(sum over valid lanes k of w[s][t][k] * Y [+ bias rows]),
+// accumulated in fp32 and rounded to nearest-even once.  In the compact layout
+// Y is the receive row that the owner lane of the lane's rank was given
+// (recv_base[d] + recv_psum[d][s] + slot - row_base(s)*Nmax), so lanes sharing a rank
 // weight the same row: the kernel reads that row once and applies the fp32
 // sum of those lanes' weights (taken in lane order).  In the expand layout Y
 // is the lane's own row expand_pos[s][t][k].

@@ -12,7 +12,9 @@
 // send is a local store.  Both kernels are pure HBM streams: one wavefront per
 // row, each lane moving 16-byte chunks c = lane + 64*i, the whole row (or a
 // CPL-chunk slice of it) loaded into VGPRs before any store, so every lane has
-// CPL independent 16-byte loads in flight.
+// CPL independent 16-byte loads in flight.  On the hybrid path the same
+// kernels address a destination's staging rows in row form (segment = the
+// source's scale-up index, then its scale-out index), through staging_region.
 #include "ep_device.h"
 #include "ep_kernels.h"
 
@@ -64,8 +66,10 @@ __device__ __forceinline__ void st16(uint8_t *p, u32x4 v) {
 }
 
 // ----------------------------------------------------------------- scatter
-// One wave per token (s, t): load the row once, store it to the staging row
-// (d, s, slot - s*Nmax) of every owner lane, with the fp8 scales and the
+// One wave per token (s, t): load the row once, store it to row
+// j = slot - row_base(s)*Nmax of source s's region in the staging rows of
+// every owner lane's destination d (or, with Direct Recv X, to the compact
+// receive row recv_base[d] + recv_psum[d][s] + j), with the fp8 scales and the
 // metadata record {t, expert ids, weight bits}.
 template <int CPL>
 __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
