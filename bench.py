@@ -56,10 +56,15 @@ def alg_bytes(w, n_rows: int, v_rows: int, direct: bool = False) -> dict:
 
 
 def source_digest(paths) -> str:
+    """Hash of the kernel sources with comments and whitespace removed, so that
+    only a change of code (not of its comments) invalidates stored counters."""
     h = hashlib.sha256()
     for p in paths:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
