@@ -195,51 +195,107 @@ __device__ __forceinline__ const int32_t *stage_tables(const DispatchArgs &a, in
 }
 
 // ------------------------------------------------- compact copy epilogue
-// One wave per filled receive row i < recv_base[R]: copy staging row
-// (d, s, j) to recv row i, and derive the per-row metadata.
+// Staging row (d, s, j) to compact receive row i = recv_base[d] +
+// recv_psum[d][s] + j: the hidden row, its scales, and the per-row metadata
+// derived from the record.
+template <int CPL>
+__device__ __forceinline__ void epilogue_row(const DispatchArgs &a, int d, int s, int j, int i, int lane) {
+    const Shape &sh = a.sh;
+    const int nchunks = sh.row_bytes / 16;
+    const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
+    const uint8_t *src = a.staging_x + row * sh.row_bytes;
+    uint8_t *dst = a.recv_x + (int64_t)i * sh.row_bytes;
+    for (int c0 = 0; c0 < nchunks; c0 += CPL * kWave) {
+        u32x4 v[CPL];
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+            const int c = c0 + q * kWave + lane;
+            if (c < nchunks) v[q] = ld16<EP_EPILOGUE_NT_LOAD>(src + (int64_t)c * 16);
+        }
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+            const int c = c0 + q * kWave + lane;
+            if (c < nchunks) st16<EP_EPILOGUE_NT_STORE>(dst + (int64_t)c * 16, v[q]);
+        }
+    }
+    for (int q = lane; q < sh.sf_per_row; q += kWave)
+        a.recv_sf[(int64_t)i * sh.sf_per_row + q] = a.staging_sf[row * sh.sf_per_row + q];
+    const int32_t *meta = a.staging_meta + row * sh.meta_words;
+    const int t = meta[0];
+    if (lane == 0) a.recv_src_idx[i] = s * sh.T + t;
+    for (int k = lane; k < sh.K; k += kWave) {
+        const int e = meta[1 + k];
+        const bool on_d = e >= 0 && e / sh.El == d;
+        a.recv_topk_idx[(int64_t)i * sh.K + k] = on_d ? e - d * sh.El : -1;
+        a.recv_topk_weights[(int64_t)i * sh.K + k] = on_d ? __int_as_float(meta[1 + sh.K + k]) : 0.0f;
+    }
+}
+
+// One wave per filled receive row i < recv_base[R], in order (consecutive
+// waves write consecutive recv_x rows); each finds its (d, s, j) from the
+// tables.  Walking the staging rows instead, latest written first so as to
+// meet them in the Infinity Cache, measured slower on MI355X.
 template <int CPL>
 __global__ void __launch_bounds__(kThreads) k_epilogue(DispatchArgs a, int tables_in_lds) {
     const Shape &sh = a.sh;
     extern __shared__ int32_t lds_tab[];
     const int32_t *tab = stage_tables(a, lds_tab, tables_in_lds != 0);
-    const int32_t *rbase = tab ? tab : a.recv_base;
-    const int32_t *rpsum = tab ? tab + sh.R + 1 : a.recv_psum;
     const int lane = lane_id();
     const int n_rows = (int)min((int64_t)a.recv_base[sh.R], a.recv_capacity_rows);
-    const int nchunks = sh.row_bytes / 16;
     const int wave0 = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
     const int nwaves = gridDim.x * kWavesPerBlock;
+    const int32_t *rbase = tab ? tab : a.recv_base;
+    const int32_t *rpsum = tab ? tab + sh.R + 1 : a.recv_psum;
     for (int i = wave0; i < n_rows; i += nwaves) {
         int d, s, j;
         locate_row(rbase, rpsum, sh.R, sh.S, i, lane, d, s, j);
         if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for tables of one layout
+        epilogue_row<CPL>(a, d, s, j, i, lane);
+    }
+}
+
+// Last index q in [0, n) with tab[q] <= key, for a non-decreasing table whose
+// first entry is <= key.
+__device__ __forceinline__ int last_le(const int32_t *tab, int n, int key) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tab[mid] <= key) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Metadata-only epilogue (Direct Recv X: the hidden rows are already in
+// place).  One thread per item (i, c) of a filled receive row i: c < K is
+// top-k lane c (c = 0 also writes the source index), K <= c < K + sf_per_row
+// copies one scale.
+__global__ void __launch_bounds__(kThreads) k_epilogue_meta(DispatchArgs a, int tables_in_lds) {
+    const Shape &sh = a.sh;
+    extern __shared__ int32_t lds_tab[];
+    const int32_t *tab = stage_tables(a, lds_tab, tables_in_lds != 0);
+    const int32_t *rbase = tab ? tab : a.recv_base;
+    const int32_t *rpsum = tab ? tab + sh.R + 1 : a.recv_psum;
+    const int n_rows = (int)min((int64_t)a.recv_base[sh.R], a.recv_capacity_rows);
+    const int W = sh.K + sh.sf_per_row;
+    const int64_t n_items = (int64_t)n_rows * W;
+    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n_items; g += (int64_t)gridDim.x * kThreads) {
+        const int i = (int)(g / W), c = (int)(g - (int64_t)i * W);
+        const int d = last_le(rbase, sh.R + 1, i);
+        const int32_t *ps = rpsum + (int64_t)d * (sh.S + 1);
+        const int s = last_le(ps, sh.S + 1, i - rbase[d]);
+        const int j = i - rbase[d] - ps[s];
+        if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for tables of one layout
         const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
-        const uint8_t *src = a.staging_x + row * sh.row_bytes;
-        uint8_t *dst = a.recv_x + (int64_t)i * sh.row_bytes;
-        // Direct Recv X: the scatter already wrote the hidden row in place.
-        for (int c0 = 0; c0 < (sh.direct ? 0 : nchunks); c0 += CPL * kWave) {
-            u32x4 v[CPL];
-#pragma unroll
-            for (int q = 0; q < CPL; ++q) {
-                const int c = c0 + q * kWave + lane;
-                if (c < nchunks) v[q] = ld16<EP_EPILOGUE_NT_LOAD>(src + (int64_t)c * 16);
-            }
-#pragma unroll
-            for (int q = 0; q < CPL; ++q) {
-                const int c = c0 + q * kWave + lane;
-                if (c < nchunks) st16<EP_EPILOGUE_NT_STORE>(dst + (int64_t)c * 16, v[q]);
-            }
-        }
-        for (int q = lane; q < sh.sf_per_row; q += kWave)
-            a.recv_sf[(int64_t)i * sh.sf_per_row + q] = a.staging_sf[row * sh.sf_per_row + q];
         const int32_t *meta = a.staging_meta + row * sh.meta_words;
-        const int t = meta[0];
-        if (lane == 0) a.recv_src_idx[i] = s * sh.T + t;
-        for (int k = lane; k < sh.K; k += kWave) {
-            const int e = meta[1 + k];
+        if (c < sh.K) {
+            if (c == 0) a.recv_src_idx[i] = s * sh.T + meta[0];
+            const int e = meta[1 + c];
             const bool on_d = e >= 0 && e / sh.El == d;
-            a.recv_topk_idx[(int64_t)i * sh.K + k] = on_d ? e - d * sh.El : -1;
-            a.recv_topk_weights[(int64_t)i * sh.K + k] = on_d ? __int_as_float(meta[1 + sh.K + k]) : 0.0f;
+            a.recv_topk_idx[(int64_t)i * sh.K + c] = on_d ? e - d * sh.El : -1;
+            a.recv_topk_weights[(int64_t)i * sh.K + c] = on_d ? __int_as_float(meta[1 + sh.K + c]) : 0.0f;
+        } else {
+            a.recv_sf[(int64_t)i * sh.sf_per_row + c - sh.K] = a.staging_sf[row * sh.sf_per_row + c - sh.K];
         }
     }
 }
@@ -398,7 +454,20 @@ hipError_t launch_scatter(const DispatchArgs &a, hipStream_t stream) {
 
 hipError_t launch_epilogue(const DispatchArgs &a, hipStream_t stream) {
     hipError_t err = hipSuccess;
-    if ((int64_t)a.sh.S * a.sh.T > 0) err = dispatch_cpl<EpilogueL>(epilogue_chunks_per_lane(a.sh), a, stream);
+    if ((int64_t)a.sh.S * a.sh.T > 0) {
+        if (a.sh.direct) {
+            const size_t tab = sizeof(int32_t) * ((size_t)a.sh.R + 1 + (size_t)a.sh.R * (a.sh.S + 1));
+            const bool fits = tab <= 32768;
+            const int64_t items = a.recv_capacity_rows * (a.sh.K + a.sh.sf_per_row);
+            int64_t blocks = (items + kThreads - 1) / kThreads;
+            blocks = blocks < 1 ? 1 : (blocks > EP_COPY_BLOCKS ? EP_COPY_BLOCKS : blocks);
+            hipLaunchKernelGGL(k_epilogue_meta, dim3((int)blocks), dim3(kThreads), fits ? tab : 0, stream, a,
+                               (int)fits);
+            err = hipGetLastError();
+        } else {
+            err = dispatch_cpl<EpilogueL>(epilogue_chunks_per_lane(a.sh), a, stream);
+        }
+    }
     if (err != hipSuccess) return err;
     if (a.sh.expand && a.sh.A > 1) {
         hipLaunchKernelGGL(k_expand_padding, dim3(a.sh.E), dim3(kThreads), 0, stream, a);

@@ -199,12 +199,11 @@ __device__ int block_exclusive_scan(int *a, int n, int *part) {
     return total;
 }
 
-// lds[col(i)] += src(i) for i in [0, n), with every thread issuing up to 8
-// global loads before its first LDS add, so a reduction of up to 2048 terms
+// lds[col(i)] += src(i) for i in [0, n), with every thread issuing up to U
+// global loads before its first LDS add, so a reduction of up to 256*U terms
 // costs one memory latency.
-template <typename Src, typename Col>
+template <int U = 8, typename Src, typename Col>
 __device__ __forceinline__ void gather_add(int64_t n, int *lds, Src src, Col col) {
-    constexpr int U = 8;
     for (int64_t i0 = 0; i0 < n; i0 += (int64_t)U * kLayoutThreads) {
         int v[U];
 #pragma unroll
@@ -303,21 +302,89 @@ __global__ void __launch_bounds__(kScanThreads) k_layout_expert_scan(LayoutArgs 
     }
 }
 
+// Receiver tables, built by one extra workgroup of the slot pass while the
+// units rank their items: the per-(source, destination) totals are reduced
+// from the unit counts (LDS integer adds), then prefixed over sources into
+// recv_psum (and, on the hybrid path, over scale-up segments into
+// recv_psum_scaleup) and over destinations into recv_base; the units' invalid
+// flags are OR-ed into error_flags.
+__device__ void build_receiver_tables(const LayoutArgs &a, int *lds) {
+    const Shape &sh = a.sh;
+    const int tid = threadIdx.x, w = tid / kWave;
+    const int R = sh.R, E = sh.E, S = sh.S, B = a.g.blocks_per_src;
+    const int64_t U = (int64_t)S * B;
+    int *part = lds + kLayoutWaves * (R + E) + R + E + (R + E);  // [256], as in the unit layout
+    int *tot = lds;                                               // [S][R] if it fits
+    const bool fits = (int64_t)S * R <= (int64_t)kLayoutWaves * (R + E);
+    int bad = 0;
+    for (int64_t q = tid; q < U; q += kLayoutThreads) bad |= a.blk_flags[q];  // in flight with the gather
+    if (fits) {
+        for (int i = tid; i < S * R; i += kLayoutThreads) tot[i] = 0;
+        __syncthreads();
+        gather_add<16>(U * R, tot, [&](int64_t i) { return a.blk_cnt_rank[i]; },
+                       [&](int64_t i) { return (int)((i / R) / B * R + i % R); });
+        __syncthreads();
+    }
+    int *tot_d = part;  // [R] totals per destination (R <= 64)
+    for (int d = tid; d < R; d += kLayoutThreads) {
+        int run = 0;
+        for (int q = 0; q < S; ++q) {
+            a.recv_psum[(int64_t)d * (S + 1) + q] = run;
+            if (fits) {
+                run += tot[q * R + d];
+            } else {
+                for (int bb = 0; bb < B; ++bb) run += a.blk_cnt_rank[((int64_t)q * B + bb) * R + d];
+            }
+        }
+        a.recv_psum[(int64_t)d * (S + 1) + S] = run;
+        tot_d[d] = run;
+        if (sh.n_out > 1) {
+            // Hybrid row form: prefix over scale-up segments; segment u
+            // holds the sources s with s % n_up == u.
+            int32_t *ps = a.recv_psum_scaleup + (int64_t)d * (sh.n_up + 1);
+            int seg_run = 0;
+            for (int u = 0; u < sh.n_up; ++u) {
+                ps[u] = seg_run;
+                for (int o = 0; o < sh.n_out; ++o) {
+                    const int q = o * sh.n_up + u;
+                    seg_run += a.recv_psum[(int64_t)d * (S + 1) + q + 1] - a.recv_psum[(int64_t)d * (S + 1) + q];
+                }
+            }
+            ps[sh.n_up] = seg_run;
+        }
+    }
+    bad = ballot(bad != 0) != 0;
+    if (lane_id() == 0) part[64 + w] = bad;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int d = 0; d < R; ++d) {
+            a.recv_base[d] = run;
+            run += tot_d[d];
+        }
+        a.recv_base[R] = run;
+        a.error_flags[0] = (part[64] | part[65] | part[66] | part[67]) ? 1 : 0;
+    }
+}
+
 __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
     const Shape &sh = a.sh;
     const int b = blockIdx.x, s = blockIdx.y, B = a.g.blocks_per_src;
     const int w = threadIdx.x / kWave, tid = threadIdx.x;
-    const int R = sh.R, E = sh.E, S = sh.S;
+    const int R = sh.R, E = sh.E;
     const bool expand = sh.expand != 0;
-    const int64_t U = (int64_t)S * B, me = (int64_t)s * B + b;
+    const int64_t me = (int64_t)s * B + b;
 
     extern __shared__ int lds[];
+    if (b == B) {  // the extra column: workgroup (B, 0) builds the receiver tables
+        if (s == 0) build_receiver_tables(a, lds);
+        return;
+    }
     int *cnt_d = lds;                       // [4][R] per-wave counts, then running bases
     int *cnt_e = cnt_d + kLayoutWaves * R;  // [4][E]
     int *base_d = cnt_e + kLayoutWaves * E; // [R]   this unit's base per destination
     int *base_e = base_d + R;               // [E]   expand: this unit's first row per expert
     int *col = base_e + E;                  // [R+E] per-source totals of this unit's share of columns
-    int *part = col + R + E;                // [256] scratch for unit (0,0)
 
     int t0, t1;
     wave_range(a, b, w, t0, t1);
@@ -410,66 +477,6 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
             }
         }
     }
-
-    // Receiver tables (unit 0 only): recv_psum, recv_base, error flags.  The
-    // per-(source, destination) totals are reduced with every thread (LDS
-    // integer adds), then prefixed over sources and destinations.
-    if (me == 0) {
-        __syncthreads();
-        int *tot = cnt_d;  // reuse the (finished) per-wave rows: [S][R] if it fits, else global loads per d
-        const bool fits = (int64_t)S * R <= (int64_t)kLayoutWaves * (R + E);
-        if (fits) {
-            for (int i = tid; i < S * R; i += kLayoutThreads) tot[i] = 0;
-            __syncthreads();
-            gather_add(U * R, tot, [&](int64_t i) { return a.blk_cnt_rank[i]; },
-                       [&](int64_t i) { return (int)((i / R) / B * R + i % R); });
-            __syncthreads();
-        }
-        int *tot_d = part;  // [R] totals per destination (R <= 64)
-        for (int d = tid; d < R; d += kLayoutThreads) {
-            int run = 0;
-            for (int q = 0; q < S; ++q) {
-                a.recv_psum[(int64_t)d * (S + 1) + q] = run;
-                if (fits) {
-                    run += tot[q * R + d];
-                } else {
-                    for (int bb = 0; bb < B; ++bb) run += a.blk_cnt_rank[((int64_t)q * B + bb) * R + d];
-                }
-            }
-            a.recv_psum[(int64_t)d * (S + 1) + S] = run;
-            tot_d[d] = run;
-            if (sh.n_out > 1) {
-                // Hybrid row form: prefix over scale-up segments; segment u
-                // holds the sources s with s % n_up == u.
-                int32_t *ps = a.recv_psum_scaleup + (int64_t)d * (sh.n_up + 1);
-                int seg_run = 0;
-                for (int u = 0; u < sh.n_up; ++u) {
-                    ps[u] = seg_run;
-                    for (int o = 0; o < sh.n_out; ++o) {
-                        const int q = o * sh.n_up + u;
-                        seg_run += a.recv_psum[(int64_t)d * (S + 1) + q + 1] - a.recv_psum[(int64_t)d * (S + 1) + q];
-                    }
-                }
-                ps[sh.n_up] = seg_run;
-            }
-        }
-        int bad = 0;
-        for (int64_t q = tid; q < U; q += kLayoutThreads) bad |= a.blk_flags[q];
-        bad = ballot(bad != 0) != 0;
-        __syncthreads();
-        if (tid == 0) {
-            int run = 0;
-            for (int d = 0; d < R; ++d) {
-                a.recv_base[d] = run;
-                run += tot_d[d];
-            }
-            a.recv_base[R] = run;
-        }
-        __syncthreads();
-        if (lane_id() == 0) part[64 + w] = bad;
-        __syncthreads();
-        if (tid == 0) a.error_flags[0] = (part[64] | part[65] | part[66] | part[67]) ? 1 : 0;
-    }
 }
 
 size_t count_lds_bytes(const Shape &sh) {
@@ -495,7 +502,10 @@ hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(k_layout_slot, grid, dim3(kLayoutThreads), slot_lds_bytes(a.sh), stream, a);
+    // One more column of workgroups: (B, 0) builds the receiver tables, the
+    // rest of that column exits at once.
+    hipLaunchKernelGGL(k_layout_slot, dim3(a.g.blocks_per_src + 1, a.sh.S), dim3(kLayoutThreads),
+                       slot_lds_bytes(a.sh), stream, a);
     return hipGetLastError();
 }
 
