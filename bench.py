@@ -200,6 +200,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-direct", action="store_true", help="skip the Direct Recv X variant")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache per-stage timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (the reference for the byte counters)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
@@ -280,8 +281,36 @@ def main():
         stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
         return ms, stage_ms
 
+    def cold_stages(c, recv, reps=20, warm=3):
+        """Each stage alone, after a 1 GiB device fill has flushed L2 and the
+        Infinity Cache; median and minimum over `reps` runs."""
+        flush = torch.empty((1 << 30) // 4, dtype=torch.int32, device=dev)
+        calls = {
+            "layout": lambda: ep.ep_layout(c, topk, L, stream),
+            "scatter": lambda: ep.ep_dispatch(c, x, x_sf, topk, wts, L, recv, ep.EP_PHASE_SCATTER, stream),
+            "epilogue": lambda: ep.ep_dispatch(c, x, x_sf, topk, wts, L, recv, ep.EP_PHASE_EPILOGUE, stream),
+            "combine": lambda: ep.ep_combine(c, L, topk, wts, y, out, stream),
+        }
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = {n: [] for n in names}
+        for r in range(warm + reps):
+            for n in names:
+                flush.fill_(r)
+                e0.record(stream)
+                calls[n]()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                if r >= warm:
+                    times[n].append(e0.elapsed_time(e1))
+        del flush
+        return {n: (float(np.median(v)), float(np.min(v))) for n, v in times.items()}
+
     print(f"[bench] {w.name}: warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
     ms, stage_ms = measure(cfg, R)
+    cold = None
+    if not args.no_cold:
+        print("[bench] cold per-stage timing", file=sys.stderr, flush=True)
+        cold = cold_stages(cfg, R)
     n_rows = int(L.recv_base[-1].item())
     v_rows = int(((topk >= 0) & (topk < w.E)).sum().item())
     b = alg_bytes(w, n_rows, v_rows)
@@ -316,6 +345,14 @@ def main():
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(epi_gbps / PEAK_HBM_GBPS, 4),
                      "alg_bytes_per_launch": epi_alg, "traffic": traffic},
     }
+    if cold is not None:
+        cold_ms = sum(v[0] for v in cold.values())
+        res["cold_per_stage"] = {
+            "protocol": "each stage alone after a 1 GiB fill (L2 and Infinity Cache flushed), 3 warm-up + 20 runs",
+            "median_us": {k: round(v[0] * 1e3, 2) for k, v in cold.items()},
+            "min_us": {k: round(v[1] * 1e3, 2) for k, v in cold.items()},
+            "value": round(b["total"] / (cold_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "ms_per_step": round(cold_ms, 5)}
     if not args.no_graph:
         # The same step captured once in a HIP graph and replayed K times.
         print("[bench] graph replay", file=sys.stderr, flush=True)

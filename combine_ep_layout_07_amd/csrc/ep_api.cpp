@@ -167,7 +167,8 @@ int ep_layout(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layo
     a.blk_cnt_rank = static_cast<int32_t *>(layout->scratch_dev);
     a.blk_cnt_expert = a.blk_cnt_rank + units * sh.R;
     a.blk_flags = a.blk_cnt_expert + units * sh.E;
-    a.blk_base_expert = sh.expand ? a.blk_flags + units : nullptr;
+    a.blk_pre_expert = sh.expand ? a.blk_flags + units : nullptr;
+    a.cnt_expert = sh.expand ? a.blk_pre_expert + units * sh.E : nullptr;
     return ep::launch_layout(a, (hipStream_t)stream) == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 

@@ -48,6 +48,16 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #ifndef EP_SCATTER_SLICES
 #define EP_SCATTER_SLICES 1  // column slices of a token's row, each a separate work unit
 #endif
+// Column slices of a compact receive row, each a separate work unit, and the
+// epilogue's grid cap.  Measured on MI355X at T=4096, H=7168: whole rows per
+// wave are fastest (2, 4 and 7 slices cost 2%, 9% and 19% more time); 1024 to
+// 4096 workgroups are within 2% of each other.
+#ifndef EP_EPILOGUE_SLICES
+#define EP_EPILOGUE_SLICES 1
+#endif
+#ifndef EP_EPILOGUE_BLOCKS
+#define EP_EPILOGUE_BLOCKS 2048
+#endif
 #ifndef EP_COPY_BLOCKS
 #define EP_COPY_BLOCKS 2048
 #endif
@@ -199,25 +209,26 @@ __device__ __forceinline__ const int32_t *stage_tables(const DispatchArgs &a, in
 // recv_psum[d][s] + j: the hidden row, its scales, and the per-row metadata
 // derived from the record.
 template <int CPL>
-__device__ __forceinline__ void epilogue_row(const DispatchArgs &a, int d, int s, int j, int i, int lane) {
+__device__ __forceinline__ void epilogue_row(const DispatchArgs &a, int d, int s, int j, int i, int lane, int c_lo,
+                                             int c_hi) {
     const Shape &sh = a.sh;
-    const int nchunks = sh.row_bytes / 16;
     const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
     const uint8_t *src = a.staging_x + row * sh.row_bytes;
     uint8_t *dst = a.recv_x + (int64_t)i * sh.row_bytes;
-    for (int c0 = 0; c0 < nchunks; c0 += CPL * kWave) {
+    for (int c0 = c_lo; c0 < c_hi; c0 += CPL * kWave) {
         u32x4 v[CPL];
 #pragma unroll
         for (int q = 0; q < CPL; ++q) {
             const int c = c0 + q * kWave + lane;
-            if (c < nchunks) v[q] = ld16<EP_EPILOGUE_NT_LOAD>(src + (int64_t)c * 16);
+            if (c < c_hi) v[q] = ld16<EP_EPILOGUE_NT_LOAD>(src + (int64_t)c * 16);
         }
 #pragma unroll
         for (int q = 0; q < CPL; ++q) {
             const int c = c0 + q * kWave + lane;
-            if (c < nchunks) st16<EP_EPILOGUE_NT_STORE>(dst + (int64_t)c * 16, v[q]);
+            if (c < c_hi) st16<EP_EPILOGUE_NT_STORE>(dst + (int64_t)c * 16, v[q]);
         }
     }
+    if (c_lo != 0) return;  // slice 0 also moves the scales and the metadata
     for (int q = lane; q < sh.sf_per_row; q += kWave)
         a.recv_sf[(int64_t)i * sh.sf_per_row + q] = a.staging_sf[row * sh.sf_per_row + q];
     const int32_t *meta = a.staging_meta + row * sh.meta_words;
@@ -246,11 +257,16 @@ __global__ void __launch_bounds__(kThreads) k_epilogue(DispatchArgs a, int table
     const int nwaves = gridDim.x * kWavesPerBlock;
     const int32_t *rbase = tab ? tab : a.recv_base;
     const int32_t *rpsum = tab ? tab + sh.R + 1 : a.recv_psum;
-    for (int i = wave0; i < n_rows; i += nwaves) {
+    const int nchunks = sh.row_bytes / 16;
+    const int slices = a.slices;
+    const int cps = ((nchunks + slices - 1) / slices + kWave - 1) / kWave * kWave;  // chunks per slice
+    const int64_t n_units = (int64_t)n_rows * slices;
+    for (int64_t u = wave0; u < n_units; u += nwaves) {
+        const int i = (int)(u / slices), slice = (int)(u - (int64_t)i * slices);
         int d, s, j;
         locate_row(rbase, rpsum, sh.R, sh.S, i, lane, d, s, j);
         if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for tables of one layout
-        epilogue_row<CPL>(a, d, s, j, i, lane);
+        epilogue_row<CPL>(a, d, s, j, i, lane, slice * cps, min(slice * cps + cps, nchunks));
     }
 }
 
@@ -268,16 +284,16 @@ __device__ __forceinline__ int last_le(const int32_t *tab, int n, int key) {
 
 // Metadata-only epilogue (Direct Recv X: the hidden rows are already in
 // place).  One thread per item (i, c) of a filled receive row i: c < K is
-// top-k lane c (c = 0 also writes the source index), K <= c < K + sf_per_row
-// copies one scale.
-__global__ void __launch_bounds__(kThreads) k_epilogue_meta(DispatchArgs a, int tables_in_lds) {
+// top-k lane c (c = 0 also writes the source index); each further item copies
+// sf_vec scales (4 = one 16-byte chunk when rows and buffers allow, else 1).
+__global__ void __launch_bounds__(kThreads) k_epilogue_meta(DispatchArgs a, int tables_in_lds, int sf_vec) {
     const Shape &sh = a.sh;
     extern __shared__ int32_t lds_tab[];
     const int32_t *tab = stage_tables(a, lds_tab, tables_in_lds != 0);
     const int32_t *rbase = tab ? tab : a.recv_base;
     const int32_t *rpsum = tab ? tab + sh.R + 1 : a.recv_psum;
     const int n_rows = (int)min((int64_t)a.recv_base[sh.R], a.recv_capacity_rows);
-    const int W = sh.K + sh.sf_per_row;
+    const int W = sh.K + sh.sf_per_row / sf_vec;
     const int64_t n_items = (int64_t)n_rows * W;
     for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n_items; g += (int64_t)gridDim.x * kThreads) {
         const int i = (int)(g / W), c = (int)(g - (int64_t)i * W);
@@ -294,6 +310,10 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_meta(DispatchArgs a, int 
             const bool on_d = e >= 0 && e / sh.El == d;
             a.recv_topk_idx[(int64_t)i * sh.K + c] = on_d ? e - d * sh.El : -1;
             a.recv_topk_weights[(int64_t)i * sh.K + c] = on_d ? __int_as_float(meta[1 + sh.K + c]) : 0.0f;
+        } else if (sf_vec == 4) {
+            const int q = (c - sh.K) * 4;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(a.staging_sf + row * sh.sf_per_row + q);
+            *reinterpret_cast<u32x4 *>(a.recv_sf + (int64_t)i * sh.sf_per_row + q) = v;
         } else {
             a.recv_sf[(int64_t)i * sh.sf_per_row + c - sh.K] = a.staging_sf[row * sh.sf_per_row + c - sh.K];
         }
@@ -394,7 +414,16 @@ int chunks_per_lane(const Shape &sh) {
     const int cps = ((nchunks + slices - 1) / slices + kWave - 1) / kWave * kWave;
     return cps / kWave;
 }
-int epilogue_chunks_per_lane(const Shape &sh) { return (sh.row_bytes / 16 + kWave - 1) / kWave; }
+int epilogue_slices(const Shape &sh) {
+    const int nchunks = sh.row_bytes / 16;
+    int slices = sh.expand ? 1 : (EP_EPILOGUE_SLICES < 1 ? 1 : EP_EPILOGUE_SLICES);
+    if (slices > (nchunks + kWave - 1) / kWave) slices = (nchunks + kWave - 1) / kWave;
+    return slices;
+}
+int epilogue_chunks_per_lane(const Shape &sh) {
+    const int nchunks = sh.row_bytes / 16, slices = epilogue_slices(sh);
+    return (((nchunks + slices - 1) / slices + kWave - 1) / kWave * kWave) / kWave;
+}
 
 template <template <int> class Launcher, typename... Args>
 hipError_t dispatch_cpl(int need, Args &&...args) {
@@ -407,10 +436,10 @@ hipError_t dispatch_cpl(int need, Args &&...args) {
     return Launcher<16>::run(args...);
 }
 
-int grid_for(int64_t work_waves) {
+int grid_for(int64_t work_waves, int max_blocks = EP_COPY_BLOCKS) {
     // Enough waves to fill 256 CUs several times over; extra work is strided.
     int64_t blocks = (work_waves + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (blocks > EP_COPY_BLOCKS) blocks = EP_COPY_BLOCKS;
+    if (blocks > max_blocks) blocks = max_blocks;
     if (blocks < 1) blocks = 1;
     return (int)blocks;
 }
@@ -430,7 +459,9 @@ struct ScatterL {
 
 template <int CPL>
 struct EpilogueL {
-    static hipError_t run(const DispatchArgs &a, hipStream_t st) {
+    static hipError_t run(const DispatchArgs &args, hipStream_t st) {
+        DispatchArgs a = args;
+        a.slices = epilogue_slices(a.sh);
         const size_t tab = sizeof(int32_t) * ((size_t)a.sh.R + 1 + (size_t)a.sh.R * (a.sh.S + 1));
         const bool fits = tab <= 32768;
         const int64_t rows = a.sh.expand ? (int64_t)a.sh.S * a.sh.T * (a.sh.K < a.sh.R ? a.sh.K : a.sh.R)
@@ -439,7 +470,8 @@ struct EpilogueL {
             hipLaunchKernelGGL(k_epilogue_expand<CPL>, dim3(grid_for(rows)), dim3(kThreads), fits ? tab : 0, st, a,
                                (int)fits);
         else
-            hipLaunchKernelGGL(k_epilogue<CPL>, dim3(grid_for(rows)), dim3(kThreads), fits ? tab : 0, st, a,
+            hipLaunchKernelGGL(k_epilogue<CPL>, dim3(grid_for(rows * a.slices, EP_EPILOGUE_BLOCKS)), dim3(kThreads),
+                               fits ? tab : 0, st, a,
                                (int)fits);
         return hipGetLastError();
     }
@@ -458,11 +490,15 @@ hipError_t launch_epilogue(const DispatchArgs &a, hipStream_t stream) {
         if (a.sh.direct) {
             const size_t tab = sizeof(int32_t) * ((size_t)a.sh.R + 1 + (size_t)a.sh.R * (a.sh.S + 1));
             const bool fits = tab <= 32768;
-            const int64_t items = a.recv_capacity_rows * (a.sh.K + a.sh.sf_per_row);
+            // Scales move as 16-byte chunks when every row and both buffers are 16-byte aligned.
+            const bool vec = a.sh.sf_per_row % 4 == 0 && ((uintptr_t)a.staging_sf % 16) == 0 &&
+                             ((uintptr_t)a.recv_sf % 16) == 0;
+            const int sf_vec = vec ? 4 : 1;
+            const int64_t items = a.recv_capacity_rows * (a.sh.K + a.sh.sf_per_row / sf_vec);
             int64_t blocks = (items + kThreads - 1) / kThreads;
-            blocks = blocks < 1 ? 1 : (blocks > EP_COPY_BLOCKS ? EP_COPY_BLOCKS : blocks);
+            blocks = blocks < 1 ? 1 : (blocks > 4 * EP_COPY_BLOCKS ? 4 * EP_COPY_BLOCKS : blocks);
             hipLaunchKernelGGL(k_epilogue_meta, dim3((int)blocks), dim3(kThreads), fits ? tab : 0, stream, a,
-                               (int)fits);
+                               (int)fits, sf_vec);
             err = hipGetLastError();
         } else {
             err = dispatch_cpl<EpilogueL>(epilogue_chunks_per_lane(a.sh), a, stream);

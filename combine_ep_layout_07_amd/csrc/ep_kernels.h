@@ -53,7 +53,8 @@ struct LayoutArgs {
     int32_t *blk_cnt_rank;    // scratch [S*B][R]
     int32_t *blk_cnt_expert;  // scratch [S*B][E]
     int32_t *blk_flags;       // scratch [S*B]
-    int32_t *blk_base_expert; // scratch [S*B][E], expand only
+    int32_t *blk_pre_expert;  // scratch [S*B][E], expand only: valid lanes of the earlier units per expert
+    int32_t *cnt_expert;      // scratch [E], expand only: valid lanes per expert over all sources
 };
 
 struct DispatchArgs {

@@ -21,13 +21,15 @@
 //
 //   k_layout_count: per-unit counts of owner lanes per destination and of
 //     valid lanes per expert, plus an invalid-id flag, into scratch;
-//   k_layout_expert_scan (expand only): per-expert segment bases (padded to
-//     A) and each unit's first row in every expert segment;
+//   k_layout_expert_scan (expand only): for every expert, the valid lanes of
+//     all earlier units (a column prefix over units) and the total;
 //   k_layout_slot: each unit reduces the counts of the earlier units of its
 //     source (its base per destination), recounts per wave for the wave
 //     bases, then ranks every item and writes dst_slot (and expand_pos); the
-//     units also share out the per-source counts, and unit (0,0) writes the
-//     receiver tables (recv_psum, recv_base, error_flags).
+//     units also share out the per-source counts; expand adds the expert
+//     segment bases (padded totals, scanned over experts) to each unit's
+//     column prefix; one extra workgroup writes the receiver tables
+//     (recv_psum, recv_base, expert_base, error_flags).
 #include "ep_device.h"
 #include "ep_kernels.h"
 
@@ -37,6 +39,9 @@ constexpr int kLayoutThreads = 256;
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kBatch = 8;  // steps whose items a wave loads together
 constexpr int kScanThreads = 1024;
+constexpr int kScanCols = 64;                        // experts per scan workgroup
+constexpr int kScanSegs = kScanThreads / kScanCols;  // unit segments per expert
+constexpr int kScanRegs = 16;                        // counts a scan thread keeps in registers
 
 LayoutGeom layout_geometry(const Shape &sh, int num_layout_cus) {
     LayoutGeom g;
@@ -65,7 +70,7 @@ LayoutGeom layout_geometry(const Shape &sh, int num_layout_cus) {
 
 uint64_t layout_scratch_bytes(const Shape &sh, const LayoutGeom &g) {
     const uint64_t units = (uint64_t)sh.S * g.blocks_per_src;
-    return units * (uint64_t)(sh.R + sh.E + 1 + (sh.expand ? sh.E : 0)) * sizeof(int32_t);
+    return (units * (uint64_t)(sh.R + sh.E + 1 + (sh.expand ? sh.E : 0)) + (sh.expand ? sh.E : 0)) * sizeof(int32_t);
 }
 
 namespace {
@@ -262,44 +267,63 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_count(LayoutArgs a) {
     if (tid == 0) a.blk_flags[u] = flag[0] | flag[1] | flag[2] | flag[3];
 }
 
-// Expand layout only.  One workgroup: thread (seg, e) owns expert column e
-// over a contiguous segment of units.  Writes expert_base [E+1] (segments of
-// the valid-lane counts, padded to A) and blk_base_expert[u][e], the first row
-// of unit u inside expert e's segment (units in (s, t) order).
+// Expand layout only.  Workgroup x covers experts [64x, 64x + 64); thread
+// (seg, c) owns expert e = 64x + c over one of 16 contiguous segments of the
+// units (units in (s, t) order), loads its counts in batches of independent
+// loads (keeping up to 16 in registers for the second pass), and the 16
+// segment sums of each expert are prefixed in LDS.  Writes blk_pre_expert[u][e]
+// (valid lanes of units before u on expert e) and cnt_expert[e].
 __global__ void __launch_bounds__(kScanThreads) k_layout_expert_scan(LayoutArgs a) {
     const Shape &sh = a.sh;
     const int E = sh.E, tid = threadIdx.x;
     const int64_t U = (int64_t)sh.S * a.g.blocks_per_src;
-    const int nseg = kScanThreads / E;  // E <= 1024
-    const int e = tid % E, seg = tid / E;
-    const bool active = seg < nseg;
-    const int64_t u0 = active ? U * seg / nseg : 0, u1 = active ? U * (seg + 1) / nseg : 0;
-    extern __shared__ int lds[];
-    int *part = lds;                     // [nseg][E]
-    int *base = part + nseg * E;         // [E+1]
-    int *scan_part = base + E + 1;       // [kScanThreads]
+    const int c = tid % kScanCols, seg = tid / kScanCols;
+    const int e = blockIdx.x * kScanCols + c;
+    const bool active = e < E;
+    const int64_t u0 = U * seg / kScanSegs, u1 = U * (seg + 1) / kScanSegs;
+    const bool in_regs = u1 - u0 <= kScanRegs;
+    __shared__ int part[kScanSegs][kScanCols];
+    int v[kScanRegs];
     int sum = 0;
-    for (int64_t u = u0; u < u1; ++u) sum += a.blk_cnt_expert[u * E + e];
-    if (active) part[seg * E + e] = sum;
-    __syncthreads();
-    if (tid < E) {
-        int tot = 0;
-        for (int q = 0; q < nseg; ++q) tot += part[q * E + tid];
-        base[tid] = (tot + sh.A - 1) / sh.A * sh.A;
+    if (active && in_regs) {
+#pragma unroll
+        for (int q = 0; q < kScanRegs; ++q) v[q] = u0 + q < u1 ? a.blk_cnt_expert[(u0 + q) * E + e] : 0;
+#pragma unroll
+        for (int q = 0; q < kScanRegs; ++q) sum += v[q];
+    } else if (active) {
+        for (int64_t u = u0; u < u1; ++u) sum += a.blk_cnt_expert[u * E + e];
     }
+    part[seg][c] = sum;
     __syncthreads();
-    const int total = block_exclusive_scan<kScanThreads>(base, E, scan_part);
-    if (tid == 0) base[E] = total;
-    __syncthreads();
-    for (int i = tid; i <= E; i += kScanThreads) a.expert_base[i] = base[i];
-    if (active) {
-        int run = base[e];
-        for (int q = 0; q < seg; ++q) run += part[q * E + e];
+    int run = 0;
+    for (int q = 0; q < seg; ++q) run += part[q][c];
+    if (active && seg == kScanSegs - 1) a.cnt_expert[e] = run + sum;
+    if (!active) return;
+    if (in_regs) {
+#pragma unroll
+        for (int q = 0; q < kScanRegs; ++q) {
+            if (u0 + q < u1) a.blk_pre_expert[(u0 + q) * E + e] = run;
+            run += v[q];
+        }
+    } else {
         for (int64_t u = u0; u < u1; ++u) {
-            a.blk_base_expert[u * E + e] = run;
+            a.blk_pre_expert[u * E + e] = run;
             run += a.blk_cnt_expert[u * E + e];
         }
     }
+}
+
+// Expert segment bases (expand): seg[e] <- sum over e' < e of the valid lanes
+// of expert e' padded up to a multiple of A; returns the total.  Every thread
+// of the workgroup calls it; seg has E entries in LDS, part 256.
+__device__ int expert_segment_bases(const LayoutArgs &a, int *seg, int *part) {
+    const Shape &sh = a.sh;
+    for (int e = threadIdx.x; e < sh.E; e += kLayoutThreads) {
+        const int cnt = a.cnt_expert[e];
+        seg[e] = (cnt + sh.A - 1) / sh.A * sh.A;
+    }
+    __syncthreads();
+    return block_exclusive_scan<kLayoutThreads>(seg, sh.E, part);
 }
 
 // Receiver tables, built by one extra workgroup of the slot pass while the
@@ -307,7 +331,7 @@ __global__ void __launch_bounds__(kScanThreads) k_layout_expert_scan(LayoutArgs 
 // from the unit counts (LDS integer adds), then prefixed over sources into
 // recv_psum (and, on the hybrid path, over scale-up segments into
 // recv_psum_scaleup) and over destinations into recv_base; the units' invalid
-// flags are OR-ed into error_flags.
+// flags are OR-ed into error_flags; expand also writes expert_base.
 __device__ void build_receiver_tables(const LayoutArgs &a, int *lds) {
     const Shape &sh = a.sh;
     const int tid = threadIdx.x, w = tid / kWave;
@@ -318,6 +342,13 @@ __device__ void build_receiver_tables(const LayoutArgs &a, int *lds) {
     const bool fits = (int64_t)S * R <= (int64_t)kLayoutWaves * (R + E);
     int bad = 0;
     for (int64_t q = tid; q < U; q += kLayoutThreads) bad |= a.blk_flags[q];  // in flight with the gather
+    if (sh.expand) {
+        int *eb = lds + kLayoutWaves * (R + E) + R;  // [E], unused by the rest of this workgroup
+        const int total = expert_segment_bases(a, eb, part);
+        for (int e = tid; e < E; e += kLayoutThreads) a.expert_base[e] = eb[e];
+        if (tid == 0) a.expert_base[E] = total;
+        __syncthreads();
+    }
     if (fits) {
         for (int i = tid; i < S * R; i += kLayoutThreads) tot[i] = 0;
         __syncthreads();
@@ -400,8 +431,23 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
     const int32_t *src_rank = a.blk_cnt_rank + (int64_t)s * B * R;
     gather_add((int64_t)b * R, base_d, [&](int64_t i) { return src_rank[i]; },
                [&](int64_t i) { return (int)(i % R); });
-    if (expand)
-        for (int e = tid; e < E; e += kLayoutThreads) base_e[e] = a.blk_base_expert[me * E + e];
+    if (expand) {
+        // First row of this unit in expert e's segment: the segment base plus
+        // what the earlier units put there.
+        int *part = col + R + E;
+        int pre[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + q * kLayoutThreads;
+            pre[q] = e < E ? a.blk_pre_expert[me * E + e] : 0;
+        }
+        expert_segment_bases(a, base_e, part);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + q * kLayoutThreads;
+            if (e < E) base_e[e] += pre[q];
+        }
+    }
     // This unit's share of the per-source totals: columns c = b, b+B, ...
     // (destinations first, then experts), each summed over the source's units.
     const int ncol = b < R + E ? (R + E - b + B - 1) / B : 0;
@@ -482,10 +528,6 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
 size_t count_lds_bytes(const Shape &sh) {
     return sizeof(int) * ((size_t)kLayoutWaves * (sh.R + sh.E) + kLayoutWaves);
 }
-size_t scan_lds_bytes(const Shape &sh) {
-    const int nseg = kScanThreads / sh.E;
-    return sizeof(int) * ((size_t)nseg * sh.E + sh.E + 1 + kScanThreads);
-}
 size_t slot_lds_bytes(const Shape &sh) {
     return sizeof(int) * ((size_t)kLayoutWaves * (sh.R + sh.E) + sh.R + sh.E + (sh.R + sh.E) + kLayoutThreads);
 }
@@ -498,7 +540,8 @@ hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (a.sh.expand) {
-        hipLaunchKernelGGL(k_layout_expert_scan, dim3(1), dim3(kScanThreads), scan_lds_bytes(a.sh), stream, a);
+        hipLaunchKernelGGL(k_layout_expert_scan, dim3((a.sh.E + kScanCols - 1) / kScanCols), dim3(kScanThreads), 0,
+                           stream, a);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

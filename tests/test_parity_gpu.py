@@ -114,6 +114,16 @@ def test_direct_recv_x_small(w):
     _full_case(w, 11, EDGE, direct=True)
 
 
+@pytest.mark.parametrize("mode", ["staging", "direct", "expand"])
+def test_receiver_tables_beyond_lds(mode):
+    """R * (S + 1) > 8192 table entries: the epilogues search recv_base and
+    recv_psum in global memory instead of staging them in LDS."""
+    w = Workload("many_sources", S=160, T=5, H=64, K=3, E=64, R=64, Nmax=6, expand=mode == "expand",
+                 alignment=2 if mode == "expand" else 1)
+    assert w.R * (w.S + 1) + w.R + 1 > 8192
+    _full_case(w, 31, EDGE, direct=mode == "direct")
+
+
 @pytest.mark.parametrize("case", ["tiny", "dsv3_share", "expand_small", "expand_a4_fp8"])
 @pytest.mark.parametrize("nb", [1, 2])
 def test_combine_bias(case, nb):
