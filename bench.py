@@ -191,6 +191,34 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_md: str, command: str
     print("\n".join(lines))
 
 
+def summarize_trace(stats_csv: str, bench_json: str, out_md: str, command: str) -> None:
+    """Turn a rocprofv3 --kernel-trace --stats summary (kernel_stats.csv) and the
+    JSON line bench.py printed in the same run into a short markdown summary."""
+    rows = [r for r in _counter_rows(stats_csv) if "ep::" in r["Name"]]
+    with open(bench_json) as f:
+        b = json.loads(f.read().strip().splitlines()[-1])
+    lines = [f"# Kernel trace: {b['config']['workload']}", "", "command: " + command, "",
+             "rocprofv3 --stats summary (kernel_stats.csv), libep kernels only. Durations in microseconds.", "",
+             "| kernel | calls | avg us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "")
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} "
+                     f"| {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
+    lines += ["", f"bench.py line of the same (profiled) run: value {b['value']} GB/s, ms_per_step {b['ms_per_step']}, "
+                  f"stage_us {b['stage_us']}, epilogue achieved {b['roofline']['achieved']} GB/s (HIP events around "
+                  "the launch, which add a few microseconds of dispatch and timestamp overhead)."]
+    epi = [r for r in rows if "k_epilogue" in r["Name"] and "meta" not in r["Name"]]
+    if epi:
+        avg = float(epi[0]["AverageNs"]) / 1e3
+        alg = b["roofline"]["alg_bytes_per_launch"]
+        lines.append(f"The same algorithmic bytes ({alg} B per launch) over the rocprofv3 average duration of the "
+                     f"copy epilogue ({avg:.2f} us): {alg / avg / 1e3:.1f} GB/s = "
+                     f"{alg / avg / 1e3 / PEAK_HBM_GBPS * 100:.1f}% of 8 TB/s.")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,10 +233,15 @@ def main():
                     help="also run a plain 256 MiB device copy (the reference for the byte counters)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
                     help="write the traffic summary from two rocprofv3 --pmc CSVs and exit (no GPU use)")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "BENCH_JSON", "OUT_MD"),
+                    help="write a kernel-trace summary from rocprofv3 --stats output and exit (no GPU use)")
     ap.add_argument("--command", default="", help="profiling command recorded in the summary")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, command=args.command)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, command=args.command)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

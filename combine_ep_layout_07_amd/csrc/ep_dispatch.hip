@@ -49,9 +49,10 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #define EP_SCATTER_SLICES 1  // column slices of a token's row, each a separate work unit
 #endif
 // Column slices of a compact receive row, each a separate work unit, and the
-// epilogue's grid cap.  Measured on MI355X at T=4096, H=7168: whole rows per
-// wave are fastest (2, 4 and 7 slices cost 2%, 9% and 19% more time); 1024 to
-// 4096 workgroups are within 2% of each other.
+// epilogue's grid cap.  Measured on MI355X at T=4096, H=7168: one whole row
+// per wave in one pass is fastest (2, 4 and 7 slices cost 2%, 9% and 19% more
+// time, two passes of half a row 3%, two rows per wave 1%); 1024 to 4096
+// workgroups are within 2% of each other.
 #ifndef EP_EPILOGUE_SLICES
 #define EP_EPILOGUE_SLICES 1
 #endif

@@ -1,0 +1,92 @@
+"""Host-side pieces of bench.py (no GPU): the one-GPU guard, the algorithmic
+byte formula, and the counter summary that feeds the roofline's traffic."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from combine_ep_layout_07_amd.workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+# Expected totals at each workload's expected row counts (N deduplicated
+# entries, V valid lanes), worked out per stage by hand from the byte model:
+# layout S*T*K*12 (+4 per lane for expand), scatter reads x and the ids,
+# slots, weights and writes N staging rows with their records, the epilogue
+# reads the N staging rows and writes the receive rows, combine reads the ids,
+# weights and slots, the expert rows and writes the output.
+@pytest.mark.parametrize("cfg,n,v,total,tol", [
+    (1, 441, 512, 1.1e6, 0.05),
+    (2, 26719, 32768, 1.657e9, 0.002),
+    (3, 26719, 32768, 1.072e9, 0.002),
+    (4, 35600, 65536, 1.31e9, 0.01),
+    (5, 213755, 262144, 14.63e9, 0.002),
+])
+def test_algorithmic_bytes_match_the_worked_totals(cfg, n, v, total, tol):
+    b = bench.alg_bytes(WORKLOADS[cfg], n, v)
+    assert b["total"] == b["layout"] + b["scatter"] + b["epilogue"] + b["combine"]
+    assert abs(b["total"] - total) / total < tol
+
+
+def test_algorithmic_bytes_per_stage_dsv3_share():
+    b = bench.alg_bytes(WORKLOADS[2], 26719, 32768)
+    row = 7168 * 2
+    assert b["layout"] == 4096 * 8 * 12
+    assert b["scatter"] == 4096 * row + 4096 * 8 * 16 + 26719 * (row + 4 * 17)
+    assert b["epilogue"] == 26719 * (row + 4 * 17) + 26719 * (row + 4 + 64)
+    assert b["combine"] == 4096 * 8 * 16 + 26719 * row + 4096 * row
+    d = bench.alg_bytes(WORKLOADS[2], 26719, 32768, direct=True)
+    assert d["scatter"] == b["scatter"]
+    assert d["epilogue"] == 26719 * 4 * 17 + 26719 * (4 + 64)
+
+
+def test_source_digest_ignores_comments_only(tmp_path):
+    a, b, c = tmp_path / "a.hip", tmp_path / "b.hip", tmp_path / "c.hip"
+    a.write_text("// header\nint f(int x) { return x + 1; }  /* tail */\n")
+    b.write_text("/* another\n header */\nint f(int x) {\n  return x + 1;  // same code\n}\n")
+    c.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.source_digest([str(a)]) == bench.source_digest([str(b)])
+    assert bench.source_digest([str(a)]) != bench.source_digest([str(c)])
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, value in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_counter_summary_round_trip(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("int k;\n")
+    out = tmp_path / "traffic.md"
+    monkeypatch.setattr(bench, "EPILOGUE_SOURCES", [str(src)])
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    cal_kib = bench.COPY_CAL_BYTES / 1024
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    # FETCH_SIZE reads half the copy's bytes (scale 2), WRITE_SIZE all of them (scale 1).
+    _counter_csv(fetch, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", cal_kib / 2), ("__amd_rocclr_copyBuffer", 4.0),
+                                       ("void ep::k_epilogue<14>(ep::DispatchArgs, int)", 1000.0),
+                                       ("void ep::k_epilogue<14>(ep::DispatchArgs, int)", 1002.0)])
+    _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", cal_kib),
+                                       ("void ep::k_epilogue<14>(ep::DispatchArgs, int)", 3000.0)])
+    bench.summarize_counters(str(fetch), str(write), str(out), command="rocprofv3 --pmc ...")
+    want = (1001.0 * 2 + 3000.0) * 1024
+    assert bench.read_traffic(0) == pytest.approx(want)
+    src.write_text("int k;  // a comment keeps the counters valid\n")
+    assert bench.read_traffic(0) == pytest.approx(want)
+    src.write_text("int k2;\n")
+    assert bench.read_traffic(0) is None
