@@ -31,13 +31,15 @@ EPILOGUE_SOURCES = [os.path.join(ROOT, "combine_ep_layout_07_amd", "csrc", f)
                     for f in ("ep_dispatch.hip", "ep_device.h", "ep_kernels.h")]
 
 
-def alg_bytes(w, n_rows: int, v_rows: int, direct: bool = False) -> dict:
+def alg_bytes(w, n_rows: int, v_rows: int, direct: bool = False, pad_rows: int = 0, n_bias: int = 0) -> dict:
     """Algorithmic bytes per stage: each mandatory input read and output write once.
 
     Rw row bytes, F scale bytes per row, M = 4(1+2K) staging metadata bytes,
     Y = 2H expert-output row bytes; N deduplicated rows, V valid lanes.  With
     Direct Recv X the scatter writes the hidden rows to recv_x (same bytes) and
-    the epilogue moves only scales and metadata."""
+    the epilogue moves only scales and metadata.  Expand padding rows (expert
+    alignment > 1) are written like expand rows; each bias tensor adds one
+    [S][T][H] bf16 read to the combine."""
     S, T, K, H = w.S, w.T, w.K, w.H
     Rw = H if w.dtype == "fp8" else 2 * H
     F = (H // 128) * 4 if w.dtype == "fp8" else 0
@@ -49,8 +51,9 @@ def alg_bytes(w, n_rows: int, v_rows: int, direct: bool = False) -> dict:
     if direct:
         epilogue = n_rows * (F + M) + n_rows * (F + 4 + 8 * K)
     else:
-        epilogue = n_rows * (Rw + F + M) + (v_rows * (Rw + F + 8) if w.expand else n_rows * (Rw + F + 4 + 8 * K))
-    combine = lanes * 16 + (v_rows if w.expand else n_rows) * Y + S * T * Y
+        epilogue = n_rows * (Rw + F + M) + ((v_rows + pad_rows) * (Rw + F + 8) if w.expand
+                                            else n_rows * (Rw + F + 4 + 8 * K))
+    combine = lanes * 16 + (v_rows if w.expand else n_rows) * Y + S * T * Y + n_bias * S * T * Y
     return dict(layout=layout, scatter=scatter, epilogue=epilogue, combine=combine,
                 total=layout + scatter + epilogue + combine)
 
@@ -219,6 +222,81 @@ def summarize_trace(stats_csv: str, bench_json: str, out_md: str, command: str) 
     print("\n".join(lines))
 
 
+def measure_extras(steps: int, warmup: int) -> dict:
+    """The API's further modes at the headline shape (4096 tokens, H=7168 bf16,
+    top-8 of 256 experts on 16 ranks), each timed as whole steps between two
+    events on the launch stream, on its own byte count:
+      bias2          combine adds two bias tensors (ep_combine_bias);
+      cached_layout  dispatch + combine replaying a layout computed once;
+      expand_a128    expand layout, expert alignment 128 with zero padding;
+      hybrid_2x8     hybrid row form: 16 sources = 2 scale-out x 8 scale-up
+                     ranks of 256 tokens each, Nmax = 256."""
+    import torch
+
+    import combine_ep_layout_07_amd.ep as ep
+    from combine_ep_layout_07_amd.workloads import WORKLOADS, generate, seed_for
+
+    stream = torch.cuda.current_stream()
+    base = WORKLOADS[2]
+    cases = {
+        "bias2": base,
+        "cached_layout": base,
+        "expand_a128": base.with_(name="dsv3_share_expand_a128", expand=True, alignment=128),
+        "hybrid_2x8": base.with_(name="hybrid_2x8", S=16, T=256, Nmax=256, n_out=2),
+    }
+    res = {}
+    for name, w in cases.items():
+        print(f"[bench] extra: {name}", file=sys.stderr, flush=True)
+        d = generate(w, seed_for(2, 5))
+        topk = torch.from_numpy(d["topk_idx"]).cuda()
+        wts = torch.from_numpy(d["topk_weights"]).cuda()
+        x = torch.from_numpy(d["x"].reshape(w.S * w.T, -1)).cuda()
+        cfg = ep.config_for(w)
+        L, R = ep.alloc_layout(cfg), ep.alloc_recv(cfg)
+        rows_cap = int(ep.ep_query_sizes(cfg).recv_rows)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(777)
+        y = torch.randn((rows_cap, w.H), generator=gen, device="cuda").to(torch.bfloat16)
+        out = torch.empty((w.S * w.T, w.H), dtype=torch.bfloat16, device="cuda")
+        bias = [torch.randn((w.S * w.T, w.H), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(2)]
+        ep.ep_layout(cfg, topk, L, stream)
+
+        def step():
+            if name != "cached_layout":
+                ep.ep_layout(cfg, topk, L, stream)
+            ep.ep_dispatch(cfg, x, None, topk, wts, L, R, ep.EP_PHASE_ALL, stream)
+            if name == "bias2":
+                ep.ep_combine_bias(cfg, L, topk, wts, y, bias[0], bias[1], out, stream)
+            else:
+                ep.ep_combine(cfg, L, topk, wts, y, out, stream)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        n_rows = int(L.recv_base[-1].item())
+        v_rows = int(((topk >= 0) & (topk < w.E)).sum().item())
+        pad = int(L.expert_base[-1].item()) - v_rows if w.expand else 0
+        b = alg_bytes(w, n_rows, v_rows, pad_rows=pad, n_bias=2 if name == "bias2" else 0)
+        total = b["total"] - (b["layout"] if name == "cached_layout" else 0)
+        res[name] = {"workload": f"{w.name}: S={w.S} T={w.T} H={w.H} K={w.K} E={w.E} R={w.R} Nmax={w.Nmax}"
+                                 f"{' expand A=%d' % w.alignment if w.expand else ''}"
+                                 f"{' n_out=%d' % w.n_out if w.n_out > 1 else ''}",
+                     "value": round(total / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+                     "pct_of_peak": round(100.0 * total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+                     "ms_per_step": round(ms, 5), "tokens_per_s": round(w.S * w.T / (ms * 1e-3), 1),
+                     "alg_bytes_per_step": total, "rows": {"dedup_N": n_rows, "valid_V": v_rows, "padding": pad}}
+        del L, R, y, out, bias, x
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,6 +307,8 @@ def main():
     ap.add_argument("--no-direct", action="store_true", help="skip the Direct Recv X variant")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache per-stage timing")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the bias / cached-layout / expand-alignment / hybrid measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (the reference for the byte counters)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
@@ -427,6 +507,8 @@ def main():
             "ms_per_step": round(ms_d, 5), "tokens_per_s": round(w.S * w.T / (ms_d * 1e-3), 1),
             "alg_bytes_per_step": bd, "stage_us": {k: round(v * 1e3, 2) for k, v in stage_d.items()},
             "speedup_vs_staging": round(ms / ms_d, 3)}
+    if args.config == 2 and not args.no_extras:
+        res["extras"] = measure_extras(args.steps, args.warmup)
     if args.copy_calibration:
         copy_calibration()
     if not args.no_cpu_baseline:

@@ -90,3 +90,14 @@ def test_counter_summary_round_trip(tmp_path, monkeypatch):
     assert bench.read_traffic(0) == pytest.approx(want)
     src.write_text("int k2;\n")
     assert bench.read_traffic(0) is None
+
+
+def test_algorithmic_bytes_padding_and_bias_terms():
+    w = WORKLOADS[2].with_(expand=True, alignment=128)
+    base = bench.alg_bytes(w, 26719, 32768)
+    padded = bench.alg_bytes(w, 26719, 32768, pad_rows=1000)
+    assert padded["epilogue"] - base["epilogue"] == 1000 * (7168 * 2 + 8)
+    assert padded["combine"] == base["combine"]          # padding rows are never combined
+    b2 = bench.alg_bytes(WORKLOADS[2], 26719, 32768, n_bias=2)
+    b0 = bench.alg_bytes(WORKLOADS[2], 26719, 32768)
+    assert b2["combine"] - b0["combine"] == 2 * 4096 * 7168 * 2

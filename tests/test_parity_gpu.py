@@ -188,6 +188,18 @@ def test_hybrid_direct_recv_x():
     _full_case(HYBRID[0], 21, direct=True, check_combine=False)
 
 
+def test_expand_alignment_128_at_dsv3_shape():
+    """The expand layout at the pages' benchmark alignment (128, zero padding)
+    on the 4096-token H=7168 shape: ~32k padding rows next to 32k lane rows."""
+    _full_case(WORKLOADS[2].with_(name="dsv3_share_expand_a128", expand=True, alignment=128), seed_for(2, 5))
+
+
+def test_hybrid_2x8_at_dsv3_token_count():
+    """16 sources of 256 tokens (2 scale-out x 8 scale-up): the same 4096
+    tokens as the headline shape, in the hybrid row form."""
+    _full_case(WORKLOADS[2].with_(name="hybrid_2x8", S=16, T=256, Nmax=256, n_out=2), seed_for(2, 5))
+
+
 def test_error_flag_for_out_of_range_ids():
     w = Workload("bad_ids", S=1, T=64, H=64, K=4, E=16, R=4, Nmax=64)
     inputs = generate(w, 3, invalid_frac=0.2)
