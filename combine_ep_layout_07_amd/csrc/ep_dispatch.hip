@@ -387,7 +387,8 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_expand(DispatchArgs a, in
 }
 
 // Padding rows of each expert segment (alignment A > 1): zero row and
-// scales, source index -1, weight +0.  One workgroup per expert.
+// scales, source index -1, weight +0.  Workgroup (e, y) takes rows r0 + y,
+// r0 + y + gridDim.y, ... of expert e's padding (at most A - 1 rows).
 __global__ void __launch_bounds__(kThreads) k_expand_padding(DispatchArgs a) {
     const Shape &sh = a.sh;
     const int e = blockIdx.x;
@@ -397,7 +398,7 @@ __global__ void __launch_bounds__(kThreads) k_expand_padding(DispatchArgs a) {
     const int r1 = (int)min((int64_t)a.expert_base[e + 1], a.recv_capacity_rows);
     const int nchunks = sh.row_bytes / 16;
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int r = r0; r < r1; ++r) {
+    for (int r = r0 + (int)blockIdx.y; r < r1; r += (int)gridDim.y) {
         uint8_t *dst = a.recv_x + (int64_t)r * sh.row_bytes;
         for (int c = threadIdx.x; c < nchunks; c += kThreads) st16<false>(dst + (int64_t)c * 16, zero);
         for (int q = threadIdx.x; q < sh.sf_per_row; q += kThreads) a.recv_sf[(int64_t)r * sh.sf_per_row + q] = 0.0f;
@@ -507,7 +508,8 @@ hipError_t launch_epilogue(const DispatchArgs &a, hipStream_t stream) {
     }
     if (err != hipSuccess) return err;
     if (a.sh.expand && a.sh.A > 1) {
-        hipLaunchKernelGGL(k_expand_padding, dim3(a.sh.E), dim3(kThreads), 0, stream, a);
+        const int split = a.sh.A - 1 < 16 ? a.sh.A - 1 : 16;  // workgroups per expert
+        hipLaunchKernelGGL(k_expand_padding, dim3(a.sh.E, split), dim3(kThreads), 0, stream, a);
         err = hipGetLastError();
     }
     return err;
