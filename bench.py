@@ -222,6 +222,36 @@ def summarize_trace(stats_csv: str, bench_json: str, out_md: str, command: str) 
     print("\n".join(lines))
 
 
+def measure_ceilings(reps: int = 10) -> dict:
+    """Practical HBM ceilings of this device for context: torch's own device
+    kernels on 1 GiB buffers (copy_ reads and writes, fill_ writes), timed
+    between events on the current stream.  (torch's reductions are not
+    read-bound enough to serve as a read ceiling.)"""
+    import torch
+
+    n = 1 << 30
+    stream = torch.cuda.current_stream()
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    ops = {"copy": (lambda: b.copy_(a), 2 * n), "write": (lambda: b.fill_(2.0), n)}
+    res = {}
+    for name, (fn, nbytes) in ops.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbps = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        res[name] = {"GB/s": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+    del a, b
+    torch.cuda.empty_cache()
+    res["what"] = "torch copy_ (read + write) and fill_ (write) on 1 GiB, 10 back-to-back launches"
+    return res
+
+
 def measure_extras(steps: int, warmup: int) -> dict:
     """The API's further modes at the headline shape (4096 tokens, H=7168 bf16,
     top-8 of 256 experts on 16 ranks), each timed as whole steps between two
@@ -509,6 +539,8 @@ def main():
             "speedup_vs_staging": round(ms / ms_d, 3)}
     if args.config == 2 and not args.no_extras:
         res["extras"] = measure_extras(args.steps, args.warmup)
+    if not args.no_extras:
+        res["ceilings"] = measure_ceilings()
     if args.copy_calibration:
         copy_calibration()
     if not args.no_cpu_baseline:

@@ -36,7 +36,8 @@ int make_shape(const ep_config_t *c, ep::Shape *sh) {
     if (c->x_dtype != EP_DTYPE_BF16 && c->x_dtype != EP_DTYPE_FP8_E4M3FN) return EP_ERR_INVALID_ARG;
     if (c->expand != 0 && c->expand != 1) return EP_ERR_INVALID_ARG;
     if (c->num_experts % c->num_ranks != 0) return EP_ERR_INVALID_ARG;
-    if (c->num_ranks > EP_MAX_RANKS || c->num_topk > EP_MAX_TOPK || c->num_experts > EP_MAX_EXPERTS)
+    if (c->num_ranks > EP_MAX_RANKS || c->num_topk > EP_MAX_TOPK || c->num_experts > EP_MAX_EXPERTS ||
+        c->hidden > EP_MAX_HIDDEN)
         return EP_ERR_UNSUPPORTED;
     const bool fp8 = c->x_dtype == EP_DTYPE_FP8_E4M3FN;
     if (fp8 && c->hidden % 128 != 0) return EP_ERR_INVALID_ARG;

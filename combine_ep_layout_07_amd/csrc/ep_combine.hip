@@ -6,10 +6,10 @@
 // out[s][t] = bf16(sum over valid lanes k of w[s][t][k] * Y [+ bias rows]),
 // accumulated in fp32 and rounded to nearest-even once.  In the compact layout
 // Y is the receive row that the owner lane of the lane's rank was given
-// (recv_base[d] + recv_psum[d][s] + slot - row_base(s)*Nmax), so lanes sharing a rank
-// weight the same row: the kernel reads that row once and applies the fp32
-// sum of those lanes' weights (taken in lane order).  In the expand layout Y
-// is the lane's own row expand_pos[s][t][k].
+// (recv_base[d] + recv_psum[d][s] + slot - row_base(s)*Nmax), so lanes sharing
+// a rank weight the same row: the kernel reads that row once and applies the
+// fp32 sum of those lanes' weights (taken in lane order).  In the expand layout
+// Y is the lane's own row expand_pos[s][t][k].
 //
 // The work is an HBM stream with about one FMA per 2 bytes read, far below
 // the MFMA ridge, so it runs on the vector ALUs.  A work unit is one column

@@ -76,7 +76,8 @@ def _rc(cfg):
     (dict(S=0), ep.EP_ERR_INVALID_ARG),
     (dict(T=-1), ep.EP_ERR_INVALID_ARG),
     (dict(S=2, Nmax=2**30 + 1, T=4096), ep.EP_ERR_UNSUPPORTED),  # S * Nmax >= 2^31
-    (dict(S=70000, Nmax=0, T=0), ep.EP_ERR_UNSUPPORTED),         # S > 65535
+    (dict(S=70000, Nmax=0, T=0), ep.EP_ERR_UNSUPPORTED),  # S > 65535
+    (dict(H=262144 + 8), ep.EP_ERR_UNSUPPORTED),          # H > EP_MAX_HIDDEN
 ])
 def test_validation_codes(kw, code):
     base = dict(S=1, T=4096, H=7168, K=8, E=256, R=16, Nmax=4096)
