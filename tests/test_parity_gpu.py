@@ -188,6 +188,16 @@ def test_hybrid_direct_recv_x():
     _full_case(HYBRID[0], 21, direct=True, check_combine=False)
 
 
+@pytest.mark.parametrize("cus", [0, 1200])
+def test_expand_widest_expert_and_topk_limits(cus):
+    """Expand at the limits: E = 1024 experts (16 expert-scan workgroups), K = 32
+    lanes per token (two tokens per wave step), R = 64, alignment 3; 1200
+    layout workgroups give 300 units, more per scan segment than it keeps in
+    registers."""
+    w = Workload("expand_e1024_k32", S=3, T=400, H=64, K=32, E=1024, R=64, Nmax=400, expand=True, alignment=3)
+    _full_case(w, 41, EDGE, num_layout_cus=cus)
+
+
 def test_expand_alignment_128_at_dsv3_shape():
     """The expand layout at the pages' benchmark alignment (128, zero padding)
     on the 4096-token H=7168 shape: ~32k padding rows next to 32k lane rows."""
