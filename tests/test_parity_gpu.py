@@ -10,6 +10,8 @@ K * 2^-24 * sum|w*y| ~ 3e-6, which the absolute term covers).
 The five workloads run at their full sizes in the launch configuration the
 benchmark times; the small cases cover edge lanes, ragged sizes and limits.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -375,3 +377,19 @@ def test_random_small_configurations(seed):
     edge = dict(masked_frac=float(rng.random() * 0.3), invalid_frac=float(rng.random() * 0.05),
                 dup_frac=float(rng.random() * 0.4))
     _full_case(w, 100 + seed, edge, num_layout_cus=int(rng.choice([0, 0, 1, 5])), direct=direct)
+
+
+def test_readme_example_runs():
+    """The Python example in README.md, executed as written: with an identity
+    expert the combine returns bf16(sum_k w_k * x) = x up to rounding."""
+    import re
+
+    text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "README.md")).read()
+    code = re.search(r"```python\n(.*?)```", text, flags=re.S).group(1)
+    say("[case] README example")
+    env = {}
+    exec(compile(code, "README.md", "exec"), env)
+    torch.cuda.synchronize()
+    x, out, w = env["x"].float(), env["out"].float(), env["topk_w"]
+    want = x * w.sum(-1).reshape(-1, 1)
+    assert torch.allclose(out, want, rtol=1e-2, atol=1e-2)
