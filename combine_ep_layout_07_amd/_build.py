@@ -53,5 +53,22 @@ def build_library(lib: str = LIB, obj_dir: str = OBJ, defines=()) -> str:
     return lib
 
 
+EXAMPLE_SRC = os.path.join(HERE, "examples", "ep_example.c")
+EXAMPLE_BIN = os.path.join(HERE, "examples", "ep_example")
+
+
+def build_example(lib_dir: str = HERE) -> str:
+    """The plain-C11 example of the ABI, built with gcc against include/ep.h
+    and libep.so (no C++ and no torch on that side)."""
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           "-I", os.path.join(ROOT, "include"), EXAMPLE_SRC, "-L", lib_dir, "-lep", "-L/opt/rocm/lib",
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/..", "-Wl,-rpath,/opt/rocm/lib", "-o", EXAMPLE_BIN]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0 or r.stderr.strip():
+        raise RuntimeError(f"gcc failed for the C example:\n{r.stdout}\n{r.stderr}")
+    return EXAMPLE_BIN
+
+
 if __name__ == "__main__":
     print(build_library())
+    print(build_example())

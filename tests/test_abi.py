@@ -5,6 +5,7 @@ import ctypes
 import json
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -186,3 +187,14 @@ def test_binding_refuses_host_tensors():
     cfg = ep.make_config(1, 4, 64, 2, 8, 4, 4)
     with pytest.raises(ValueError):
         ep._ptr(torch.zeros(4), "x", 16)
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/ep.h compiles as strict C11 on its own (no C++ types leak into
+    the boundary)."""
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "ep.h"\nint main(void) { ep_config_t c; (void)c; return EP_OK; }\n')
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    r = subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only", "-I", inc,
+                        str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr

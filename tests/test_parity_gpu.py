@@ -393,3 +393,17 @@ def test_readme_example_runs():
     x, out, w = env["x"].float(), env["out"].float(), env["topk_w"]
     want = x * w.sum(-1).reshape(-1, 1)
     assert torch.allclose(out, want, rtol=1e-2, atol=1e-2)
+
+
+def test_plain_c_example_runs():
+    """combine_ep_layout_07_amd/examples/ep_example.c: the ABI driven from C11
+    with hipMalloc'd buffers (built by build()); it checks its own results."""
+    import subprocess
+
+    from combine_ep_layout_07_amd import _build
+
+    assert os.path.exists(_build.EXAMPLE_BIN), "the C example is not built; run __graft_entry__.build()"
+    say("[case] plain C example")
+    r = subprocess.run([_build.EXAMPLE_BIN], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "ep_example: ok" in r.stdout
