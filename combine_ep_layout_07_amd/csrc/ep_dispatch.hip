@@ -59,6 +59,12 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #ifndef EP_EPILOGUE_BLOCKS
 #define EP_EPILOGUE_BLOCKS 2048
 #endif
+#ifndef EP_SCATTER_BLOCKS
+#define EP_SCATTER_BLOCKS 2048
+#endif
+#ifndef EP_DIRECT_INFLIGHT_BYTES
+#define EP_DIRECT_INFLIGHT_BYTES 7340032
+#endif
 #ifndef EP_COPY_BLOCKS
 #define EP_COPY_BLOCKS 2048
 #endif
@@ -77,6 +83,32 @@ __device__ __forceinline__ void st16(uint8_t *p, u32x4 v) {
 }
 
 // ----------------------------------------------------------------- scatter
+// Scales and metadata record {t, expert ids, weight bits} of token g for the
+// staging row of every owner lane.  Metadata words i = lane and i = lane + 64
+// (K = 32 needs 65 words): word 0 = t, words 1..K = expert ids, words
+// K+1..2K = weight bits, shuffled with every lane active before any divergent
+// store.
+__device__ __forceinline__ void store_records(const DispatchArgs &a, int64_t g, int s, int t, int e, int slot,
+                                              int wbits, uint64_t owners, int lane) {
+    const Shape &sh = a.sh;
+    const int ev = shfl(e, lane >= 1 ? lane - 1 : 0);
+    const int wv = shfl(wbits, lane - 1 - sh.K >= 0 ? lane - 1 - sh.K : 0);
+    const int hi_src = lane + kWave - 1 - sh.K;
+    const int wv_hi = shfl(wbits, hi_src >= 0 && hi_src < kWave ? hi_src : 0);
+    const int word0 = lane == 0 ? t : (lane <= sh.K ? ev : wv);
+    for (uint64_t m = owners; m; m &= m - 1) {
+        const int k = __builtin_ctzll(m);
+        const int d = read_lane(e, k) / sh.El;
+        const int j = read_lane(slot, k) - row_base(sh, s) * sh.Nmax;
+        if ((unsigned)j >= (unsigned)sh.Nmax) continue;
+        const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
+        for (int i = lane; i < sh.sf_per_row; i += kWave)
+            a.staging_sf[row * sh.sf_per_row + i] = a.x_sf[g * sh.sf_per_row + i];
+        if (lane < sh.meta_words) a.staging_meta[row * sh.meta_words + lane] = word0;
+        if (lane + kWave < sh.meta_words) a.staging_meta[row * sh.meta_words + lane + kWave] = wv_hi;
+    }
+}
+
 // One wave per token (s, t): load the row once, store it to row
 // j = slot - row_base(s)*Nmax of source s's region in the staging rows of
 // every owner lane's destination d (or, with Direct Recv X, to the compact
@@ -149,27 +181,102 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
                 }
             }
         }
-        if (slice != 0) continue;
-        // Metadata words i = lane and i = lane + 64 (K = 32 needs 65 words):
-        // word 0 = t, words 1..K = expert ids, words K+1..2K = weight bits.
-        // Shuffled with every lane active, before any divergent store.
-        const int ev = shfl(e, lane >= 1 ? lane - 1 : 0);
-        const int wv = shfl(wbits, lane - 1 - sh.K >= 0 ? lane - 1 - sh.K : 0);
-        const int hi_src = lane + kWave - 1 - sh.K;
-        const int wv_hi = shfl(wbits, hi_src >= 0 && hi_src < kWave ? hi_src : 0);
-        const int word0 = lane == 0 ? t : (lane <= sh.K ? ev : wv);
-        // Scales and metadata of every owner's staging row.
-        for (uint64_t m = owners; m; m &= m - 1) {
-            const int k = __builtin_ctzll(m);
-            const int d = read_lane(e, k) / sh.El;
-            const int j = read_lane(slot, k) - row_base(sh, s) * sh.Nmax;
-            if ((unsigned)j >= (unsigned)sh.Nmax) continue;
-            const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
-            for (int i = lane; i < sh.sf_per_row; i += kWave)
-                a.staging_sf[row * sh.sf_per_row + i] = a.x_sf[g * sh.sf_per_row + i];
-            if (lane < sh.meta_words) a.staging_meta[row * sh.meta_words + lane] = word0;
-            if (lane + kWave < sh.meta_words) a.staging_meta[row * sh.meta_words + lane + kWave] = wv_hi;
+        if (slice == 0) store_records(a, g, s, t, e, slot, wbits, owners, lane);
+    }
+}
+
+// ------------------------------------------- Direct Recv X scatter, pipelined
+// The stores of one token (whole row in one pass): rows, scales and metadata.
+template <int CPL>
+__device__ __forceinline__ void scatter_token(const DispatchArgs &a, int64_t g, int e, int slot, int wbits,
+                                              const u32x4 (&v)[CPL], int lane) {
+    const Shape &sh = a.sh;
+    const int nchunks = sh.row_bytes / 16;
+    const int s = (int)(g / sh.T), t = (int)(g - (int64_t)s * sh.T);
+    const uint64_t owners = ballot(lane < sh.K && slot >= 0);
+    int recv_row0 = 0;
+    if (sh.direct && lane < sh.K && slot >= 0) {
+        const int d = e / sh.El;
+        recv_row0 = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s];
+    }
+    for (uint64_t m = owners; m; m &= m - 1) {
+        const int k = __builtin_ctzll(m);
+        const int d = read_lane(e, k) / sh.El;
+        const int j = read_lane(slot, k) - row_base(sh, s) * sh.Nmax;
+        if ((unsigned)j >= (unsigned)sh.Nmax) continue;
+        if (sh.direct) {
+            const int64_t i = (int64_t)read_lane(recv_row0, k) + j;
+            if (i >= a.recv_capacity_rows) continue;
+            uint8_t *dst = a.recv_x + i * sh.row_bytes;
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) {
+                const int c = q * kWave + lane;
+                if (c < nchunks) st16<EP_DIRECT_NT_STORE>(dst + (int64_t)c * 16, v[q]);
+            }
+        } else {
+            uint8_t *dst = a.staging_x + (staging_region(sh, d, s) * sh.Nmax + j) * sh.row_bytes;
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) {
+                const int c = q * kWave + lane;
+                if (c < nchunks) st16<EP_SCATTER_NT_STORE>(dst + (int64_t)c * 16, v[q]);
+            }
         }
+    }
+    store_records(a, g, s, t, e, slot, wbits, owners, lane);
+}
+
+// Software-pipelined scatter, used for Direct Recv X: each wave takes tokens
+// g, g + nwaves, ... and loads the next token's ids, slots, weights and row
+// before storing the current one, so its reads overlap its writes; the grid
+// is sized so that the resident waves hold about EP_DIRECT_INFLIGHT_BYTES of
+// rows.  Measured on MI355X (Direct Recv X steps at T=4096, H=7168: 175 ->
+// 166 us; fp8 and H=4096 rows 1-2% faster): with the receive rows written
+// non-temporally straight to HBM, fewer waves that overlap their own reads
+// and writes beat one wave per token.  The staging scatter keeps one wave per
+// token: it gains from writes the Infinity Cache absorbs and measured no
+// faster pipelined.  Needs the whole row in one pass (64 * CPL chunks).
+template <int CPL>
+__global__ void __launch_bounds__(kThreads) k_scatter_pf(DispatchArgs a) {
+    const Shape &sh = a.sh;
+    const int lane = lane_id();
+    const int64_t n_tok = (int64_t)sh.S * sh.T;
+    const int nchunks = sh.row_bytes / 16;
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+    int64_t g = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    if (g >= n_tok) return;
+    auto fetch = [&](int64_t gg, int &e_, int &slot_, int &w_, u32x4 (&vv)[CPL]) {
+        e_ = -1;
+        slot_ = -1;
+        w_ = 0;
+        if (lane < sh.K) {
+            const int64_t e64 = a.topk_idx[gg * sh.K + lane];
+            e_ = (e64 >= 0 && e64 < sh.E) ? (int)e64 : -1;
+            slot_ = a.dst_slot[gg * sh.K + lane];
+            w_ = __float_as_int(a.topk_weights[gg * sh.K + lane]);
+        }
+        const uint8_t *src = a.x + gg * sh.row_bytes;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = i * kWave + lane;
+            if (c < nchunks) vv[i] = ld16<EP_SCATTER_NT_LOAD>(src + (int64_t)c * 16);
+        }
+    };
+    int e, slot, wbits;
+    u32x4 v[CPL];
+    fetch(g, e, slot, wbits, v);
+    while (true) {
+        const int64_t gn = g + nwaves;
+        const bool more = gn < n_tok;
+        int en = -1, sn = -1, wn = 0;
+        u32x4 vn[CPL];
+        if (more) fetch(gn, en, sn, wn, vn);
+        scatter_token<CPL>(a, g, e, slot, wbits, v, lane);
+        if (!more) break;
+        g = gn;
+        e = en;
+        slot = sn;
+        wbits = wn;
+        for (int i = 0; i < CPL; ++i) v[i] = vn[i];
     }
 }
 
@@ -454,7 +561,15 @@ struct ScatterL {
         a.slices = EP_SCATTER_SLICES < 1 ? 1 : EP_SCATTER_SLICES;
         if (a.slices > (nchunks + kWave - 1) / kWave) a.slices = (nchunks + kWave - 1) / kWave;
         const int64_t units = (int64_t)a.sh.S * a.sh.T * a.slices;
-        hipLaunchKernelGGL(k_scatter<CPL>, dim3(grid_for(units)), dim3(kThreads), 0, st, a);
+        if (a.sh.direct && a.slices == 1 && nchunks <= CPL * kWave) {
+            // about EP_DIRECT_INFLIGHT_BYTES of rows held by the resident waves
+            int64_t blocks = ((int64_t)EP_DIRECT_INFLIGHT_BYTES + (int64_t)a.sh.row_bytes * kWavesPerBlock - 1) /
+                             ((int64_t)a.sh.row_bytes * kWavesPerBlock);
+            blocks = blocks < 1 ? 1 : (blocks > EP_COPY_BLOCKS ? EP_COPY_BLOCKS : blocks);
+            hipLaunchKernelGGL(k_scatter_pf<CPL>, dim3(grid_for(units, (int)blocks)), dim3(kThreads), 0, st, a);
+            return hipGetLastError();
+        }
+        hipLaunchKernelGGL(k_scatter<CPL>, dim3(grid_for(units, EP_SCATTER_BLOCKS)), dim3(kThreads), 0, st, a);
         return hipGetLastError();
     }
 };
