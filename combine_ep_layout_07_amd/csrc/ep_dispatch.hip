@@ -378,6 +378,62 @@ __global__ void __launch_bounds__(kThreads) k_epilogue(DispatchArgs a, int table
     }
 }
 
+// Software-pipelined compact epilogue, the default when a row fits one pass
+// (64 * CPL chunks): each wave takes receive rows i, i + nwaves, ... and
+// loads the next row before storing the current one, so its reads overlap its
+// writes.  Measured on MI355X with the same grid as one row per pass: the
+// epilogue 143 -> 139 us at T=4096, H=7168 (steps 1.5-3.5% faster on the
+// bf16, fp8 and H=4096 workloads).
+template <int CPL>
+__global__ void __launch_bounds__(kThreads) k_epilogue_pf(DispatchArgs a, int tables_in_lds) {
+    const Shape &sh = a.sh;
+    extern __shared__ int32_t lds_tab[];
+    const int32_t *tab = stage_tables(a, lds_tab, tables_in_lds != 0);
+    const int32_t *rbase = tab ? tab : a.recv_base;
+    const int32_t *rpsum = tab ? tab + sh.R + 1 : a.recv_psum;
+    const int lane = lane_id();
+    const int n_rows = (int)min((int64_t)a.recv_base[sh.R], a.recv_capacity_rows);
+    const int nchunks = sh.row_bytes / 16;
+    const int nwaves = gridDim.x * kWavesPerBlock;
+    int i = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    if (i >= n_rows) return;
+    auto fetch = [&](int ii, int &d_, int &s_, int &j_, u32x4 (&vv)[CPL]) {
+        locate_row(rbase, rpsum, sh.R, sh.S, ii, lane, d_, s_, j_);
+        if ((unsigned)j_ >= (unsigned)sh.Nmax) return;  // never true for tables of one layout
+        const uint8_t *src = a.staging_x + (staging_region(sh, d_, s_) * sh.Nmax + j_) * sh.row_bytes;
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+            const int c = q * kWave + lane;
+            if (c < nchunks) vv[q] = ld16<EP_EPILOGUE_NT_LOAD>(src + (int64_t)c * 16);
+        }
+    };
+    int d, s, j;
+    u32x4 v[CPL];
+    fetch(i, d, s, j, v);
+    while (true) {
+        const int in = i + nwaves;
+        const bool more = in < n_rows;
+        int dn = 0, sn = 0, jn = -1;
+        u32x4 vn[CPL];
+        if (more) fetch(in, dn, sn, jn, vn);
+        if ((unsigned)j < (unsigned)sh.Nmax) {
+            uint8_t *dst = a.recv_x + (int64_t)i * sh.row_bytes;
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) {
+                const int c = q * kWave + lane;
+                if (c < nchunks) st16<EP_EPILOGUE_NT_STORE>(dst + (int64_t)c * 16, v[q]);
+            }
+            epilogue_row<CPL>(a, d, s, j, i, lane, 0, 0);  // scales and metadata only
+        }
+        if (!more) break;
+        i = in;
+        d = dn;
+        s = sn;
+        j = jn;
+        for (int q = 0; q < CPL; ++q) v[q] = vn[q];
+    }
+}
+
 // Last index q in [0, n) with tab[q] <= key, for a non-decreasing table whose
 // first entry is <= key.
 __device__ __forceinline__ int last_le(const int32_t *tab, int n, int key) {
@@ -586,6 +642,9 @@ struct EpilogueL {
         if (a.sh.expand)
             hipLaunchKernelGGL(k_epilogue_expand<CPL>, dim3(grid_for(rows)), dim3(kThreads), fits ? tab : 0, st, a,
                                (int)fits);
+        else if (a.slices == 1 && a.sh.row_bytes / 16 <= CPL * kWave)
+            hipLaunchKernelGGL(k_epilogue_pf<CPL>, dim3(grid_for(rows, EP_EPILOGUE_BLOCKS)), dim3(kThreads),
+                               fits ? tab : 0, st, a, (int)fits);
         else
             hipLaunchKernelGGL(k_epilogue<CPL>, dim3(grid_for(rows * a.slices, EP_EPILOGUE_BLOCKS)), dim3(kThreads),
                                fits ? tab : 0, st, a,

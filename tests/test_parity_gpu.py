@@ -200,6 +200,18 @@ def test_expand_widest_expert_and_topk_limits(cus):
     _full_case(w, 41, EDGE, num_layout_cus=cus)
 
 
+@pytest.mark.parametrize("mode", ["staging", "direct", "expand", "fp8"])
+def test_rows_wider_than_one_pass(mode):
+    """H = 10240 bf16 (or 16512 fp8): 1280 (1032) 16-byte chunks per row, more
+    than one pass of 64 lanes x 16 chunks, so the scatter, the epilogues and
+    the combine loop over column passes (the pipelined one-pass kernels are
+    not used)."""
+    fp8 = mode == "fp8"
+    w = Workload(f"wide_{mode}", S=2, T=45, H=16512 if fp8 else 10240, K=4, E=16, R=4, Nmax=48,
+                 expand=mode == "expand", alignment=2 if mode == "expand" else 1, dtype="fp8" if fp8 else "bf16")
+    _full_case(w, 51, EDGE, direct=mode == "direct")
+
+
 def test_expand_alignment_128_at_dsv3_shape():
     """The expand layout at the pages' benchmark alignment (128, zero padding)
     on the 4096-token H=7168 shape: ~32k padding rows next to 32k lane rows."""
