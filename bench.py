@@ -495,7 +495,7 @@ def main():
         "rows": {"dedup_N": n_rows, "valid_V": v_rows},
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "stage_gbps": {k: round(b[k] / (stage_ms[k] * 1e-3) / 1e9, 1) for k in names},
-        "roofline": {"bound": "hbm", "kernel": "k_epilogue (copy epilogue)", "achieved": round(epi_gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_epilogue_pf (copy epilogue)", "achieved": round(epi_gbps, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(epi_gbps / PEAK_HBM_GBPS, 4),
                      "alg_bytes_per_launch": epi_alg, "traffic": traffic,
                      "timing": "mean of K epilogue launches back to back between two HIP events on the launch "
