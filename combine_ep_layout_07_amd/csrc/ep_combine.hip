@@ -44,6 +44,7 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #endif
 constexpr int kRowsPerGroup = EP_COMBINE_ROWS;
 
+
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) {
     const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
 #if EP_COMBINE_NT_LOAD
@@ -72,6 +73,48 @@ __device__ __forceinline__ void fma_row(float (&acc)[CPL][8], const u32x4 (&v)[C
     }
 }
 
+// The distinct rows of token g, one per "row lane": every valid lane in the
+// expand layout; the owner (lowest valid lane) of each rank otherwise, whose
+// weight becomes the lane-ordered fp32 sum over the lanes of its rank.
+// Returns the mask of row lanes; row / wrow hold each row lane's row and weight.
+__device__ __forceinline__ uint64_t token_rows(const CombineArgs &a, int64_t g, int lane, int &row, float &wrow) {
+    const Shape &sh = a.sh;
+    const int s = (int)(g / sh.T);
+    bool valid = false;
+    float w = 0.0f;
+    int e = 0, slot = -1, pos = -1;
+    if (lane < sh.K) {
+        const int64_t e64 = a.topk_idx[g * sh.K + lane];
+        valid = e64 >= 0 && e64 < sh.E;
+        e = valid ? (int)e64 : 0;
+        w = a.topk_weights[g * sh.K + lane];
+        if (sh.expand) pos = a.expand_pos[g * sh.K + lane];
+        else slot = a.dst_slot[g * sh.K + lane];
+    }
+    const uint64_t vmask = ballot(valid);
+    row = -1;
+    wrow = 0.0f;
+    if (sh.expand) {
+        row = valid ? pos : -1;
+        wrow = w;
+    } else {
+        const int d = valid ? e / sh.El : 0;
+        const uint64_t peers = match_key((uint32_t)d, sh.bits_R, vmask);
+        const int owner = peers ? __builtin_ctzll(peers) : 0;
+        const bool is_owner = valid && owner == lane;
+        if (is_owner)
+            row = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s] + (slot - row_base(sh, s) * sh.Nmax);
+        for (uint64_t m = vmask; m; m &= m - 1) {
+            const int k = __builtin_ctzll(m);
+            const float wk = __int_as_float(read_lane(__float_as_int(w), k));
+            const int ok = read_lane(owner, k);
+            if (lane == ok) wrow += wk;
+        }
+    }
+    // Rows outside y never occur for a layout of this topk_idx; drop them.
+    return ballot(row >= 0 && (int64_t)row < a.y_rows);
+}
+
 template <int CPL>
 __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
     constexpr int G = kRowsPerGroup;
@@ -93,43 +136,9 @@ __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
         const int c_lo = (int)(unit - g * slices) * cps;
         const int c_hi = min(c_lo + cps, nchunks);
         if (c_lo >= c_hi) continue;
-        const int s = (int)(g / sh.T);
-        bool valid = false;
-        float w = 0.0f;
-        int e = 0, slot = -1, pos = -1;
-        if (lane < sh.K) {
-            const int64_t e64 = a.topk_idx[g * sh.K + lane];
-            valid = e64 >= 0 && e64 < sh.E;
-            e = valid ? (int)e64 : 0;
-            w = a.topk_weights[g * sh.K + lane];
-            if (sh.expand) pos = a.expand_pos[g * sh.K + lane];
-            else slot = a.dst_slot[g * sh.K + lane];
-        }
-        const uint64_t vmask = ballot(valid);
-        // Distinct rows, one per "row lane": every valid lane in the expand
-        // layout; the owner (lowest valid lane) of each rank otherwise, whose
-        // weight becomes the lane-ordered fp32 sum over the lanes of its rank.
-        int row = -1;
-        float wrow = 0.0f;
-        if (sh.expand) {
-            row = valid ? pos : -1;
-            wrow = w;
-        } else {
-            const int d = valid ? e / sh.El : 0;
-            const uint64_t peers = match_key((uint32_t)d, sh.bits_R, vmask);
-            const int owner = peers ? __builtin_ctzll(peers) : 0;
-            const bool is_owner = valid && owner == lane;
-            if (is_owner)
-                row = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s] + (slot - row_base(sh, s) * sh.Nmax);
-            for (uint64_t m = vmask; m; m &= m - 1) {
-                const int k = __builtin_ctzll(m);
-                const float wk = __int_as_float(read_lane(__float_as_int(w), k));
-                const int ok = read_lane(owner, k);
-                if (lane == ok) wrow += wk;
-            }
-        }
-        // Rows outside y never occur for a layout of this topk_idx; drop them.
-        const uint64_t rows_mask = ballot(row >= 0 && (int64_t)row < a.y_rows);
+        int row;
+        float wrow;
+        const uint64_t rows_mask = token_rows(a, g, lane, row, wrow);
         const int wbits = __float_as_int(wrow);
         uint16_t *out = a.out + g * sh.H;
         for (int c0 = c_lo; c0 < c_hi; c0 += CPL * kWave) {
