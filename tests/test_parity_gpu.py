@@ -374,7 +374,9 @@ def _random_workload(rng):
     S = n_out * int(rng.integers(1, 4))
     T = int(rng.integers(0, 200))
     dtype = "fp8" if rng.random() < 0.3 else "bf16"
-    H = int(rng.choice([128, 256, 384])) if dtype == "fp8" else int(rng.choice([8, 64, 136, 512, 1032]))
+    # row sizes that reach every chunks-per-lane instantiation below the full-size workloads' (1, 2, 4, 7)
+    H = int(rng.choice([128, 256, 384, 1152])) if dtype == "fp8" else int(rng.choice([8, 64, 136, 512, 1024, 1032,
+                                                                                         3072]))
     expand = bool(rng.random() < 0.3)
     return Workload(f"rand", S=S, T=T, H=H, K=K, E=R * El, R=R, Nmax=T + int(rng.integers(0, 5)), dtype=dtype,
                     expand=expand, alignment=int(rng.choice([1, 2, 8])) if expand else 1, n_out=n_out)
