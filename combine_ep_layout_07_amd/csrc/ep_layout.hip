@@ -29,7 +29,9 @@
 //     units also share out the per-source counts; expand adds the expert
 //     segment bases (padded totals, scanned over experts) to each unit's
 //     column prefix; one extra workgroup writes the receiver tables
-//     (recv_psum, recv_base, expert_base, error_flags).
+//     (recv_psum, recv_base, expert_base, error_flags);
+//   k_layout_single: for one source whose items fit one workgroup, all of the
+//     above in one launch (the unit's counts are the source's totals).
 #include "ep_device.h"
 #include "ep_kernels.h"
 
@@ -52,6 +54,14 @@ LayoutGeom layout_geometry(const Shape &sh, int num_layout_cus) {
     const int tps = kWave / sh.K;              // tokens per step
     const int min_chunk = kLayoutWaves * tps;  // one step per wave
     const int max_b = T > 4 ? (T + 3) / 4 : 1;     // at least one token per wave
+    g.single = 0;
+    if (num_layout_cus == 0 && sh.S == 1 && (T + 3) / 4 <= kBatch * tps) {
+        // every wave's quarter of the tokens fits one batch of loads
+        g.blocks_per_src = 1;
+        g.chunk = T > 0 ? (T + 3) / 4 * 4 : 4;
+        g.single = 1;
+        return g;
+    }
     int B;
     if (num_layout_cus > 0) {
         B = (num_layout_cus + sh.S - 1) / sh.S;
@@ -231,6 +241,59 @@ __device__ __forceinline__ void wave_range(const LayoutArgs &a, int b, int w, in
     const int cw = a.g.chunk / kLayoutWaves;
     t0 = min(b * a.g.chunk + w * cw, a.sh.T);
     t1 = min(t0 + cw, a.sh.T);
+}
+
+// Per-wave counts [4][n] in LDS become each wave's running base: base[i]
+// plus the counts of the earlier waves.  Every thread of the workgroup calls it.
+__device__ __forceinline__ void wave_bases(int *cnt, int n, const int *base) {
+    for (int i = threadIdx.x; i < n; i += kLayoutThreads) {
+        int run = base[i];
+        for (int q = 0; q < kLayoutWaves; ++q) {
+            const int v = cnt[q * n + i];
+            cnt[q * n + i] = run;
+            run += v;
+        }
+    }
+}
+
+// Ranking: every item of the wave's tokens [t0, t1) of source s gets its slot
+// (row_base * Nmax + running count, [DET] Approach) and, in the expand layout,
+// its row; run_d / run_e are the wave's running counters in LDS.  When the
+// range fits one batch, the ids are already in `buf`.
+__device__ void rank_range(const LayoutArgs &a, int s, int t0, int t1, const StepCtx &c,
+                           const int64_t (&buf)[kBatch], bool single, int *run_d, int *run_e) {
+    const Shape &sh = a.sh;
+    const bool expand = sh.expand != 0;
+    const int32_t slot_base = row_base(sh, s) * sh.Nmax;
+    auto rank = [&](const Item &it) {
+        const int rd = it.owner ? run_d[it.d] : 0;
+        const int re = (expand && it.valid) ? run_e[it.e] : 0;
+        if (it.in) {
+            const int64_t idx = ((int64_t)s * sh.T + it.t) * sh.K + it.k;
+            a.dst_slot[idx] = it.owner ? slot_base + rd + it.rank_d : -1;
+            if (expand) a.expand_pos[idx] = it.valid ? re + it.rank_e : -1;
+        }
+        if (it.last_d) run_d[it.d] = rd + it.rank_d + 1;
+        if (expand && it.last_e) run_e[it.e] = re + it.rank_e + 1;
+    };
+    if (single) {
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int ts = t0 + i * c.tps;
+            if (ts < t1) rank(make_item(sh, buf[i], ts, t1, c, expand));
+        }
+    } else {
+        const int64_t *topk_src = a.topk_idx + (int64_t)s * sh.T * sh.K;
+        for (int tb = t0; tb < t1; tb += kBatch * c.tps) {
+            int64_t b2[kBatch];
+            load_batch(sh, topk_src, tb, t1, c, b2);
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const int ts = tb + i * c.tps;
+                if (ts < t1) rank(make_item(sh, b2[i], ts, t1, c, expand));
+            }
+        }
+    }
 }
 
 __global__ void __launch_bounds__(kLayoutThreads) k_layout_count(LayoutArgs a) {
@@ -472,64 +535,80 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
     // Per-wave counts of this unit, then each wave's running base.
     wave_count(sh, topk_src, t0, t1, cnt_d + w * R, cnt_e + w * E, expand, c, buf, single);
     __syncthreads();
+    wave_bases(cnt_d, R, base_d);
+    if (expand) wave_bases(cnt_e, E, base_e);
+    __syncthreads();
+    rank_range(a, s, t0, t1, c, buf, single, cnt_d + w * R, cnt_e + w * E);
+}
+
+// The whole layout in one workgroup, for one source whose items fit one batch
+// of loads per wave: the unit's own counts are the source's totals, so the
+// receiver tables and the expert segment bases need no other workgroup, and
+// the layout takes one launch instead of two.
+__global__ void __launch_bounds__(kLayoutThreads) k_layout_single(LayoutArgs a) {
+    const Shape &sh = a.sh;
+    const int w = threadIdx.x / kWave, tid = threadIdx.x;
+    const int R = sh.R, E = sh.E;
+    const bool expand = sh.expand != 0;
+    extern __shared__ int lds[];
+    int *cnt_d = lds;                        // [4][R] per-wave counts, then running bases
+    int *cnt_e = cnt_d + kLayoutWaves * R;   // [4][E]
+    int *zero_d = cnt_e + kLayoutWaves * E;  // [R]   the unit's base per destination: 0
+    int *seg = zero_d + R;                   // [E]   expand: expert segment bases
+    int *part = seg + E;                     // [256] totals per destination, then scan scratch
+    int *flag = part + kLayoutThreads;       // [4]
+
+    int t0, t1;
+    wave_range(a, 0, w, t0, t1);
+    const StepCtx c = make_ctx(sh.K);
+    int64_t buf[kBatch];
+    load_batch(sh, a.topk_idx, t0, t1, c, buf);
+    for (int i = tid; i < kLayoutWaves * (R + E) + R + E; i += kLayoutThreads) lds[i] = 0;
+    __syncthreads();
+    const bool bad = wave_count(sh, a.topk_idx, t0, t1, cnt_d + w * R, cnt_e + w * E, true, c, buf, true);
+    if (lane_id() == 0) flag[w] = bad ? 1 : 0;
+    __syncthreads();
     for (int d = tid; d < R; d += kLayoutThreads) {
-        int run = base_d[d];
-        for (int q = 0; q < kLayoutWaves; ++q) {
-            const int v = cnt_d[q * R + d];
-            cnt_d[q * R + d] = run;
-            run += v;
-        }
+        int tot = 0;
+        for (int q = 0; q < kLayoutWaves; ++q) tot += cnt_d[q * R + d];
+        a.tokens_per_rank[d] = tot;
+        a.recv_psum[2 * d] = 0;
+        a.recv_psum[2 * d + 1] = tot;
+        part[d] = tot;
     }
-    if (expand) {
-        for (int e = tid; e < E; e += kLayoutThreads) {
-            int run = base_e[e];
-            for (int q = 0; q < kLayoutWaves; ++q) {
-                const int v = cnt_e[q * E + e];
-                cnt_e[q * E + e] = run;
-                run += v;
-            }
-        }
+    for (int e = tid; e < E; e += kLayoutThreads) {
+        int tot = 0;
+        for (int q = 0; q < kLayoutWaves; ++q) tot += cnt_e[q * E + e];
+        a.tokens_per_expert[e] = tot;
+        seg[e] = (tot + sh.A - 1) / sh.A * sh.A;
     }
     __syncthreads();
-
-    // Ranking: every item of the wave's range gets its slot / expand row.
-    {
-        int *run_d = cnt_d + w * R;
-        int *run_e = cnt_e + w * E;
-        const int32_t slot_base = row_base(sh, s) * sh.Nmax;  // row_base * Nmax ([DET] Approach)
-        auto rank = [&](const Item &it) {
-            const int rd = it.owner ? run_d[it.d] : 0;
-            const int re = (expand && it.valid) ? run_e[it.e] : 0;
-            if (it.in) {
-                const int64_t idx = ((int64_t)s * sh.T + it.t) * sh.K + it.k;
-                a.dst_slot[idx] = it.owner ? slot_base + rd + it.rank_d : -1;
-                if (expand) a.expand_pos[idx] = it.valid ? re + it.rank_e : -1;
-            }
-            if (it.last_d) run_d[it.d] = rd + it.rank_d + 1;
-            if (expand && it.last_e) run_e[it.e] = re + it.rank_e + 1;
-        };
-        if (single) {
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                const int ts = t0 + i * c.tps;
-                if (ts < t1) rank(make_item(sh, buf[i], ts, t1, c, expand));
-            }
-        } else {
-            for (int tb = t0; tb < t1; tb += kBatch * c.tps) {
-                int64_t b2[kBatch];
-                load_batch(sh, topk_src, tb, t1, c, b2);
-#pragma unroll
-                for (int i = 0; i < kBatch; ++i) {
-                    const int ts = tb + i * c.tps;
-                    if (ts < t1) rank(make_item(sh, b2[i], ts, t1, c, expand));
-                }
-            }
+    if (tid == 0) {
+        int run = 0;
+        for (int d = 0; d < R; ++d) {
+            a.recv_base[d] = run;
+            run += part[d];
         }
+        a.recv_base[R] = run;
+        a.error_flags[0] = (flag[0] | flag[1] | flag[2] | flag[3]) ? 1 : 0;
     }
+    __syncthreads();
+    if (expand) {
+        const int total = block_exclusive_scan<kLayoutThreads>(seg, E, part);
+        for (int e = tid; e < E; e += kLayoutThreads) a.expert_base[e] = seg[e];
+        if (tid == 0) a.expert_base[E] = total;
+    }
+    wave_bases(cnt_d, R, zero_d);
+    if (expand) wave_bases(cnt_e, E, seg);
+    __syncthreads();
+    rank_range(a, 0, t0, t1, c, buf, true, cnt_d + w * R, cnt_e + w * E);
 }
 
 size_t count_lds_bytes(const Shape &sh) {
     return sizeof(int) * ((size_t)kLayoutWaves * (sh.R + sh.E) + kLayoutWaves);
+}
+size_t single_lds_bytes(const Shape &sh) {
+    return sizeof(int) * ((size_t)kLayoutWaves * (sh.R + sh.E) + sh.R + sh.E + kLayoutThreads + kLayoutWaves);
 }
 size_t slot_lds_bytes(const Shape &sh) {
     return sizeof(int) * ((size_t)kLayoutWaves * (sh.R + sh.E) + sh.R + sh.E + (sh.R + sh.E) + kLayoutThreads);
@@ -538,6 +617,10 @@ size_t slot_lds_bytes(const Shape &sh) {
 }  // namespace
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
+    if (a.g.single) {
+        hipLaunchKernelGGL(k_layout_single, dim3(1), dim3(kLayoutThreads), single_lds_bytes(a.sh), stream, a);
+        return hipGetLastError();
+    }
     const dim3 grid(a.g.blocks_per_src, a.sh.S);
     hipLaunchKernelGGL(k_layout_count, grid, dim3(kLayoutThreads), count_lds_bytes(a.sh), stream, a);
     hipError_t err = hipGetLastError();

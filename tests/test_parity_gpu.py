@@ -238,12 +238,18 @@ def test_error_flag_for_out_of_range_ids():
     assert int(L.error_flags.item()) == 0
 
 
-@pytest.mark.parametrize("cfg_id", [2, 4, 5])
+SINGLE_EXPAND = Workload("single_expand", S=1, T=200, H=64, K=4, E=32, R=8, Nmax=200, expand=True, alignment=4)
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2, 4, 5, "single_expand"])
 def test_layout_independent_of_workgroup_count(cfg_id):
     """Slots are a pure function of topk_idx: the number of layout workgroups
-    (the pages' num_prologue_sms) changes nothing."""
-    w = WORKLOADS[cfg_id]
-    inputs = generate(w, seed_for(cfg_id), with_x=False)
+    (the pages' num_prologue_sms) changes nothing.  Workload 1 and the small
+    expand case take the one-launch layout at num_layout_cus = 0 and the
+    two-pass one otherwise."""
+    w = SINGLE_EXPAND if cfg_id == "single_expand" else WORKLOADS[cfg_id]
+    inputs = generate(w, seed_for(cfg_id) if cfg_id != "single_expand" else 61, with_x=False, masked_frac=0.1,
+                      invalid_frac=0.02, dup_frac=0.2)
     inputs["x"] = np.zeros((w.S, w.T, 16), np.uint8)
     dev = upload(w, inputs)
     ref = None
