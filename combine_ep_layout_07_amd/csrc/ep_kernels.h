@@ -38,7 +38,7 @@ __host__ __device__ inline int64_t staging_region(const Shape &sh, int d, int s)
 struct LayoutGeom {
     int blocks_per_src;
     int chunk;
-    int single;  // one source whose items fit one workgroup: the whole layout in one launch
+    int single;  // 0, or the waves (8 or 16) of the one-workgroup layout of a small single source
 };
 
 LayoutGeom layout_geometry(const Shape &sh, int num_layout_cus);

@@ -41,6 +41,12 @@ constexpr int kLayoutThreads = 256;
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kBatch = 8;  // steps whose items a wave loads together
 constexpr int kScanThreads = 1024;
+
+// LDS of the one-workgroup layout with nw waves: counts [nw][R+E], bases
+// [R+E], scan scratch [64 nw], flags [nw].
+size_t single_lds_bytes(const Shape &sh, int nw) {
+    return sizeof(int) * ((size_t)nw * (sh.R + sh.E) + sh.R + sh.E + (size_t)nw * kWave + nw);
+}
 constexpr int kScanCols = 64;                        // experts per scan workgroup
 constexpr int kScanSegs = kScanThreads / kScanCols;  // unit segments per expert
 constexpr int kScanRegs = 16;                        // counts a scan thread keeps in registers
@@ -55,12 +61,19 @@ LayoutGeom layout_geometry(const Shape &sh, int num_layout_cus) {
     const int min_chunk = kLayoutWaves * tps;  // one step per wave
     const int max_b = T > 4 ? (T + 3) / 4 : 1;     // at least one token per wave
     g.single = 0;
-    if (num_layout_cus == 0 && sh.S == 1 && (T + 3) / 4 <= kBatch * tps) {
-        // every wave's quarter of the tokens fits one batch of loads
-        g.blocks_per_src = 1;
-        g.chunk = T > 0 ? (T + 3) / 4 * 4 : 4;
-        g.single = 1;
-        return g;
+    // One source with at most 4096 (token, lane) items: the whole layout in one
+    // workgroup, 8 waves up to 1024 items, 16 above.  Measured on MI355X (K=8):
+    // 4.5 / 5.9 / 7.7 / 11.5 us at T = 64 / 128 / 256 / 512 against about 13 us
+    // for the two launches, which win again from T = 1024.
+    const int64_t lanes = (int64_t)T * sh.K;
+    if (num_layout_cus == 0 && sh.S == 1 && lanes <= 4096) {
+        const int nw = lanes <= 1024 ? 8 : 16;
+        if (single_lds_bytes(sh, nw) <= 65536) {
+            g.blocks_per_src = 1;
+            g.chunk = T > 0 ? (T + 3) / 4 * 4 : 4;
+            g.single = nw;
+            return g;
+        }
     }
     int B;
     if (num_layout_cus > 0) {
@@ -243,12 +256,13 @@ __device__ __forceinline__ void wave_range(const LayoutArgs &a, int b, int w, in
     t1 = min(t0 + cw, a.sh.T);
 }
 
-// Per-wave counts [4][n] in LDS become each wave's running base: base[i]
+// Per-wave counts [NW][n] in LDS become each wave's running base: base[i]
 // plus the counts of the earlier waves.  Every thread of the workgroup calls it.
+template <int NW = kLayoutWaves>
 __device__ __forceinline__ void wave_bases(int *cnt, int n, const int *base) {
-    for (int i = threadIdx.x; i < n; i += kLayoutThreads) {
+    for (int i = threadIdx.x; i < n; i += NW * kWave) {
         int run = base[i];
-        for (int q = 0; q < kLayoutWaves; ++q) {
+        for (int q = 0; q < NW; ++q) {
             const int v = cnt[q * n + i];
             cnt[q * n + i] = run;
             run += v;
@@ -541,44 +555,47 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
     rank_range(a, s, t0, t1, c, buf, single, cnt_d + w * R, cnt_e + w * E);
 }
 
-// The whole layout in one workgroup, for one source whose items fit one batch
-// of loads per wave: the unit's own counts are the source's totals, so the
-// receiver tables and the expert segment bases need no other workgroup, and
-// the layout takes one launch instead of two.
-__global__ void __launch_bounds__(kLayoutThreads) k_layout_single(LayoutArgs a) {
+// The whole layout in one workgroup of NW waves, for one small source: the
+// workgroup's own counts are the source's totals, so the receiver tables and
+// the expert segment bases need no other workgroup, and the layout takes one
+// launch instead of two.  Wave w owns tokens [w*cw, (w+1)*cw), cw = ceil(T/NW).
+template <int NW>
+__global__ void __launch_bounds__(NW * kWave) k_layout_single(LayoutArgs a) {
+    constexpr int NT = NW * kWave;
     const Shape &sh = a.sh;
     const int w = threadIdx.x / kWave, tid = threadIdx.x;
     const int R = sh.R, E = sh.E;
     const bool expand = sh.expand != 0;
     extern __shared__ int lds[];
-    int *cnt_d = lds;                        // [4][R] per-wave counts, then running bases
-    int *cnt_e = cnt_d + kLayoutWaves * R;   // [4][E]
-    int *zero_d = cnt_e + kLayoutWaves * E;  // [R]   the unit's base per destination: 0
-    int *seg = zero_d + R;                   // [E]   expand: expert segment bases
-    int *part = seg + E;                     // [256] totals per destination, then scan scratch
-    int *flag = part + kLayoutThreads;       // [4]
+    int *cnt_d = lds;               // [NW][R] per-wave counts, then running bases
+    int *cnt_e = cnt_d + NW * R;    // [NW][E]
+    int *zero_d = cnt_e + NW * E;   // [R]    the base per destination: 0
+    int *seg = zero_d + R;          // [E]    expand: expert segment bases
+    int *part = seg + E;            // [NT]   totals per destination, then scan scratch
+    int *flag = part + NT;          // [NW]
 
-    int t0, t1;
-    wave_range(a, 0, w, t0, t1);
+    const int cw = (sh.T + NW - 1) / NW;
+    const int t0 = min(w * cw, sh.T), t1 = min(t0 + cw, sh.T);
     const StepCtx c = make_ctx(sh.K);
+    const bool one_batch = t1 - t0 <= kBatch * c.tps;
     int64_t buf[kBatch];
-    load_batch(sh, a.topk_idx, t0, t1, c, buf);
-    for (int i = tid; i < kLayoutWaves * (R + E) + R + E; i += kLayoutThreads) lds[i] = 0;
+    if (one_batch) load_batch(sh, a.topk_idx, t0, t1, c, buf);
+    for (int i = tid; i < NW * (R + E) + R + E; i += NT) lds[i] = 0;
     __syncthreads();
-    const bool bad = wave_count(sh, a.topk_idx, t0, t1, cnt_d + w * R, cnt_e + w * E, true, c, buf, true);
+    const bool bad = wave_count(sh, a.topk_idx, t0, t1, cnt_d + w * R, cnt_e + w * E, true, c, buf, one_batch);
     if (lane_id() == 0) flag[w] = bad ? 1 : 0;
     __syncthreads();
-    for (int d = tid; d < R; d += kLayoutThreads) {
+    for (int d = tid; d < R; d += NT) {
         int tot = 0;
-        for (int q = 0; q < kLayoutWaves; ++q) tot += cnt_d[q * R + d];
+        for (int q = 0; q < NW; ++q) tot += cnt_d[q * R + d];
         a.tokens_per_rank[d] = tot;
         a.recv_psum[2 * d] = 0;
         a.recv_psum[2 * d + 1] = tot;
         part[d] = tot;
     }
-    for (int e = tid; e < E; e += kLayoutThreads) {
+    for (int e = tid; e < E; e += NT) {
         int tot = 0;
-        for (int q = 0; q < kLayoutWaves; ++q) tot += cnt_e[q * E + e];
+        for (int q = 0; q < NW; ++q) tot += cnt_e[q * E + e];
         a.tokens_per_expert[e] = tot;
         seg[e] = (tot + sh.A - 1) / sh.A * sh.A;
     }
@@ -590,25 +607,24 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_single(LayoutArgs a) 
             run += part[d];
         }
         a.recv_base[R] = run;
-        a.error_flags[0] = (flag[0] | flag[1] | flag[2] | flag[3]) ? 1 : 0;
+        int any = 0;
+        for (int q = 0; q < NW; ++q) any |= flag[q];
+        a.error_flags[0] = any ? 1 : 0;
     }
     __syncthreads();
     if (expand) {
-        const int total = block_exclusive_scan<kLayoutThreads>(seg, E, part);
-        for (int e = tid; e < E; e += kLayoutThreads) a.expert_base[e] = seg[e];
+        const int total = block_exclusive_scan<NT>(seg, E, part);
+        for (int e = tid; e < E; e += NT) a.expert_base[e] = seg[e];
         if (tid == 0) a.expert_base[E] = total;
     }
-    wave_bases(cnt_d, R, zero_d);
-    if (expand) wave_bases(cnt_e, E, seg);
+    wave_bases<NW>(cnt_d, R, zero_d);
+    if (expand) wave_bases<NW>(cnt_e, E, seg);
     __syncthreads();
-    rank_range(a, 0, t0, t1, c, buf, true, cnt_d + w * R, cnt_e + w * E);
+    rank_range(a, 0, t0, t1, c, buf, one_batch, cnt_d + w * R, cnt_e + w * E);
 }
 
 size_t count_lds_bytes(const Shape &sh) {
     return sizeof(int) * ((size_t)kLayoutWaves * (sh.R + sh.E) + kLayoutWaves);
-}
-size_t single_lds_bytes(const Shape &sh) {
-    return sizeof(int) * ((size_t)kLayoutWaves * (sh.R + sh.E) + sh.R + sh.E + kLayoutThreads + kLayoutWaves);
 }
 size_t slot_lds_bytes(const Shape &sh) {
     return sizeof(int) * ((size_t)kLayoutWaves * (sh.R + sh.E) + sh.R + sh.E + (sh.R + sh.E) + kLayoutThreads);
@@ -617,8 +633,12 @@ size_t slot_lds_bytes(const Shape &sh) {
 }  // namespace
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
-    if (a.g.single) {
-        hipLaunchKernelGGL(k_layout_single, dim3(1), dim3(kLayoutThreads), single_lds_bytes(a.sh), stream, a);
+    if (a.g.single == 8) {
+        hipLaunchKernelGGL(k_layout_single<8>, dim3(1), dim3(8 * kWave), single_lds_bytes(a.sh, 8), stream, a);
+        return hipGetLastError();
+    }
+    if (a.g.single == 16) {
+        hipLaunchKernelGGL(k_layout_single<16>, dim3(1), dim3(16 * kWave), single_lds_bytes(a.sh, 16), stream, a);
         return hipGetLastError();
     }
     const dim3 grid(a.g.blocks_per_src, a.sh.S);

@@ -238,17 +238,23 @@ def test_error_flag_for_out_of_range_ids():
     assert int(L.error_flags.item()) == 0
 
 
-SINGLE_EXPAND = Workload("single_expand", S=1, T=200, H=64, K=4, E=32, R=8, Nmax=200, expand=True, alignment=4)
+SINGLE = {  # one-launch layout at num_layout_cus = 0 (8 waves up to 1024 lanes, 16 above)
+    "single8_expand": Workload("single8_expand", S=1, T=200, H=64, K=4, E=32, R=8, Nmax=200, expand=True,
+                               alignment=4),
+    "single16": Workload("single16", S=1, T=400, H=64, K=8, E=64, R=16, Nmax=400),
+    "single16_expand": Workload("single16_expand", S=1, T=400, H=64, K=8, E=64, R=16, Nmax=400, expand=True,
+                                alignment=3),
+}
 
 
-@pytest.mark.parametrize("cfg_id", [1, 2, 4, 5, "single_expand"])
+@pytest.mark.parametrize("cfg_id", [1, 2, 4, 5] + list(SINGLE))
 def test_layout_independent_of_workgroup_count(cfg_id):
     """Slots are a pure function of topk_idx: the number of layout workgroups
     (the pages' num_prologue_sms) changes nothing.  Workload 1 and the small
-    expand case take the one-launch layout at num_layout_cus = 0 and the
-    two-pass one otherwise."""
-    w = SINGLE_EXPAND if cfg_id == "single_expand" else WORKLOADS[cfg_id]
-    inputs = generate(w, seed_for(cfg_id) if cfg_id != "single_expand" else 61, with_x=False, masked_frac=0.1,
+    single-source cases take the one-launch layout at num_layout_cus = 0 and
+    the two-pass one otherwise."""
+    w = SINGLE[cfg_id] if cfg_id in SINGLE else WORKLOADS[cfg_id]
+    inputs = generate(w, seed_for(cfg_id) if cfg_id not in SINGLE else 61, with_x=False, masked_frac=0.1,
                       invalid_frac=0.02, dup_frac=0.2)
     inputs["x"] = np.zeros((w.S, w.T, 16), np.uint8)
     dev = upload(w, inputs)
@@ -261,6 +267,12 @@ def test_layout_independent_of_workgroup_count(cfg_id):
             ref = tabs
         else:
             compare_tables(tabs, ref)
+
+
+@pytest.mark.parametrize("name", list(SINGLE))
+def test_one_launch_layout_parity(name):
+    """The one-launch layout (8 and 16 waves) against the oracle, with edge lanes."""
+    _full_case(SINGLE[name], 62, EDGE)
 
 
 def test_dispatch_is_bitwise_reproducible():
