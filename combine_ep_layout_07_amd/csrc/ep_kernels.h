@@ -34,7 +34,7 @@ __host__ __device__ inline int64_t staging_region(const Shape &sh, int d, int s)
 }
 
 // Layout pass geometry: B workgroups per source, each owning `chunk` tokens
-// (split into 4 equal wave ranges of chunk/4 tokens).
+// (split into equal wave ranges, one per wave of the workgroup).
 struct LayoutGeom {
     int blocks_per_src;
     int chunk;

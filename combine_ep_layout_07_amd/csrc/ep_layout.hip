@@ -37,6 +37,8 @@
 
 namespace ep {
 
+// Layout workgroups of 4 waves: measured on MI355X against 8 and 16 waves
+// with 32-128 units, which were 10-60% slower at T=4096 and 16 x 2048.
 constexpr int kLayoutThreads = 256;
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kBatch = 8;  // steps whose items a wave loads together
@@ -59,14 +61,15 @@ LayoutGeom layout_geometry(const Shape &sh, int num_layout_cus) {
     // idle, more units lengthen the gathers of the unit counts.
     const int tps = kWave / sh.K;              // tokens per step
     const int min_chunk = kLayoutWaves * tps;  // one step per wave
-    const int max_b = T > 4 ? (T + 3) / 4 : 1;     // at least one token per wave
+    const int max_b = T > kLayoutWaves ? (T + kLayoutWaves - 1) / kLayoutWaves : 1;  // >= one token per wave
     g.single = 0;
-    // One source with at most 4096 (token, lane) items: the whole layout in one
-    // workgroup, 8 waves up to 1024 items, 16 above.  Measured on MI355X (K=8):
-    // 4.5 / 5.9 / 7.7 / 11.5 us at T = 64 / 128 / 256 / 512 against about 13 us
-    // for the two launches, which win again from T = 1024.
+    // One source with at most 2048 (token, lane) items: the whole layout in one
+    // workgroup, 8 waves up to 1024 items, 16 above.  Measured on MI355X at
+    // K=8: 4.6 / 5.9 / 7.8 us at T = 64 / 128 / 256 against 8.4-8.8 us for the
+    // two launches (expand: 6.3 / 8.0 / 10.8 against 13.7-14.3 us); from 4096
+    // items the two launches are faster.
     const int64_t lanes = (int64_t)T * sh.K;
-    if (num_layout_cus == 0 && sh.S == 1 && lanes <= 4096) {
+    if (num_layout_cus == 0 && sh.S == 1 && lanes <= 2048) {
         const int nw = lanes <= 1024 ? 8 : 16;
         if (single_lds_bytes(sh, nw) <= 65536) {
             g.blocks_per_src = 1;
@@ -86,8 +89,8 @@ LayoutGeom layout_geometry(const Shape &sh, int num_layout_cus) {
     }
     if (B > max_b) B = max_b;
     if (B < 1) B = 1;
-    int chunk = T > 0 ? (T + B - 1) / B : 4;
-    chunk = (chunk + 3) / 4 * 4;
+    int chunk = T > 0 ? (T + B - 1) / B : kLayoutWaves;
+    chunk = (chunk + kLayoutWaves - 1) / kLayoutWaves * kLayoutWaves;  // equal wave ranges
     B = T > 0 ? (T + chunk - 1) / chunk : 1;
     g.blocks_per_src = B;
     g.chunk = chunk;
@@ -274,7 +277,7 @@ __device__ __forceinline__ void wave_bases(int *cnt, int n, const int *base) {
 // (row_base * Nmax + running count, [DET] Approach) and, in the expand layout,
 // its row; run_d / run_e are the wave's running counters in LDS.  When the
 // range fits one batch, the ids are already in `buf`.
-__device__ void rank_range(const LayoutArgs &a, int s, int t0, int t1, const StepCtx &c,
+__device__ __forceinline__ void rank_range(const LayoutArgs &a, int s, int t0, int t1, const StepCtx &c,
                            const int64_t (&buf)[kBatch], bool single, int *run_d, int *run_e) {
     const Shape &sh = a.sh;
     const bool expand = sh.expand != 0;
@@ -315,9 +318,9 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_count(LayoutArgs a) {
     const int b = blockIdx.x, s = blockIdx.y, B = a.g.blocks_per_src;
     const int w = threadIdx.x / kWave, tid = threadIdx.x;
     extern __shared__ int lds[];
-    int *cnt_d = lds;                          // [4][R]
-    int *cnt_e = cnt_d + kLayoutWaves * sh.R;  // [4][E]
-    int *flag = cnt_e + kLayoutWaves * sh.E;   // [4]
+    int *cnt_d = lds;                          // [waves][R]
+    int *cnt_e = cnt_d + kLayoutWaves * sh.R;  // [waves][E]
+    int *flag = cnt_e + kLayoutWaves * sh.E;   // [waves]
 
     int t0, t1;
     wave_range(a, b, w, t0, t1);
@@ -344,7 +347,11 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_count(LayoutArgs a) {
         for (int q = 0; q < kLayoutWaves; ++q) v += cnt_e[q * sh.E + e];
         a.blk_cnt_expert[u * sh.E + e] = v;
     }
-    if (tid == 0) a.blk_flags[u] = flag[0] | flag[1] | flag[2] | flag[3];
+    if (tid == 0) {
+        int any = 0;
+        for (int q = 0; q < kLayoutWaves; ++q) any |= flag[q];
+        a.blk_flags[u] = any;
+    }
 }
 
 // Expand layout only.  Workgroup x covers experts [64x, 64x + 64); thread
@@ -474,7 +481,9 @@ __device__ void build_receiver_tables(const LayoutArgs &a, int *lds) {
             run += tot_d[d];
         }
         a.recv_base[R] = run;
-        a.error_flags[0] = (part[64] | part[65] | part[66] | part[67]) ? 1 : 0;
+        int any = 0;
+        for (int q = 0; q < kLayoutWaves; ++q) any |= part[64 + q];
+        a.error_flags[0] = any ? 1 : 0;
     }
 }
 
@@ -491,8 +500,8 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
         if (s == 0) build_receiver_tables(a, lds);
         return;
     }
-    int *cnt_d = lds;                       // [4][R] per-wave counts, then running bases
-    int *cnt_e = cnt_d + kLayoutWaves * R;  // [4][E]
+    int *cnt_d = lds;                       // [waves][R] per-wave counts, then running bases
+    int *cnt_e = cnt_d + kLayoutWaves * R;  // [waves][E]
     int *base_d = cnt_e + kLayoutWaves * E; // [R]   this unit's base per destination
     int *base_e = base_d + R;               // [E]   expand: this unit's first row per expert
     int *col = base_e + E;                  // [R+E] per-source totals of this unit's share of columns
@@ -552,7 +561,43 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
     wave_bases(cnt_d, R, base_d);
     if (expand) wave_bases(cnt_e, E, base_e);
     __syncthreads();
-    rank_range(a, s, t0, t1, c, buf, single, cnt_d + w * R, cnt_e + w * E);
+
+    // Ranking: every item of the wave's range gets its slot / expand row.
+    // (Written out here rather than through rank_range: inlined into this
+    // kernel the helper makes the compiler spill the id batches to scratch.)
+    {
+        int *run_d = cnt_d + w * R;
+        int *run_e = cnt_e + w * E;
+        const int32_t slot_base = row_base(sh, s) * sh.Nmax;  // row_base * Nmax ([DET] Approach)
+        auto rank = [&](const Item &it) {
+            const int rd = it.owner ? run_d[it.d] : 0;
+            const int re = (expand && it.valid) ? run_e[it.e] : 0;
+            if (it.in) {
+                const int64_t idx = ((int64_t)s * sh.T + it.t) * sh.K + it.k;
+                a.dst_slot[idx] = it.owner ? slot_base + rd + it.rank_d : -1;
+                if (expand) a.expand_pos[idx] = it.valid ? re + it.rank_e : -1;
+            }
+            if (it.last_d) run_d[it.d] = rd + it.rank_d + 1;
+            if (expand && it.last_e) run_e[it.e] = re + it.rank_e + 1;
+        };
+        if (single) {
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const int ts = t0 + i * c.tps;
+                if (ts < t1) rank(make_item(sh, buf[i], ts, t1, c, expand));
+            }
+        } else {
+            for (int tb = t0; tb < t1; tb += kBatch * c.tps) {
+                int64_t b2[kBatch];
+                load_batch(sh, topk_src, tb, t1, c, b2);
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) {
+                    const int ts = tb + i * c.tps;
+                    if (ts < t1) rank(make_item(sh, b2[i], ts, t1, c, expand));
+                }
+            }
+        }
+    }
 }
 
 // The whole layout in one workgroup of NW waves, for one small source: the

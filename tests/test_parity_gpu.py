@@ -238,11 +238,11 @@ def test_error_flag_for_out_of_range_ids():
     assert int(L.error_flags.item()) == 0
 
 
-SINGLE = {  # one-launch layout at num_layout_cus = 0 (8 waves up to 1024 lanes, 16 above)
+SINGLE = {  # one-launch layout at num_layout_cus = 0 (8 waves up to 1024 items, 16 up to 2048)
     "single8_expand": Workload("single8_expand", S=1, T=200, H=64, K=4, E=32, R=8, Nmax=200, expand=True,
                                alignment=4),
-    "single16": Workload("single16", S=1, T=400, H=64, K=8, E=64, R=16, Nmax=400),
-    "single16_expand": Workload("single16_expand", S=1, T=400, H=64, K=8, E=64, R=16, Nmax=400, expand=True,
+    "single16": Workload("single16", S=1, T=250, H=64, K=8, E=64, R=16, Nmax=250),
+    "single16_expand": Workload("single16_expand", S=1, T=250, H=64, K=8, E=64, R=16, Nmax=250, expand=True,
                                 alignment=3),
 }
 
