@@ -9,12 +9,23 @@
 // compact recv_x plus the metadata and top-k tensors.
 //
 // Here all source and destination ranks are partitions of one GPU's HBM, so a
-// send is a local store.  Both kernels are pure HBM streams: one wavefront per
-// row, each lane moving 16-byte chunks c = lane + 64*i, the whole row (or a
-// CPL-chunk slice of it) loaded into VGPRs before any store, so every lane has
-// CPL independent 16-byte loads in flight.  On the hybrid path the same
-// kernels address a destination's staging rows in row form (segment = the
-// source's scale-up index, then its scale-out index), through staging_region.
+// send is a local store.  The kernels are HBM streams of 16-byte chunks: a
+// wavefront moves one row at a time, lane l taking chunks c = l + 64*i, the
+// whole row (or a CPL-chunk slice of it) loaded into VGPRs before any store, so
+// every lane has CPL independent 16-byte loads in flight.
+//   k_scatter        one wave per token, its row stored to every owner's
+//                    staging row (plus scales and the metadata record);
+//   k_scatter_pf     Direct Recv X: rows straight to the receive rows, each
+//                    wave pipelining several tokens (next row loaded before
+//                    the current stores);
+//   k_epilogue_pf    compact epilogue, pipelined the same way over receive
+//                    rows (k_epilogue for rows wider than one pass);
+//   k_epilogue_meta  Direct Recv X: scales and metadata only, one thread per
+//                    (row, item);
+//   k_epilogue_expand, k_expand_padding   the per-expert layout.
+// On the hybrid path the same kernels address a destination's staging rows in
+// row form (segment = the source's scale-up index, then its scale-out index),
+// through staging_region.
 #include "ep_device.h"
 #include "ep_kernels.h"
 
@@ -111,9 +122,9 @@ __device__ __forceinline__ void store_records(const DispatchArgs &a, int64_t g, 
 
 // One wave per token (s, t): load the row once, store it to row
 // j = slot - row_base(s)*Nmax of source s's region in the staging rows of
-// every owner lane's destination d (or, with Direct Recv X, to the compact
-// receive row recv_base[d] + recv_psum[d][s] + j), with the fp8 scales and the
-// metadata record {t, expert ids, weight bits}.
+// every owner lane's destination d (with Direct Recv X, used here only for
+// rows wider than one pass, to the compact receive row recv_base[d] +
+// recv_psum[d][s] + j), with the fp8 scales and the metadata record.
 template <int CPL>
 __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
     const Shape &sh = a.sh;
