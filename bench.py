@@ -488,7 +488,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: S={w.S} T={w.T} H={w.H} {w.dtype} K={w.K} E={w.E} R={w.R} "
                                f"Nmax={w.Nmax} {'expand' if w.expand else 'compact'} layout, {w.routing} routing",
-                   "global_batch": w.S * w.T, "seq_len": None, "parallelism": "ep16 emulated on 1 GPU"},
+                   "source_partitions": w.S, "tokens_per_source": w.T, "hidden": w.H, "top_k": w.K,
+                   "experts": w.E, "destination_ranks": w.R, "num_max_tokens_per_rank": w.Nmax,
+                   "layout": "expand" if w.expand else "compact",
+                   "emulation": f"{w.S} source and {w.R} destination ranks as partitions of one GPU's HBM"},
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
         "tokens_per_s": round(w.S * w.T / (ms * 1e-3), 1),
         "alg_bytes_per_step": b,
