@@ -43,6 +43,11 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #define EP_COMBINE_SLICES 0
 #endif
 constexpr int kRowsPerGroup = EP_COMBINE_ROWS;
+// One wave per work unit, no grid-stride cap (measured at 16 x 2048 tokens:
+// 771 us capped at 16384 workgroups, 756 us uncapped).
+#ifndef EP_COMBINE_MAX_BLOCKS
+#define EP_COMBINE_MAX_BLOCKS (1 << 20)
+#endif
 
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) {
@@ -215,7 +220,7 @@ template <int CPL>
 hipError_t run(const CombineArgs &a, hipStream_t st) {
     const int64_t units = (int64_t)a.sh.S * a.sh.T * a.slices;
     int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (blocks > 16384) blocks = 16384;
+    if (blocks > EP_COMBINE_MAX_BLOCKS) blocks = EP_COMBINE_MAX_BLOCKS;
     hipLaunchKernelGGL(k_combine<CPL>, dim3((int)blocks), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }

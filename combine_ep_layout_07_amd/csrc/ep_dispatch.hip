@@ -70,14 +70,24 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #ifndef EP_EPILOGUE_BLOCKS
 #define EP_EPILOGUE_BLOCKS 2048
 #endif
+// The staging scatter runs one wave per token with no grid-stride cap
+// (measured at 16 x 2048 tokens: 708 us capped at 2048 workgroups, 674 us
+// uncapped; the same at 4096 tokens, which never reaches the cap).
 #ifndef EP_SCATTER_BLOCKS
-#define EP_SCATTER_BLOCKS 2048
+#define EP_SCATTER_BLOCKS (1 << 20)
 #endif
 #ifndef EP_DIRECT_INFLIGHT_BYTES
 #define EP_DIRECT_INFLIGHT_BYTES 7340032
 #endif
 #ifndef EP_COPY_BLOCKS
 #define EP_COPY_BLOCKS 2048
+#endif
+// The expand epilogue runs one wave per staging row with no grid-stride cap:
+// its per-row chain (locate, record, the lanes' expand rows) needs many waves
+// in flight.  Measured on MI355X at 16 x 2048 tokens: 2048 / 16384 / 65536
+// workgroups 1349 / 1327 / 1280 us.
+#ifndef EP_EXPAND_BLOCKS
+#define EP_EXPAND_BLOCKS (1 << 20)
 #endif
 
 template <bool NT>
@@ -651,8 +661,8 @@ struct EpilogueL {
         const int64_t rows = a.sh.expand ? (int64_t)a.sh.S * a.sh.T * (a.sh.K < a.sh.R ? a.sh.K : a.sh.R)
                                          : a.recv_capacity_rows;
         if (a.sh.expand)
-            hipLaunchKernelGGL(k_epilogue_expand<CPL>, dim3(grid_for(rows)), dim3(kThreads), fits ? tab : 0, st, a,
-                               (int)fits);
+            hipLaunchKernelGGL(k_epilogue_expand<CPL>, dim3(grid_for(rows, EP_EXPAND_BLOCKS)), dim3(kThreads),
+                               fits ? tab : 0, st, a, (int)fits);
         else if (a.slices == 1 && a.sh.row_bytes / 16 <= CPL * kWave)
             hipLaunchKernelGGL(k_epilogue_pf<CPL>, dim3(grid_for(rows, EP_EPILOGUE_BLOCKS)), dim3(kThreads),
                                fits ? tab : 0, st, a, (int)fits);
