@@ -55,6 +55,7 @@ int make_shape(const ep_config_t *c, ep::Shape *sh) {
     sh->E = c->num_experts;
     sh->R = c->num_ranks;
     sh->El = c->num_experts / c->num_ranks;
+    sh->el_mul = (1u << 22) / (uint32_t)sh->El + 1u;
     sh->Nmax = c->num_max_tokens_per_rank;
     sh->expand = c->expand;
     sh->A = c->expert_alignment;

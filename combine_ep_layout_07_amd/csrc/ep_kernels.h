@@ -19,6 +19,7 @@ struct Shape {
     int bits_R, bits_E;  // key widths for ballot matching of ranks / experts
     int direct;          // Direct Recv X: hidden rows go straight to recv_x
     int n_out, n_up;     // hybrid row form when n_out > 1: rank s = (s / n_up, s % n_up)
+    uint32_t el_mul;     // floor(2^22 / El) + 1: e / El == (e * el_mul) >> 22 for 0 <= e < 1024
 };
 
 // Row base of source s: the source itself on the direct path, its scale-out

@@ -134,16 +134,24 @@ __device__ __forceinline__ StepCtx make_ctx(int K) {
     return c;
 }
 
-// Load the expert ids of `n` consecutive steps starting at token ts (ids of
-// lanes without an item are returned as -1; n <= kBatch).
+// Expert ids of kBatch consecutive steps from token ts (-1 for lanes without
+// an item).  They stay raw until make_item, so that nothing waits on the
+// loads before the wave has issued the rest of its loads.
 __device__ __forceinline__ void load_batch(const Shape &sh, const int64_t *topk_src, int ts, int t_end,
-                                           const StepCtx &c, int64_t (&buf)[kBatch]) {
+                                           const StepCtx &c, int64_t (&ids)[kBatch]) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
         const int t = ts + i * c.tps + c.l_tok;
-        buf[i] = (c.used && t < t_end) ? topk_src[(int64_t)t * sh.K + c.l_k] : (int64_t)-1;
+        ids[i] = (c.used && t < t_end) ? topk_src[(int64_t)t * sh.K + c.l_k] : (int64_t)-1;
     }
 }
+
+// Destination rank of expert e, e / El, as a multiply and a shift: with
+// m = floor(2^22 / El) + 1, e * m / 2^22 exceeds e / El by less than
+// e / 2^22 < 2^-12, while the fraction of e / El is at most 1 - 1/El <=
+// 1 - 2^-10, so the floor is exact for all 0 <= e < 1024 and El <= 1024, and
+// e * m < 2^32.
+__device__ __forceinline__ int rank_of(const Shape &sh, int e) { return (int)(((uint32_t)e * sh.el_mul) >> 22); }
 
 __device__ __forceinline__ Item make_item(const Shape &sh, int64_t e64, int t_step, int t_end, const StepCtx &c,
                                           bool need_e) {
@@ -154,7 +162,7 @@ __device__ __forceinline__ Item make_item(const Shape &sh, int64_t e64, int t_st
     it.invalid = it.in && e64 >= sh.E;
     it.valid = it.in && e64 >= 0 && e64 < sh.E;
     it.e = it.valid ? (int)e64 : 0;
-    it.d = it.valid ? it.e / sh.El : 0;
+    it.d = rank_of(sh, it.e);
     const uint64_t vmask = ballot(it.valid);
     const uint64_t peers_d = match_key((uint32_t)it.d, sh.bits_R, vmask);
     it.owner = it.valid && ((peers_d & c.seg & mask_lt(c.lane)) == 0);
@@ -174,6 +182,32 @@ __device__ __forceinline__ Item make_item(const Shape &sh, int64_t e64, int t_st
     return it;
 }
 
+// f(item) for every step of tokens [t0, t1) of one source, in token order.
+// The ids come in batches of kBatch steps (one memory latency per batch);
+// when `have_first` the first batch is already in `first`.  The step loop
+// stays rolled: each layout workgroup runs once on its CU, cold in the
+// instruction cache, so every inlined copy of the step costs fetch latency.
+template <typename F>
+__device__ __forceinline__ void walk_steps(const Shape &sh, const int64_t *topk_src, int t0, int t1,
+                                           const StepCtx &c, const int64_t (&first)[kBatch], bool have_first,
+                                           bool need_e, F &&f) {
+    for (int tb = t0; tb < t1; tb += kBatch * c.tps) {
+        int64_t ids[kBatch];
+        if (have_first && tb == t0) {
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) ids[i] = first[i];
+        } else {
+            load_batch(sh, topk_src, tb, t1, c, ids);
+        }
+#pragma unroll 1
+        for (int i = 0, ts = tb; i < kBatch && ts < t1; ++i, ts += c.tps) {
+            f(make_item(sh, ids[0], ts, t1, c, need_e));
+#pragma unroll
+            for (int j = 0; j + 1 < kBatch; ++j) ids[j] = ids[j + 1];
+        }
+    }
+}
+
 __device__ __forceinline__ void count_item(const Item &it, int *cnt_d, int *cnt_e, bool need_e, bool &bad) {
     if (it.last_d) cnt_d[it.d] += it.cnt_d;
     if (need_e && it.last_e) cnt_e[it.e] += it.cnt_e;
@@ -182,27 +216,12 @@ __device__ __forceinline__ void count_item(const Item &it, int *cnt_d, int *cnt_
 
 // Count owner lanes per destination (and valid lanes per expert) over tokens
 // [t0, t1) of one source into this wave's LDS rows; returns the invalid flag.
-// When the range fits one batch, the ids stay in `buf` for the ranking pass.
-__device__ bool wave_count(const Shape &sh, const int64_t *topk_src, int t0, int t1, int *cnt_d, int *cnt_e,
-                           bool need_e, const StepCtx &c, int64_t (&buf)[kBatch], bool single) {
+__device__ __forceinline__ bool wave_count(const Shape &sh, const int64_t *topk_src, int t0, int t1, int *cnt_d,
+                                           int *cnt_e, bool need_e, const StepCtx &c, const int64_t (&first)[kBatch],
+                                           bool have_first) {
     bool bad = false;
-    if (single) {
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            const int ts = t0 + i * c.tps;
-            if (ts < t1) count_item(make_item(sh, buf[i], ts, t1, c, need_e), cnt_d, cnt_e, need_e, bad);
-        }
-    } else {
-        for (int tb = t0; tb < t1; tb += kBatch * c.tps) {
-            int64_t b2[kBatch];
-            load_batch(sh, topk_src, tb, t1, c, b2);
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                const int ts = tb + i * c.tps;
-                if (ts < t1) count_item(make_item(sh, b2[i], ts, t1, c, need_e), cnt_d, cnt_e, need_e, bad);
-            }
-        }
-    }
+    walk_steps(sh, topk_src, t0, t1, c, first, have_first, need_e,
+               [&](const Item &it) { count_item(it, cnt_d, cnt_e, need_e, bad); });
     return ballot(bad) != 0;
 }
 
@@ -233,24 +252,71 @@ __device__ int block_exclusive_scan(int *a, int n, int *part) {
     return total;
 }
 
-// lds[col(i)] += src(i) for i in [0, n), with every thread issuing up to U
-// global loads before its first LDS add, so a reduction of up to 256*U terms
-// costs one memory latency.
-template <int U = 8, typename Src, typename Col>
-__device__ __forceinline__ void gather_add(int64_t n, int *lds, Src src, Col col) {
-    for (int64_t i0 = 0; i0 < n; i0 += (int64_t)U * kLayoutThreads) {
-        int v[U];
+// lds[j] += the sum over rows r in [0, nrows) of p_j[r * stride_j] for every
+// column j in [0, ncols), where col(j, stride_j) returns p_j.  Each thread
+// owns one column of a group of up to 256 and every (256 / group)-th row,
+// sums in a register with up to 8 loads in flight, and adds once to LDS.
+template <typename Col>
+__device__ __forceinline__ void column_sums(int nrows, int ncols, int *lds, Col col) {
+    for (int jg = 0; jg < ncols; jg += kLayoutThreads) {
+        const int nc = min(ncols - jg, kLayoutThreads);
+        const int rstep = kLayoutThreads / nc;
+        const int r0 = threadIdx.x / nc, j = jg + (threadIdx.x - r0 * nc);
+        if (r0 >= rstep) continue;
+        int64_t stride;
+        const int32_t *p = col(j, stride);
+        int sum = 0;
+        for (int r = r0; r < nrows; r += 8 * rstep) {
+            int v[8];
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int64_t i = i0 + (int64_t)k * kLayoutThreads + threadIdx.x;
-            v[k] = i < n ? src(i) : 0;
-        }
+            for (int u = 0; u < 8; ++u) {
+                const int rr = r + u * rstep;
+                v[u] = rr < nrows ? p[(int64_t)rr * stride] : 0;
+            }
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int64_t i = i0 + (int64_t)k * kLayoutThreads + threadIdx.x;
-            if (i < n && v[k] != 0) atomicAdd(&lds[col(i)], v[k]);
+            for (int u = 0; u < 8; ++u) sum += v[u];
         }
+        if (sum != 0) atomicAdd(&lds[j], sum);
     }
+}
+
+// The same column sums for at most 256 columns, split so that the loads can
+// be issued long before their sums are needed: column_issue() starts each
+// thread's first 8 rows, column_finish() adds them (and any further rows,
+// loaded then) into LDS.  Between the two the wave does other work while the
+// loads are in flight.
+struct ColumnLoads {
+    int v[8];
+    const int32_t *p;
+    int64_t stride;
+    int j, r0, rstep, nrows;
+    bool on;
+};
+
+template <typename Col>
+__device__ __forceinline__ void column_issue(ColumnLoads &cl, int nrows, int ncols, Col col) {
+    const int nc = ncols > 0 ? ncols : 1;  // ncols <= kLayoutThreads
+    cl.nrows = nrows;
+    cl.rstep = kLayoutThreads / nc;
+    cl.r0 = threadIdx.x / nc;
+    cl.j = threadIdx.x - cl.r0 * nc;
+    cl.on = ncols > 0 && cl.r0 < cl.rstep;
+    cl.stride = 0;
+    cl.p = cl.on ? col(cl.j, cl.stride) : nullptr;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int rr = cl.r0 + u * cl.rstep;
+        cl.v[u] = (cl.on && rr < nrows) ? cl.p[(int64_t)rr * cl.stride] : 0;
+    }
+}
+
+__device__ __forceinline__ void column_finish(const ColumnLoads &cl, int *lds) {
+    if (!cl.on) return;
+    int sum = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += cl.v[u];
+    for (int r = cl.r0 + 8 * cl.rstep; r < cl.nrows; r += cl.rstep) sum += cl.p[(int64_t)r * cl.stride];
+    if (sum != 0) atomicAdd(&lds[cl.j], sum);
 }
 
 __device__ __forceinline__ void wave_range(const LayoutArgs &a, int b, int w, int &t0, int &t1) {
@@ -275,14 +341,14 @@ __device__ __forceinline__ void wave_bases(int *cnt, int n, const int *base) {
 
 // Ranking: every item of the wave's tokens [t0, t1) of source s gets its slot
 // (row_base * Nmax + running count, [DET] Approach) and, in the expand layout,
-// its row; run_d / run_e are the wave's running counters in LDS.  When the
-// range fits one batch, the ids are already in `buf`.
-__device__ __forceinline__ void rank_range(const LayoutArgs &a, int s, int t0, int t1, const StepCtx &c,
-                           const int64_t (&buf)[kBatch], bool single, int *run_d, int *run_e) {
+// its row; run_d / run_e are the wave's running counters in LDS.
+__device__ __forceinline__ void rank_items(const LayoutArgs &a, int s, int t0, int t1, const StepCtx &c,
+                                           const int64_t (&first)[kBatch], bool have_first, int *run_d, int *run_e) {
     const Shape &sh = a.sh;
     const bool expand = sh.expand != 0;
     const int32_t slot_base = row_base(sh, s) * sh.Nmax;
-    auto rank = [&](const Item &it) {
+    const int64_t *topk_src = a.topk_idx + (int64_t)s * sh.T * sh.K;
+    walk_steps(sh, topk_src, t0, t1, c, first, have_first, expand, [&](const Item &it) {
         const int rd = it.owner ? run_d[it.d] : 0;
         const int re = (expand && it.valid) ? run_e[it.e] : 0;
         if (it.in) {
@@ -292,25 +358,7 @@ __device__ __forceinline__ void rank_range(const LayoutArgs &a, int s, int t0, i
         }
         if (it.last_d) run_d[it.d] = rd + it.rank_d + 1;
         if (expand && it.last_e) run_e[it.e] = re + it.rank_e + 1;
-    };
-    if (single) {
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            const int ts = t0 + i * c.tps;
-            if (ts < t1) rank(make_item(sh, buf[i], ts, t1, c, expand));
-        }
-    } else {
-        const int64_t *topk_src = a.topk_idx + (int64_t)s * sh.T * sh.K;
-        for (int tb = t0; tb < t1; tb += kBatch * c.tps) {
-            int64_t b2[kBatch];
-            load_batch(sh, topk_src, tb, t1, c, b2);
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                const int ts = tb + i * c.tps;
-                if (ts < t1) rank(make_item(sh, b2[i], ts, t1, c, expand));
-            }
-        }
-    }
+    });
 }
 
 __global__ void __launch_bounds__(kLayoutThreads) k_layout_count(LayoutArgs a) {
@@ -327,12 +375,12 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_count(LayoutArgs a) {
     const StepCtx c = make_ctx(sh.K);
     const bool single = t1 - t0 <= kBatch * c.tps;
     const int64_t *topk_src = a.topk_idx + (int64_t)s * sh.T * sh.K;
-    int64_t buf[kBatch];
-    if (single) load_batch(sh, topk_src, t0, t1, c, buf);  // in flight while LDS is cleared
+    int64_t first[kBatch] = {};
+    if (single) load_batch(sh, topk_src, t0, t1, c, first);  // in flight while LDS is cleared
     for (int i = tid; i < kLayoutWaves * (sh.R + sh.E); i += kLayoutThreads) lds[i] = 0;
     __syncthreads();
 
-    const bool bad = wave_count(sh, topk_src, t0, t1, cnt_d + w * sh.R, cnt_e + w * sh.E, true, c, buf, single);
+    const bool bad = wave_count(sh, topk_src, t0, t1, cnt_d + w * sh.R, cnt_e + w * sh.E, true, c, first, single);
     if (lane_id() == 0) flag[w] = bad ? 1 : 0;
     __syncthreads();
 
@@ -439,8 +487,10 @@ __device__ void build_receiver_tables(const LayoutArgs &a, int *lds) {
     if (fits) {
         for (int i = tid; i < S * R; i += kLayoutThreads) tot[i] = 0;
         __syncthreads();
-        gather_add<16>(U * R, tot, [&](int64_t i) { return a.blk_cnt_rank[i]; },
-                       [&](int64_t i) { return (int)((i / R) / B * R + i % R); });
+        column_sums(B, S * R, tot, [&](int p, int64_t &stride) {  // column p = (source, destination)
+            stride = R;
+            return a.blk_cnt_rank + (int64_t)(p / R) * B * R + p % R;
+        });
         __syncthreads();
     }
     int *tot_d = part;  // [R] totals per destination (R <= 64)
@@ -511,15 +561,38 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
     const StepCtx c = make_ctx(sh.K);
     const bool single = t1 - t0 <= kBatch * c.tps;
     const int64_t *topk_src = a.topk_idx + (int64_t)s * sh.T * sh.K;
-    int64_t buf[kBatch];
-    if (single) load_batch(sh, topk_src, t0, t1, c, buf);
+    int64_t first[kBatch] = {};
+    if (single) load_batch(sh, topk_src, t0, t1, c, first);
+
+    // Every global load of the unit is issued here, before the first barrier,
+    // so that the ids, the unit base and the per-source totals cost one
+    // memory latency together.  Unit base per destination: what the earlier
+    // units of this source send there.
+    const int32_t *src_rank = a.blk_cnt_rank + (int64_t)s * B * R;
+    ColumnLoads lb, lc;
+    column_issue(lb, b, R, [&](int d, int64_t &stride) {
+        stride = R;
+        return src_rank + d;
+    });
+    // This unit's share of the per-source totals: columns b, b+B, ...
+    // (destinations first, then experts), each summed over the source's units;
+    // with more than 256 such columns (few units per source) they are summed
+    // at the end instead.
+    const int ncol = b < R + E ? (R + E - b + B - 1) / B : 0;
+    auto col_src = [&](int j, int64_t &stride) -> const int32_t * {
+        const int cidx = b + j * B;
+        if (cidx < R) {
+            stride = R;
+            return a.blk_cnt_rank + (int64_t)s * B * R + cidx;
+        }
+        stride = E;
+        return a.blk_cnt_expert + (int64_t)s * B * E + (cidx - R);
+    };
+    const bool col_early = ncol <= kLayoutThreads;
+    column_issue(lc, B, col_early ? ncol : 0, col_src);
 
     for (int i = tid; i < kLayoutWaves * (R + E) + R + E + (R + E); i += kLayoutThreads) lds[i] = 0;
     __syncthreads();
-    // Unit base per destination: what the earlier units of this source send there.
-    const int32_t *src_rank = a.blk_cnt_rank + (int64_t)s * B * R;
-    gather_add((int64_t)b * R, base_d, [&](int64_t i) { return src_rank[i]; },
-               [&](int64_t i) { return (int)(i % R); });
     if (expand) {
         // First row of this unit in expert e's segment: the segment base plus
         // what the earlier units put there.
@@ -537,66 +610,23 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
             if (e < E) base_e[e] += pre[q];
         }
     }
-    // This unit's share of the per-source totals: columns c = b, b+B, ...
-    // (destinations first, then experts), each summed over the source's units.
-    const int ncol = b < R + E ? (R + E - b + B - 1) / B : 0;
-    gather_add(
-        (int64_t)ncol * B, col,
-        [&](int64_t i) {
-            const int j = (int)(i / B), q = (int)(i - (int64_t)j * B);
-            const int cidx = b + j * B;
-            return cidx < R ? a.blk_cnt_rank[((int64_t)s * B + q) * R + cidx]
-                            : a.blk_cnt_expert[((int64_t)s * B + q) * E + (cidx - R)];
-        },
-        [&](int64_t i) { return b + (int)(i / B) * B; });
-    __syncthreads();
-    for (int cidx = b + tid * B; cidx < R + E; cidx += kLayoutThreads * B) {
-        if (cidx < R) a.tokens_per_rank[(int64_t)s * R + cidx] = col[cidx];
-        else a.tokens_per_expert[(int64_t)s * E + cidx - R] = col[cidx];
-    }
 
     // Per-wave counts of this unit, then each wave's running base.
-    wave_count(sh, topk_src, t0, t1, cnt_d + w * R, cnt_e + w * E, expand, c, buf, single);
+    wave_count(sh, topk_src, t0, t1, cnt_d + w * R, cnt_e + w * E, expand, c, first, single);
+    column_finish(lb, base_d);
     __syncthreads();
     wave_bases(cnt_d, R, base_d);
     if (expand) wave_bases(cnt_e, E, base_e);
     __syncthreads();
+    rank_items(a, s, t0, t1, c, first, single, cnt_d + w * R, cnt_e + w * E);
 
-    // Ranking: every item of the wave's range gets its slot / expand row.
-    // (Written out here rather than through rank_range: inlined into this
-    // kernel the helper makes the compiler spill the id batches to scratch.)
-    {
-        int *run_d = cnt_d + w * R;
-        int *run_e = cnt_e + w * E;
-        const int32_t slot_base = row_base(sh, s) * sh.Nmax;  // row_base * Nmax ([DET] Approach)
-        auto rank = [&](const Item &it) {
-            const int rd = it.owner ? run_d[it.d] : 0;
-            const int re = (expand && it.valid) ? run_e[it.e] : 0;
-            if (it.in) {
-                const int64_t idx = ((int64_t)s * sh.T + it.t) * sh.K + it.k;
-                a.dst_slot[idx] = it.owner ? slot_base + rd + it.rank_d : -1;
-                if (expand) a.expand_pos[idx] = it.valid ? re + it.rank_e : -1;
-            }
-            if (it.last_d) run_d[it.d] = rd + it.rank_d + 1;
-            if (expand && it.last_e) run_e[it.e] = re + it.rank_e + 1;
-        };
-        if (single) {
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                const int ts = t0 + i * c.tps;
-                if (ts < t1) rank(make_item(sh, buf[i], ts, t1, c, expand));
-            }
-        } else {
-            for (int tb = t0; tb < t1; tb += kBatch * c.tps) {
-                int64_t b2[kBatch];
-                load_batch(sh, topk_src, tb, t1, c, b2);
-#pragma unroll
-                for (int i = 0; i < kBatch; ++i) {
-                    const int ts = tb + i * c.tps;
-                    if (ts < t1) rank(make_item(sh, b2[i], ts, t1, c, expand));
-                }
-            }
-        }
+    if (col_early) column_finish(lc, col);
+    else column_sums(B, ncol, col, col_src);
+    __syncthreads();
+    for (int j = tid; j < ncol; j += kLayoutThreads) {
+        const int cidx = b + j * B;
+        if (cidx < R) a.tokens_per_rank[(int64_t)s * R + cidx] = col[j];
+        else a.tokens_per_expert[(int64_t)s * E + cidx - R] = col[j];
     }
 }
 
@@ -623,11 +653,11 @@ __global__ void __launch_bounds__(NW * kWave) k_layout_single(LayoutArgs a) {
     const int t0 = min(w * cw, sh.T), t1 = min(t0 + cw, sh.T);
     const StepCtx c = make_ctx(sh.K);
     const bool one_batch = t1 - t0 <= kBatch * c.tps;
-    int64_t buf[kBatch];
-    if (one_batch) load_batch(sh, a.topk_idx, t0, t1, c, buf);
+    int64_t first[kBatch] = {};
+    if (one_batch) load_batch(sh, a.topk_idx, t0, t1, c, first);
     for (int i = tid; i < NW * (R + E) + R + E; i += NT) lds[i] = 0;
     __syncthreads();
-    const bool bad = wave_count(sh, a.topk_idx, t0, t1, cnt_d + w * R, cnt_e + w * E, true, c, buf, one_batch);
+    const bool bad = wave_count(sh, a.topk_idx, t0, t1, cnt_d + w * R, cnt_e + w * E, true, c, first, one_batch);
     if (lane_id() == 0) flag[w] = bad ? 1 : 0;
     __syncthreads();
     for (int d = tid; d < R; d += NT) {
@@ -665,7 +695,7 @@ __global__ void __launch_bounds__(NW * kWave) k_layout_single(LayoutArgs a) {
     wave_bases<NW>(cnt_d, R, zero_d);
     if (expand) wave_bases<NW>(cnt_e, E, seg);
     __syncthreads();
-    rank_range(a, 0, t0, t1, c, buf, one_batch, cnt_d + w * R, cnt_e + w * E);
+    rank_items(a, 0, t0, t1, c, first, one_batch, cnt_d + w * R, cnt_e + w * E);
 }
 
 size_t count_lds_bytes(const Shape &sh) {
