@@ -42,6 +42,9 @@ namespace ep {
 constexpr int kLayoutThreads = 256;
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kBatch = 8;  // steps whose items a wave loads together
+#ifndef EP_LAYOUT_SINGLE_MAX_ITEMS
+#define EP_LAYOUT_SINGLE_MAX_ITEMS 2048  // largest T*K laid out by one workgroup (S == 1)
+#endif
 constexpr int kScanThreads = 1024;
 
 // LDS of the one-workgroup layout with nw waves: counts [nw][R+E], bases
@@ -65,11 +68,11 @@ LayoutGeom layout_geometry(const Shape &sh, int num_layout_cus) {
     g.single = 0;
     // One source with at most 2048 (token, lane) items: the whole layout in one
     // workgroup, 8 waves up to 1024 items, 16 above.  Measured on MI355X at
-    // K=8: 4.6 / 5.9 / 7.8 us at T = 64 / 128 / 256 against 8.4-8.8 us for the
-    // two launches (expand: 6.3 / 8.0 / 10.8 against 13.7-14.3 us); from 4096
-    // items the two launches are faster.
+    // K=8: 4.4 / 5.7 / 7.4 us at T = 64 / 128 / 256 against 8.0-8.5 us for the
+    // two launches (expand: 6.2 / 7.9 / 10.5 against 13.7-13.9 us); at 4096
+    // items the two launches are faster (8.5 against 10.7 us).
     const int64_t lanes = (int64_t)T * sh.K;
-    if (num_layout_cus == 0 && sh.S == 1 && lanes <= 2048) {
+    if (num_layout_cus == 0 && sh.S == 1 && lanes <= EP_LAYOUT_SINGLE_MAX_ITEMS) {
         const int nw = lanes <= 1024 ? 8 : 16;
         if (single_lds_bytes(sh, nw) <= 65536) {
             g.blocks_per_src = 1;
@@ -342,10 +345,10 @@ __device__ __forceinline__ void wave_bases(int *cnt, int n, const int *base) {
 // Ranking: every item of the wave's tokens [t0, t1) of source s gets its slot
 // (row_base * Nmax + running count, [DET] Approach) and, in the expand layout,
 // its row; run_d / run_e are the wave's running counters in LDS.
-__device__ __forceinline__ void rank_items(const LayoutArgs &a, int s, int t0, int t1, const StepCtx &c,
-                                           const int64_t (&first)[kBatch], bool have_first, int *run_d, int *run_e) {
+__device__ __forceinline__ void rank_items(const LayoutArgs &a, bool expand, int s, int t0, int t1,
+                                           const StepCtx &c, const int64_t (&first)[kBatch], bool have_first,
+                                           int *run_d, int *run_e) {
     const Shape &sh = a.sh;
-    const bool expand = sh.expand != 0;
     const int32_t slot_base = row_base(sh, s) * sh.Nmax;
     const int64_t *topk_src = a.topk_idx + (int64_t)s * sh.T * sh.K;
     walk_steps(sh, topk_src, t0, t1, c, first, have_first, expand, [&](const Item &it) {
@@ -467,7 +470,7 @@ __device__ int expert_segment_bases(const LayoutArgs &a, int *seg, int *part) {
 // recv_psum (and, on the hybrid path, over scale-up segments into
 // recv_psum_scaleup) and over destinations into recv_base; the units' invalid
 // flags are OR-ed into error_flags; expand also writes expert_base.
-__device__ void build_receiver_tables(const LayoutArgs &a, int *lds) {
+__device__ __forceinline__ void build_receiver_tables(const LayoutArgs &a, bool expand, int *lds) {
     const Shape &sh = a.sh;
     const int tid = threadIdx.x, w = tid / kWave;
     const int R = sh.R, E = sh.E, S = sh.S, B = a.g.blocks_per_src;
@@ -477,7 +480,7 @@ __device__ void build_receiver_tables(const LayoutArgs &a, int *lds) {
     const bool fits = (int64_t)S * R <= (int64_t)kLayoutWaves * (R + E);
     int bad = 0;
     for (int64_t q = tid; q < U; q += kLayoutThreads) bad |= a.blk_flags[q];  // in flight with the gather
-    if (sh.expand) {
+    if (expand) {
         int *eb = lds + kLayoutWaves * (R + E) + R;  // [E], unused by the rest of this workgroup
         const int total = expert_segment_bases(a, eb, part);
         for (int e = tid; e < E; e += kLayoutThreads) a.expert_base[e] = eb[e];
@@ -537,17 +540,21 @@ __device__ void build_receiver_tables(const LayoutArgs &a, int *lds) {
     }
 }
 
+// One instance per layout kind, so that the compact layout's kernel carries
+// none of the expand code (each workgroup runs once, cold in the instruction
+// cache).
+template <bool EXPAND>
 __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
     const Shape &sh = a.sh;
     const int b = blockIdx.x, s = blockIdx.y, B = a.g.blocks_per_src;
     const int w = threadIdx.x / kWave, tid = threadIdx.x;
     const int R = sh.R, E = sh.E;
-    const bool expand = sh.expand != 0;
+    constexpr bool expand = EXPAND;
     const int64_t me = (int64_t)s * B + b;
 
     extern __shared__ int lds[];
     if (b == B) {  // the extra column: workgroup (B, 0) builds the receiver tables
-        if (s == 0) build_receiver_tables(a, lds);
+        if (s == 0) build_receiver_tables(a, expand, lds);
         return;
     }
     int *cnt_d = lds;                       // [waves][R] per-wave counts, then running bases
@@ -618,7 +625,7 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
     wave_bases(cnt_d, R, base_d);
     if (expand) wave_bases(cnt_e, E, base_e);
     __syncthreads();
-    rank_items(a, s, t0, t1, c, first, single, cnt_d + w * R, cnt_e + w * E);
+    rank_items(a, expand, s, t0, t1, c, first, single, cnt_d + w * R, cnt_e + w * E);
 
     if (col_early) column_finish(lc, col);
     else column_sums(B, ncol, col, col_src);
@@ -634,13 +641,13 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
 // workgroup's own counts are the source's totals, so the receiver tables and
 // the expert segment bases need no other workgroup, and the layout takes one
 // launch instead of two.  Wave w owns tokens [w*cw, (w+1)*cw), cw = ceil(T/NW).
-template <int NW>
+template <int NW, bool EXPAND>
 __global__ void __launch_bounds__(NW * kWave) k_layout_single(LayoutArgs a) {
     constexpr int NT = NW * kWave;
     const Shape &sh = a.sh;
     const int w = threadIdx.x / kWave, tid = threadIdx.x;
     const int R = sh.R, E = sh.E;
-    const bool expand = sh.expand != 0;
+    constexpr bool expand = EXPAND;
     extern __shared__ int lds[];
     int *cnt_d = lds;               // [NW][R] per-wave counts, then running bases
     int *cnt_e = cnt_d + NW * R;    // [NW][E]
@@ -695,7 +702,7 @@ __global__ void __launch_bounds__(NW * kWave) k_layout_single(LayoutArgs a) {
     wave_bases<NW>(cnt_d, R, zero_d);
     if (expand) wave_bases<NW>(cnt_e, E, seg);
     __syncthreads();
-    rank_items(a, 0, t0, t1, c, first, one_batch, cnt_d + w * R, cnt_e + w * E);
+    rank_items(a, expand, 0, t0, t1, c, first, one_batch, cnt_d + w * R, cnt_e + w * E);
 }
 
 size_t count_lds_bytes(const Shape &sh) {
@@ -708,12 +715,17 @@ size_t slot_lds_bytes(const Shape &sh) {
 }  // namespace
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
-    if (a.g.single == 8) {
-        hipLaunchKernelGGL(k_layout_single<8>, dim3(1), dim3(8 * kWave), single_lds_bytes(a.sh, 8), stream, a);
-        return hipGetLastError();
-    }
-    if (a.g.single == 16) {
-        hipLaunchKernelGGL(k_layout_single<16>, dim3(1), dim3(16 * kWave), single_lds_bytes(a.sh, 16), stream, a);
+    if (a.g.single) {
+        const int nw = a.g.single;
+        const size_t lds = single_lds_bytes(a.sh, nw);
+        if (nw == 8 && a.sh.expand)
+            hipLaunchKernelGGL((k_layout_single<8, true>), dim3(1), dim3(8 * kWave), lds, stream, a);
+        else if (nw == 8)
+            hipLaunchKernelGGL((k_layout_single<8, false>), dim3(1), dim3(8 * kWave), lds, stream, a);
+        else if (a.sh.expand)
+            hipLaunchKernelGGL((k_layout_single<16, true>), dim3(1), dim3(16 * kWave), lds, stream, a);
+        else
+            hipLaunchKernelGGL((k_layout_single<16, false>), dim3(1), dim3(16 * kWave), lds, stream, a);
         return hipGetLastError();
     }
     const dim3 grid(a.g.blocks_per_src, a.sh.S);
@@ -728,8 +740,11 @@ hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
     }
     // One more column of workgroups: (B, 0) builds the receiver tables, the
     // rest of that column exits at once.
-    hipLaunchKernelGGL(k_layout_slot, dim3(a.g.blocks_per_src + 1, a.sh.S), dim3(kLayoutThreads),
-                       slot_lds_bytes(a.sh), stream, a);
+    const dim3 slot_grid(a.g.blocks_per_src + 1, a.sh.S);
+    if (a.sh.expand)
+        hipLaunchKernelGGL(k_layout_slot<true>, slot_grid, dim3(kLayoutThreads), slot_lds_bytes(a.sh), stream, a);
+    else
+        hipLaunchKernelGGL(k_layout_slot<false>, slot_grid, dim3(kLayoutThreads), slot_lds_bytes(a.sh), stream, a);
     return hipGetLastError();
 }
 
