@@ -62,13 +62,16 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 // Column slices of a compact receive row, each a separate work unit, and the
 // epilogue's grid cap.  Measured on MI355X at T=4096, H=7168: one whole row
 // per wave in one pass is fastest (2, 4 and 7 slices cost 2%, 9% and 19% more
-// time, two passes of half a row 3%, two rows per wave 1%); 1024 to 4096
-// workgroups are within 2% of each other.
+// time, two passes of half a row 3%, two rows per wave 1%).  The grid is not
+// capped, so each wave takes one receive row: in back-to-back steps at
+// T=4096, H=7168 bf16, 2048 / 4096 / 6144 workgroups (3.3 / 1.6 / 1.1 rows
+// per wave, pipelined) gave 296 / 291.5 / 286 us per step and one row per
+// wave 283 us; at T=8192, H=4096 239.5 -> 232.8 us; fp8 rows 1% slower.
 #ifndef EP_EPILOGUE_SLICES
 #define EP_EPILOGUE_SLICES 1
 #endif
 #ifndef EP_EPILOGUE_BLOCKS
-#define EP_EPILOGUE_BLOCKS 2048
+#define EP_EPILOGUE_BLOCKS (1 << 20)
 #endif
 // The staging scatter runs one wave per token with no grid-stride cap
 // (measured at 16 x 2048 tokens: 708 us capped at 2048 workgroups, 674 us
@@ -399,12 +402,11 @@ __global__ void __launch_bounds__(kThreads) k_epilogue(DispatchArgs a, int table
     }
 }
 
-// Software-pipelined compact epilogue, the default when a row fits one pass
-// (64 * CPL chunks): each wave takes receive rows i, i + nwaves, ... and
-// loads the next row before storing the current one, so its reads overlap its
-// writes.  Measured on MI355X with the same grid as one row per pass: the
-// epilogue 143 -> 139 us at T=4096, H=7168 (steps 1.5-3.5% faster on the
-// bf16, fp8 and H=4096 workloads).
+// Compact epilogue when a row fits one pass (64 * CPL chunks): each wave
+// takes receive rows i, i + nwaves, ... and loads the next row before storing
+// the current one, so its reads overlap its writes.  With the default grid
+// (one wave per receive row) the loop does not iterate; capped at 2048
+// workgroups it took the epilogue from 143 to 139 us at T=4096, H=7168.
 template <int CPL>
 __global__ void __launch_bounds__(kThreads) k_epilogue_pf(DispatchArgs a, int tables_in_lds) {
     const Shape &sh = a.sh;
