@@ -194,9 +194,49 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_md: str, command: str
     print("\n".join(lines))
 
 
+def is_copy_epilogue(name: str) -> bool:
+    return "k_epilogue" in name and "meta" not in name
+
+
+def epilogue_runs(trace_csv: str) -> dict:
+    """Copy-epilogue dispatches of a rocprofv3 kernel trace (kernel_trace.csv),
+    split by what ran around them: "back_to_back" = launches in a run of two or
+    more consecutive epilogue dispatches (bench.py's roofline loop),
+    "in_step" = the rest (between a scatter and a combine).  For each group:
+    count, mean duration (us) and, for the back-to-back runs, the mean time per
+    launch from the first start to the last end of each run, the interval the
+    bench's two HIP events bracket."""
+    rows = sorted(_counter_rows(trace_csv), key=lambda r: int(r["Start_Timestamp"]))
+    epi = [is_copy_epilogue(r["Kernel_Name"]) for r in rows]
+    groups = {"back_to_back": [], "in_step": []}
+    spans = []
+    i = 0
+    while i < len(rows):
+        if not epi[i]:
+            i += 1
+            continue
+        j = i
+        while j + 1 < len(rows) and epi[j + 1]:
+            j += 1
+        run = rows[i:j + 1]
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in run]
+        if len(run) >= 2:
+            groups["back_to_back"] += durs
+            spans.append(((int(run[-1]["End_Timestamp"]) - int(run[0]["Start_Timestamp"])) / 1e3, len(run)))
+        else:
+            groups["in_step"] += durs
+        i = j + 1
+    out = {k: {"n": len(v), "avg_us": (sum(v) / len(v)) if v else None} for k, v in groups.items()}
+    n_span = sum(n for _, n in spans)
+    out["back_to_back"]["span_us_per_launch"] = (sum(s for s, _ in spans) / n_span) if n_span else None
+    return out
+
+
 def summarize_trace(stats_csv: str, bench_json: str, out_md: str, command: str) -> None:
     """Turn a rocprofv3 --kernel-trace --stats summary (kernel_stats.csv) and the
-    JSON line bench.py printed in the same run into a short markdown summary."""
+    JSON line bench.py printed in the same run into a short markdown summary;
+    with the run's kernel_trace.csv beside the stats file, the copy epilogue's
+    back-to-back launches (the roofline's) are also summarised on their own."""
     rows = [r for r in _counter_rows(stats_csv) if "ep::" in r["Name"]]
     with open(bench_json) as f:
         b = json.loads(f.read().strip().splitlines()[-1])
@@ -210,13 +250,27 @@ def summarize_trace(stats_csv: str, bench_json: str, out_md: str, command: str) 
     lines += ["", f"bench.py line of the same (profiled) run: value {b['value']} GB/s, ms_per_step {b['ms_per_step']}, "
                   f"stage_us {b['stage_us']}, epilogue achieved {b['roofline']['achieved']} GB/s "
                   f"({b['roofline'].get('timing', 'HIP events')})."]
-    epi = [r for r in rows if "k_epilogue" in r["Name"] and "meta" not in r["Name"]]
+    epi = [r for r in rows if is_copy_epilogue(r["Name"])]
     if epi:
         avg = float(epi[0]["AverageNs"]) / 1e3
         alg = b["roofline"]["alg_bytes_per_launch"]
         lines.append(f"The same algorithmic bytes ({alg} B per launch) over the rocprofv3 average duration of the "
                      f"copy epilogue ({avg:.2f} us): {alg / avg / 1e3:.1f} GB/s = "
                      f"{alg / avg / 1e3 / PEAK_HBM_GBPS * 100:.1f}% of 8 TB/s.")
+    trace_csv = stats_csv.replace("kernel_stats.csv", "kernel_trace.csv")
+    if epi and trace_csv != stats_csv and os.path.exists(trace_csv):
+        g = epilogue_runs(trace_csv)
+        bb, ins = g["back_to_back"], g["in_step"]
+        ev = b["stage_us"].get("epilogue_back_to_back")
+        lines += ["", "Copy-epilogue dispatches of the same run by what ran around them (kernel_trace.csv):", "",
+                  "| launches | count | rocprofv3 mean duration us | rocprofv3 first start to last end, per launch us "
+                  "| bench.py HIP events us |", "|---|---|---|---|---|"]
+        if bb["n"]:
+            lines.append(f"| back to back (roofline loop) | {bb['n']} | {bb['avg_us']:.2f} | "
+                         f"{bb['span_us_per_launch']:.2f} | {ev} |")
+        if ins["n"]:
+            lines.append(f"| inside steps (after the scatter) | {ins['n']} | {ins['avg_us']:.2f} | — | "
+                         f"{b['stage_us'].get('epilogue')} (event pair around the launch) |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))

@@ -101,3 +101,23 @@ def test_algorithmic_bytes_padding_and_bias_terms():
     b2 = bench.alg_bytes(WORKLOADS[2], 26719, 32768, n_bias=2)
     b0 = bench.alg_bytes(WORKLOADS[2], 26719, 32768)
     assert b2["combine"] - b0["combine"] == 2 * 4096 * 7168 * 2
+
+
+def test_epilogue_runs_split_back_to_back_from_in_step(tmp_path):
+    p = tmp_path / "kt_kernel_trace.csv"
+    epi, sc, cb = ("void ep::k_epilogue_pf<14>(ep::DispatchArgs, int)", "void ep::k_scatter<14>(ep::DispatchArgs)",
+                   "void ep::k_combine<2>(ep::CombineArgs)")
+    # two steps (scatter, epilogue 120 us, combine), then three epilogues back to
+    # back of 130 us each with 2 us between them; rows deliberately out of order
+    seq = [(sc, 0, 70), (epi, 71, 191), (cb, 192, 270), (sc, 300, 370), (epi, 371, 491), (cb, 492, 570),
+           (epi, 600, 730), (epi, 732, 862), (epi, 864, 994)]
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for name, a, b in reversed(seq):
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": a * 1000, "End_Timestamp": b * 1000})
+    g = bench.epilogue_runs(str(p))
+    assert g["in_step"] == {"n": 2, "avg_us": 120.0}
+    assert g["back_to_back"]["n"] == 3
+    assert g["back_to_back"]["avg_us"] == pytest.approx(130.0)
+    assert g["back_to_back"]["span_us_per_launch"] == pytest.approx(394 / 3)
