@@ -90,7 +90,7 @@ def read_traffic(per_launch_alg: float):
         return None
 
 
-def cpu_baseline(w, inputs, n_rows, v_rows, max_passes=30, budget_s=12.0):
+def cpu_baseline(w, inputs, n_rows, v_rows, max_passes=100, budget_s=12.0):
     """The oracle as it stands, single-threaded, on the same workload: whole
     passes (layout + dispatch + combine) until about budget_s of CPU time."""
     import numpy as np
@@ -114,7 +114,7 @@ def cpu_baseline(w, inputs, n_rows, v_rows, max_passes=30, budget_s=12.0):
     b = alg_bytes(w, n_rows, v_rows)["total"]
     return {"value": round(b / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"full {w.name} workload (S={w.S} T={w.T} H={w.H} K={w.K}), layout+dispatch+combine, "
-                      f"median of {len(times)} passes of {t:.2f} s, single thread",
+                      f"median of {len(times)} passes of {t:.2f} s ({sum(times):.1f} s of CPU work), single thread",
             "seconds_per_step": round(t, 3), "tokens_per_s": round(w.S * w.T / t, 1)}
 
 
