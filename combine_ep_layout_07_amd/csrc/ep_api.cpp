@@ -45,6 +45,7 @@ int make_shape(const ep_config_t *c, ep::Shape *sh) {
     if (c->num_max_tokens_per_rank < c->num_tokens) return EP_ERR_CAPACITY;
     const int64_t S = c->num_src_ranks, T = c->num_tokens, K = c->num_topk;
     if (S > 65535) return EP_ERR_UNSUPPORTED;  // sources index the layout grid's y dimension
+    if (T > EP_MAX_TOKENS) return EP_ERR_UNSUPPORTED;  // token loops step past T in 32-bit arithmetic
     if (S * c->num_max_tokens_per_rank > kInt32Max) return EP_ERR_UNSUPPORTED;
     if (S * T * K > kInt32Max) return EP_ERR_UNSUPPORTED;
     if (S * T * K + (int64_t)c->num_experts * (c->expert_alignment - 1) > kInt32Max) return EP_ERR_UNSUPPORTED;

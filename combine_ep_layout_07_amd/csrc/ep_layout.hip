@@ -58,13 +58,13 @@ constexpr int kScanRegs = 16;                        // counts a scan thread kee
 
 LayoutGeom layout_geometry(const Shape &sh, int num_layout_cus) {
     LayoutGeom g;
-    const int T = sh.T;
+    const int64_t T = sh.T;  // the arithmetic below is 64-bit; every result fits an int for T <= 2^30
     // Measured on MI355X (T=4096 and 16 x 2048 tokens, K=8): about 256 units
     // of at least one step per wave are fastest; fewer, longer units leave CUs
     // idle, more units lengthen the gathers of the unit counts.
     const int tps = kWave / sh.K;              // tokens per step
     const int min_chunk = kLayoutWaves * tps;  // one step per wave
-    const int max_b = T > kLayoutWaves ? (T + kLayoutWaves - 1) / kLayoutWaves : 1;  // >= one token per wave
+    const int64_t max_b = T > kLayoutWaves ? (T + kLayoutWaves - 1) / kLayoutWaves : 1;  // >= one token per wave
     g.single = 0;
     // One source with at most 2048 (token, lane) items: the whole layout in one
     // workgroup, 8 waves up to 1024 items, 16 above.  Measured on MI355X at
@@ -76,27 +76,27 @@ LayoutGeom layout_geometry(const Shape &sh, int num_layout_cus) {
         const int nw = lanes <= 1024 ? 8 : 16;
         if (single_lds_bytes(sh, nw) <= 65536) {
             g.blocks_per_src = 1;
-            g.chunk = T > 0 ? (T + 3) / 4 * 4 : 4;
+            g.chunk = T > 0 ? (int)((T + 3) / 4 * 4) : 4;
             g.single = nw;
             return g;
         }
     }
-    int B;
+    int64_t B;
     if (num_layout_cus > 0) {
-        B = (num_layout_cus + sh.S - 1) / sh.S;
+        B = ((int64_t)num_layout_cus + sh.S - 1) / sh.S;
     } else {
-        const int target_units = 256;
-        const int by_size = (T + min_chunk - 1) / min_chunk;
-        const int by_units = (target_units + sh.S - 1) / sh.S;
+        const int64_t target_units = 256;
+        const int64_t by_size = (T + min_chunk - 1) / min_chunk;
+        const int64_t by_units = (target_units + sh.S - 1) / sh.S;
         B = by_size < by_units ? by_size : by_units;
     }
     if (B > max_b) B = max_b;
     if (B < 1) B = 1;
-    int chunk = T > 0 ? (T + B - 1) / B : kLayoutWaves;
+    int64_t chunk = T > 0 ? (T + B - 1) / B : kLayoutWaves;
     chunk = (chunk + kLayoutWaves - 1) / kLayoutWaves * kLayoutWaves;  // equal wave ranges
     B = T > 0 ? (T + chunk - 1) / chunk : 1;
-    g.blocks_per_src = B;
-    g.chunk = chunk;
+    g.blocks_per_src = (int)B;
+    g.chunk = (int)chunk;
     return g;
 }
 

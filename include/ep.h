@@ -78,9 +78,11 @@ enum ep_flags {
 };
 
 /* Limits (checked on the host): 1 <= R <= 64, 1 <= K <= 32, E % R == 0,
- * E <= 1024, S <= 65535, H <= 262144, S * Nmax < 2^31, S * T * K < 2^31,
- * H * element size a multiple of 16 bytes, fp8 needs H % 128 == 0. */
+ * E <= 1024, S <= 65535, T <= 2^30, H <= 262144, S * Nmax < 2^31,
+ * S * T * K < 2^31, H * element size a multiple of 16 bytes, fp8 needs
+ * H % 128 == 0.  Outside them a call returns EP_ERR_UNSUPPORTED. */
 #define EP_MAX_RANKS 64
+#define EP_MAX_TOKENS (1 << 30)
 #define EP_MAX_TOPK 32
 #define EP_MAX_EXPERTS 1024
 #define EP_MAX_HIDDEN 262144

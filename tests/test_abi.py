@@ -79,6 +79,8 @@ def _rc(cfg):
     (dict(S=2, Nmax=2**30 + 1, T=4096), ep.EP_ERR_UNSUPPORTED),  # S * Nmax >= 2^31
     (dict(S=70000, Nmax=0, T=0), ep.EP_ERR_UNSUPPORTED),  # S > 65535
     (dict(H=262144 + 8), ep.EP_ERR_UNSUPPORTED),          # H > EP_MAX_HIDDEN
+    (dict(T=2**30 + 1, Nmax=2**30 + 1, K=1, E=16), ep.EP_ERR_UNSUPPORTED),  # T > EP_MAX_TOKENS
+    (dict(T=2**30, Nmax=2**30, K=1, E=16), ep.EP_OK),     # T = EP_MAX_TOKENS
 ])
 def test_validation_codes(kw, code):
     base = dict(S=1, T=4096, H=7168, K=8, E=256, R=16, Nmax=4096)
@@ -180,6 +182,9 @@ def test_layout_scratch_grows_with_num_layout_cus():
     a = ep.ep_query_sizes(ep.make_config(1, 4096, 7168, 8, 256, 16, 4096, num_layout_cus=1))
     b = ep.ep_query_sizes(ep.make_config(1, 4096, 7168, 8, 256, 16, 4096, num_layout_cus=64))
     assert 0 < a.layout_scratch < b.layout_scratch
+    # any int32 request is clamped to at least one token per wave: 4096 tokens give at most 1024 units
+    c = ep.ep_query_sizes(ep.make_config(1, 4096, 7168, 8, 256, 16, 4096, num_layout_cus=2**31 - 1))
+    assert c.layout_scratch == 1024 * (16 + 256 + 1) * 4
 
 
 def test_binding_refuses_host_tensors():
