@@ -434,8 +434,8 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_pf(DispatchArgs a, int ta
     u32x4 v[CPL];
     fetch(i, d, s, j, v);
     while (true) {
-        const int in = i + nwaves;
-        const bool more = in < n_rows;
+        const bool more = nwaves < n_rows - i;  // i + nwaves < n_rows, without forming a sum past 2^31
+        const int in = more ? i + nwaves : i;
         int dn = 0, sn = 0, jn = -1;
         u32x4 vn[CPL];
         if (more) fetch(in, dn, sn, jn, vn);
@@ -523,7 +523,8 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_expand(DispatchArgs a, in
     const int nchunks = sh.row_bytes / 16;
     const int wave0 = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
     const int nwaves = gridDim.x * kWavesPerBlock;
-    for (int i = wave0; i < n_rows; i += nwaves) {
+    for (int64_t i64 = wave0; i64 < n_rows; i64 += nwaves) {  // 64-bit: rows may approach 2^31
+        const int i = (int)i64;
         int d, s, j;
         locate_row(rbase, rpsum, sh.R, sh.S, i, lane, d, s, j);
         if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for tables of one layout
@@ -584,7 +585,7 @@ __global__ void __launch_bounds__(kThreads) k_expand_padding(DispatchArgs a) {
     const int r1 = (int)min((int64_t)a.expert_base[e + 1], a.recv_capacity_rows);
     const int nchunks = sh.row_bytes / 16;
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int r = r0 + (int)blockIdx.y; r < r1; r += (int)gridDim.y) {
+    for (int64_t r = (int64_t)r0 + blockIdx.y; r < r1; r += gridDim.y) {  // 64-bit: r1 may approach 2^31
         uint8_t *dst = a.recv_x + (int64_t)r * sh.row_bytes;
         for (int c = threadIdx.x; c < nchunks; c += kThreads) st16<false>(dst + (int64_t)c * 16, zero);
         for (int q = threadIdx.x; q < sh.sf_per_row; q += kThreads) a.recv_sf[(int64_t)r * sh.sf_per_row + q] = 0.0f;
