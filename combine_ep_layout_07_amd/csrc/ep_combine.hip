@@ -45,6 +45,14 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 constexpr int kRowsPerGroup = EP_COMBINE_ROWS;
 // One wave per work unit, no grid-stride cap (measured at 16 x 2048 tokens:
 // 771 us capped at 16384 workgroups, 756 us uncapped).
+// In the expand layout (one row per lane, 8 rows per token at top-8) the
+// launch asks for enough LDS that at most three workgroups are resident per CU
+// (3 waves per SIMD instead of the 4 the registers allow): measured on MI355X
+// at 16 x 2048 tokens, H = 7168, 754 -> 705 us (2 per SIMD: 737 us); the
+// compact layout's combine measured 3-7% slower so, and keeps all 4.
+#ifndef EP_COMBINE_EXPAND_LDS
+#define EP_COMBINE_EXPAND_LDS lds_to_cap_residency(3)
+#endif
 #ifndef EP_COMBINE_MAX_BLOCKS
 #define EP_COMBINE_MAX_BLOCKS (1 << 20)
 #endif
@@ -103,7 +111,7 @@ __device__ __forceinline__ uint64_t token_rows(const CombineArgs &a, int64_t g, 
         row = valid ? pos : -1;
         wrow = w;
     } else {
-        const int d = valid ? e / sh.El : 0;
+        const int d = valid ? rank_of(sh, e) : 0;
         const uint64_t peers = match_key((uint32_t)d, sh.bits_R, vmask);
         const int owner = peers ? __builtin_ctzll(peers) : 0;
         const bool is_owner = valid && owner == lane;
@@ -221,7 +229,8 @@ hipError_t run(const CombineArgs &a, hipStream_t st) {
     const int64_t units = (int64_t)a.sh.S * a.sh.T * a.slices;
     int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
     if (blocks > EP_COMBINE_MAX_BLOCKS) blocks = EP_COMBINE_MAX_BLOCKS;
-    hipLaunchKernelGGL(k_combine<CPL>, dim3((int)blocks), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(k_combine<CPL>, dim3((int)blocks), dim3(kThreads), a.sh.expand ? EP_COMBINE_EXPAND_LDS : 0, st,
+                       a);
     return hipGetLastError();
 }
 

@@ -52,4 +52,16 @@ __device__ __forceinline__ int bits_for(int n) {  // smallest b with (1 << b) >=
 // 16-byte vector used for all row copies.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// LDS of one CDNA4 compute unit, and the dynamic LDS a workgroup requests so
+// that at most `groups` such workgroups are resident on a CU at once (the
+// kernel never touches the extra bytes): caps the waves in flight for streams
+// that measured faster with fewer of them.  Below the 64 KiB per-workgroup
+// limit for groups >= 2.
+constexpr int kLdsPerCU = 160 * 1024;
+constexpr int lds_to_cap_residency(int groups) { return kLdsPerCU / (groups + 1) + 1024; }
+static_assert(lds_to_cap_residency(2) <= 65536 && 2 * lds_to_cap_residency(2) <= kLdsPerCU &&
+                  3 * lds_to_cap_residency(2) > kLdsPerCU, "two workgroups per CU");
+static_assert(3 * lds_to_cap_residency(3) <= kLdsPerCU && 4 * lds_to_cap_residency(3) > kLdsPerCU,
+              "three workgroups per CU");
+
 }  // namespace ep

@@ -26,6 +26,8 @@
 // On the hybrid path the same kernels address a destination's staging rows in
 // row form (segment = the source's scale-up index, then its scale-out index),
 // through staging_region.
+#include <algorithm>
+
 #include "ep_device.h"
 #include "ep_kernels.h"
 
@@ -88,7 +90,13 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 // The expand epilogue runs one wave per staging row with no grid-stride cap:
 // its per-row chain (locate, record, the lanes' expand rows) needs many waves
 // in flight.  Measured on MI355X at 16 x 2048 tokens: 2048 / 16384 / 65536
-// workgroups 1349 / 1327 / 1280 us.
+// workgroups 1349 / 1327 / 1280 us.  Its launch also asks for enough LDS that
+// at most two workgroups (2 waves per SIMD, as the compact epilogue's
+// registers allow) are resident per CU: 1284 -> 1228 us there, while 3 waves
+// per SIMD measured the same as the 4 its registers allow.
+#ifndef EP_EXPAND_LDS
+#define EP_EXPAND_LDS lds_to_cap_residency(2)
+#endif
 #ifndef EP_EXPAND_BLOCKS
 #define EP_EXPAND_BLOCKS (1 << 20)
 #endif
@@ -122,7 +130,7 @@ __device__ __forceinline__ void store_records(const DispatchArgs &a, int64_t g, 
     const int word0 = lane == 0 ? t : (lane <= sh.K ? ev : wv);
     for (uint64_t m = owners; m; m &= m - 1) {
         const int k = __builtin_ctzll(m);
-        const int d = read_lane(e, k) / sh.El;
+        const int d = rank_of(sh, read_lane(e, k));
         const int j = read_lane(slot, k) - row_base(sh, s) * sh.Nmax;
         if ((unsigned)j >= (unsigned)sh.Nmax) continue;
         const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
@@ -169,7 +177,7 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
         // dependent scalar load per owner row).
         int recv_row0 = 0;
         if (sh.direct && lane < sh.K && slot >= 0) {
-            const int d = e / sh.El;
+            const int d = rank_of(sh, e);
             recv_row0 = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s];
         }
         const uint8_t *src = a.x + g * sh.row_bytes;
@@ -182,7 +190,7 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
             }
             for (uint64_t m = owners; m; m &= m - 1) {
                 const int k = __builtin_ctzll(m);
-                const int d = read_lane(e, k) / sh.El;
+                const int d = rank_of(sh, read_lane(e, k));
                 const int j = read_lane(slot, k) - row_base(sh, s) * sh.Nmax;
                 if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for a layout of this topk_idx
                 if (sh.direct) {
@@ -220,12 +228,12 @@ __device__ __forceinline__ void scatter_token(const DispatchArgs &a, int64_t g, 
     const uint64_t owners = ballot(lane < sh.K && slot >= 0);
     int recv_row0 = 0;
     if (sh.direct && lane < sh.K && slot >= 0) {
-        const int d = e / sh.El;
+        const int d = rank_of(sh, e);
         recv_row0 = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s];
     }
     for (uint64_t m = owners; m; m &= m - 1) {
         const int k = __builtin_ctzll(m);
-        const int d = read_lane(e, k) / sh.El;
+        const int d = rank_of(sh, read_lane(e, k));
         const int j = read_lane(slot, k) - row_base(sh, s) * sh.Nmax;
         if ((unsigned)j >= (unsigned)sh.Nmax) continue;
         if (sh.direct) {
@@ -368,7 +376,7 @@ __device__ __forceinline__ void epilogue_row(const DispatchArgs &a, int d, int s
     if (lane == 0) a.recv_src_idx[i] = s * sh.T + t;
     for (int k = lane; k < sh.K; k += kWave) {
         const int e = meta[1 + k];
-        const bool on_d = e >= 0 && e / sh.El == d;
+        const bool on_d = (unsigned)e < (unsigned)sh.E && rank_of(sh, e) == d;
         a.recv_topk_idx[(int64_t)i * sh.K + k] = on_d ? e - d * sh.El : -1;
         a.recv_topk_weights[(int64_t)i * sh.K + k] = on_d ? __int_as_float(meta[1 + sh.K + k]) : 0.0f;
     }
@@ -494,7 +502,7 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_meta(DispatchArgs a, int 
         if (c < sh.K) {
             if (c == 0) a.recv_src_idx[i] = s * sh.T + meta[0];
             const int e = meta[1 + c];
-            const bool on_d = e >= 0 && e / sh.El == d;
+            const bool on_d = (unsigned)e < (unsigned)sh.E && rank_of(sh, e) == d;
             a.recv_topk_idx[(int64_t)i * sh.K + c] = on_d ? e - d * sh.El : -1;
             a.recv_topk_weights[(int64_t)i * sh.K + c] = on_d ? __int_as_float(meta[1 + sh.K + c]) : 0.0f;
         } else if (sf_vec == 4) {
@@ -531,10 +539,11 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_expand(DispatchArgs a, in
         const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
         const int32_t *meta = a.staging_meta + row * sh.meta_words;
         const int t = meta[0];
+        if ((unsigned)t >= (unsigned)sh.T) continue;  // never true for staging rows the scatter wrote
         int pos = -1, wbits = 0;
         if (lane < sh.K) {
             const int e = meta[1 + lane];
-            if (e >= 0 && e / sh.El == d) {
+            if ((unsigned)e < (unsigned)sh.E && rank_of(sh, e) == d) {
                 pos = a.expand_pos[((int64_t)s * sh.T + t) * sh.K + lane];
                 wbits = meta[1 + sh.K + lane];
             }
@@ -665,7 +674,7 @@ struct EpilogueL {
                                          : a.recv_capacity_rows;
         if (a.sh.expand)
             hipLaunchKernelGGL(k_epilogue_expand<CPL>, dim3(grid_for(rows, EP_EXPAND_BLOCKS)), dim3(kThreads),
-                               fits ? tab : 0, st, a, (int)fits);
+                               std::max<size_t>(fits ? tab : 0, EP_EXPAND_LDS), st, a, (int)fits);
         else if (a.slices == 1 && a.sh.row_bytes / 16 <= CPL * kWave)
             hipLaunchKernelGGL(k_epilogue_pf<CPL>, dim3(grid_for(rows, EP_EPILOGUE_BLOCKS)), dim3(kThreads),
                                fits ? tab : 0, st, a, (int)fits);

@@ -26,6 +26,13 @@ struct Shape {
 // index on the hybrid path.
 __host__ __device__ inline int row_base(const Shape &sh, int s) { return sh.n_out > 1 ? s / sh.n_up : s; }
 
+// Destination rank of a valid expert id e (0 <= e < E <= 1024), e / El, as a
+// multiply and a shift: with m = floor(2^22 / El) + 1, e * m / 2^22 exceeds
+// e / El by less than e / 2^22 < 2^-12, while the fraction of e / El is at most
+// 1 - 1/El <= 1 - 2^-10, so the floor is exact for all 0 <= e < 1024 and
+// El <= 1024, and e * m < 2^32.
+__host__ __device__ inline int rank_of(const Shape &sh, int e) { return (int)(((uint32_t)e * sh.el_mul) >> 22); }
+
 // Region (of Nmax rows) that source s fills in destination d's staging rows:
 // d*S + s on the direct path; in the hybrid row form, segment = scale-up
 // index, then the scale-out index inside the segment.

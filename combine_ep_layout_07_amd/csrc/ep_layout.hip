@@ -149,13 +149,6 @@ __device__ __forceinline__ void load_batch(const Shape &sh, const int64_t *topk_
     }
 }
 
-// Destination rank of expert e, e / El, as a multiply and a shift: with
-// m = floor(2^22 / El) + 1, e * m / 2^22 exceeds e / El by less than
-// e / 2^22 < 2^-12, while the fraction of e / El is at most 1 - 1/El <=
-// 1 - 2^-10, so the floor is exact for all 0 <= e < 1024 and El <= 1024, and
-// e * m < 2^32.
-__device__ __forceinline__ int rank_of(const Shape &sh, int e) { return (int)(((uint32_t)e * sh.el_mul) >> 22); }
-
 __device__ __forceinline__ Item make_item(const Shape &sh, int64_t e64, int t_step, int t_end, const StepCtx &c,
                                           bool need_e) {
     Item it;
