@@ -338,13 +338,18 @@ def test_identity_expert_round_trip(cfg_id):
     assert bool((err <= 1e-2 * want.abs() + 1e-5).all()), float(err.max())
 
 
-@pytest.mark.parametrize("cfg_id", [1, 2])
-def test_graph_replay_matches_eager(cfg_id):
+GRAPH_CASES = [WORKLOADS[1], WORKLOADS[2],
+               Workload("expand_a4_fp8_graph", S=3, T=70, H=128, K=4, E=16, R=4, Nmax=70, expand=True, alignment=4,
+                        dtype="fp8")]
+
+
+@pytest.mark.parametrize("w", GRAPH_CASES, ids=lambda w: w.name)
+def test_graph_replay_matches_eager(w):
     """A step (layout, dispatch, combine) captured in a HIP graph and replayed
     several times, with eager work and synchronisation between the replays,
-    gives the eager result every time (the library enqueues kernels only)."""
-    w = WORKLOADS[cfg_id]
-    inputs = generate(w, seed_for(cfg_id, 1))
+    gives the eager result every time (the library enqueues kernels only;
+    the expand case covers the launches that request LDS to cap residency)."""
+    inputs = generate(w, 4242)
     dev = upload(w, inputs)
     say(f"[case] {w.name} graph replay")
     cfg, L = run_layout(w, dev)
@@ -360,7 +365,7 @@ def test_graph_replay_matches_eager(cfg_id):
 
     step()
     torch.cuda.synchronize()
-    n = int(L.recv_base[-1].item())
+    n = int((L.expert_base if w.expand else L.recv_base)[-1].item())
     ref = (L.dst_slot.clone(), R.recv_x[:n].clone(), R.recv_topk_weights[:n].clone(), out.clone())
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
