@@ -134,6 +134,15 @@ def _ptr(t: Optional[torch.Tensor], name: str, nbytes: int = 0):
     return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
 
 
+def _check_elem(t: Optional[torch.Tensor], name: str, size: int) -> None:
+    """Rows are read as elements of ``size`` bytes (bf16 2, e4m3fn 1, fp32
+    scales 4): a tensor of that element width (any dtype, a bit view included)
+    or of raw bytes is accepted, so that e.g. fp32 activations passed for bf16
+    rows are refused instead of being read as bf16 bits."""
+    if t is not None and t.element_size() not in (1, size):
+        raise ValueError(f"{name} must have {size}-byte elements (or be raw bytes), got {t.dtype}")
+
+
 def _empty(nbytes: int, dtype: torch.dtype, device) -> Optional[torch.Tensor]:
     if nbytes == 0:
         return None
@@ -234,6 +243,8 @@ def ep_dispatch(cfg: EpConfig, x: torch.Tensor, x_sf: Optional[torch.Tensor], to
     rw = H if fp8 else 2 * H
     if topk_weights.dtype != torch.float32 or topk_idx.dtype != torch.int64:
         raise ValueError("topk_idx must be int64 and topk_weights float32")
+    _check_elem(x, "x", 1 if fp8 else 2)
+    _check_elem(x_sf, "x_sf", 4)
     rc = _lib.ep_dispatch(ctypes.byref(cfg), _ptr(x, "x", S * T * rw),
                           _ptr(x_sf, "x_sf", S * T * (H // 128) * 4 if fp8 else 0),
                           _ptr(topk_idx, "topk_idx", S * T * K * 8), _ptr(topk_weights, "topk_weights", S * T * K * 4),
@@ -248,6 +259,8 @@ def ep_combine(cfg: EpConfig, layout: LayoutBuffers, topk_idx: torch.Tensor, top
     rows = int(ep_query_sizes(cfg).recv_rows)
     if topk_weights.dtype != torch.float32 or topk_idx.dtype != torch.int64:
         raise ValueError("topk_idx must be int64 and topk_weights float32")
+    _check_elem(y, "y", 2)
+    _check_elem(out, "out", 2)
     rc = _lib.ep_combine(ctypes.byref(cfg), ctypes.byref(layout.struct), _ptr(topk_idx, "topk_idx", S * T * K * 8),
                          _ptr(topk_weights, "topk_weights", S * T * K * 4), _ptr(y, "y", rows * H * 2),
                          _ptr(out, "out", S * T * H * 2), _stream(stream))
@@ -263,6 +276,8 @@ def ep_combine_bias(cfg: EpConfig, layout: LayoutBuffers, topk_idx: torch.Tensor
     rows = int(ep_query_sizes(cfg).recv_rows)
     if topk_weights.dtype != torch.float32 or topk_idx.dtype != torch.int64:
         raise ValueError("topk_idx must be int64 and topk_weights float32")
+    for t, name in ((y, "y"), (bias0, "bias0"), (bias1, "bias1"), (out, "out")):
+        _check_elem(t, name, 2)
     nb = S * T * H * 2
     rc = _lib.ep_combine_bias(ctypes.byref(cfg), ctypes.byref(layout.struct), _ptr(topk_idx, "topk_idx", S * T * K * 8),
                               _ptr(topk_weights, "topk_weights", S * T * K * 4), _ptr(y, "y", rows * H * 2),

@@ -6,6 +6,7 @@ import json
 import os
 import re
 import subprocess
+import types
 
 import pytest
 
@@ -185,6 +186,20 @@ def test_layout_scratch_grows_with_num_layout_cus():
     # any int32 request is clamped to at least one token per wave: 4096 tokens give at most 1024 units
     c = ep.ep_query_sizes(ep.make_config(1, 4096, 7168, 8, 256, 16, 4096, num_layout_cus=2**31 - 1))
     assert c.layout_scratch == 1024 * (16 + 256 + 1) * 4
+
+
+def test_binding_checks_element_sizes():
+    import torch
+    cfg = ep.make_config(1, 4, 64, 2, 8, 4, 4)
+    L = types.SimpleNamespace(struct=ep.EpLayoutT())
+    idx, w = torch.zeros((1, 4, 2), dtype=torch.int64), torch.zeros((1, 4, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="x must have 2-byte elements"):
+        ep.ep_dispatch(cfg, torch.zeros((4, 64), dtype=torch.float32), None, idx, w, L, None)
+    with pytest.raises(ValueError, match="y must have 2-byte elements"):
+        ep.ep_combine(cfg, L, idx, w, torch.zeros((8, 64), dtype=torch.float32), torch.zeros((4, 64)))
+    with pytest.raises(ValueError, match="bias0 must have 2-byte elements"):
+        ep.ep_combine_bias(cfg, L, idx, w, torch.zeros((8, 64), dtype=torch.bfloat16),
+                           torch.zeros((4, 64), dtype=torch.float32), None, torch.zeros((4, 64), dtype=torch.bfloat16))
 
 
 def test_binding_refuses_host_tensors():
