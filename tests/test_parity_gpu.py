@@ -416,6 +416,39 @@ def test_random_small_configurations(seed):
     _full_case(w, 100 + seed, edge, num_layout_cus=int(rng.choice([0, 0, 1, 5])), direct=direct)
 
 
+def _random_large_workload(rng):
+    """Larger random shapes: up to 3000 tokens per source, H up to 7168, up to
+    64 ranks and 1024 experts, staging kept under 4 GiB."""
+    while True:
+        R = int(rng.choice([1, 2, 8, 16, 32, 64]))
+        El = int(rng.choice([1, 2, 4, 8, 16]))
+        if R * El > 1024:
+            continue
+        K = int(rng.integers(1, min(8, R * El) + 1))
+        n_out = int(rng.choice([1, 1, 2]))
+        S = n_out * int(rng.choice([1, 2]))
+        T = int(rng.integers(0, 3001))
+        dtype = "fp8" if rng.random() < 0.3 else "bf16"
+        H = int(rng.choice([1024, 7168])) if dtype == "fp8" else int(rng.choice([128, 1024, 2048, 4096, 7168]))
+        expand = bool(rng.random() < 0.3)
+        Nmax = T + int(rng.integers(0, 9))
+        if R * S * Nmax * (H if dtype == "fp8" else 2 * H) <= 4 << 30:
+            return Workload("rand_large", S=S, T=T, H=H, K=K, E=R * El, R=R, Nmax=Nmax, dtype=dtype, expand=expand,
+                            alignment=int(rng.choice([1, 4, 128])) if expand else 1, n_out=n_out)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_large_configurations(seed):
+    """Random larger shapes (layouts, fp8, hybrid, Direct Recv X, edge lanes,
+    layout workgroup counts up to 300) against the oracle."""
+    rng = np.random.default_rng(77000 + seed)
+    w = _random_large_workload(rng)
+    direct = (not w.expand) and rng.random() < 0.4
+    edge = dict(masked_frac=float(rng.random() * 0.2), invalid_frac=float(rng.random() * 0.02),
+                dup_frac=float(rng.random() * 0.2))
+    _full_case(w, 500 + seed, edge, num_layout_cus=int(rng.choice([0, 0, 7, 300])), direct=direct)
+
+
 def test_readme_example_runs():
     """The Python example in README.md, executed as written: with an identity
     expert the combine returns bf16(sum_k w_k * x) = x up to rounding."""
