@@ -1,6 +1,7 @@
 """Host-side pieces of bench.py (no GPU): the one-GPU guard, the algorithmic
 byte formula, and the counter summary that feeds the roofline's traffic."""
 import csv
+import json
 import os
 import subprocess
 import sys
@@ -121,3 +122,32 @@ def test_epilogue_runs_split_back_to_back_from_in_step(tmp_path):
     assert g["back_to_back"]["n"] == 3
     assert g["back_to_back"]["avg_us"] == pytest.approx(130.0)
     assert g["back_to_back"]["span_us_per_launch"] == pytest.approx(394 / 3)
+
+
+def test_trace_summary_end_to_end(tmp_path):
+    stats, trace, js, md = (tmp_path / "kt_kernel_stats.csv", tmp_path / "kt_kernel_trace.csv", tmp_path / "b.json",
+                            tmp_path / "out.md")
+    epi = "void ep::(anonymous namespace)::k_epilogue_pf<14>(ep::DispatchArgs, int)"
+    with open(stats, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"])
+        w.writeheader()
+        w.writerow({"Name": epi, "Calls": 3, "AverageNs": 128000, "MinNs": 120000, "MaxNs": 134000, "Percentage": 52})
+        w.writerow({"Name": "void at::native::fill", "Calls": 1, "AverageNs": 5, "MinNs": 5, "MaxNs": 5,
+                    "Percentage": 1})
+    with open(trace, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for name, a, b in [("void ep::k_scatter<14>(ep::DispatchArgs)", 0, 70), (epi, 70, 190),
+                           ("void ep::k_combine<2>(ep::CombineArgs)", 190, 268), (epi, 300, 434), (epi, 434, 568)]:
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": a * 1000, "End_Timestamp": b * 1000})
+    js.write_text("[bench] progress\n" + json.dumps({
+        "config": {"workload": "dsv3_share: test"}, "value": 5900.0, "ms_per_step": 0.282,
+        "stage_us": {"epilogue": 130.0, "epilogue_back_to_back": 134.5},
+        "roofline": {"achieved": 5731.0, "alg_bytes_per_launch": 770844464, "timing": "events"}}) + "\n")
+    bench.summarize_trace(str(stats), str(js), str(md), command="rocprofv3 --kernel-trace --stats ...")
+    text = md.read_text()
+    assert "| `void ep::k_epilogue_pf<14>(ep::DispatchArgs, int)` | 3 | 128.00 |" in text
+    assert "at::native" not in text                                   # library kernels only
+    assert "| back to back (roofline loop) | 2 | 134.00 | 134.00 | 134.5 |" in text
+    assert "| inside steps (after the scatter) | 1 | 120.00 |" in text
+    assert "6022.2 GB/s = 75.3% of 8 TB/s" in text                     # 770844464 B / 128 us
