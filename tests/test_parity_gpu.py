@@ -416,6 +416,21 @@ def test_random_small_configurations(seed):
     _full_case(w, 100 + seed, edge, num_layout_cus=int(rng.choice([0, 0, 1, 5])), direct=direct)
 
 
+MAX_CASES = [
+    Workload("h_max_bf16", S=1, T=16, H=262144, K=2, E=8, R=4, Nmax=16),        # 512 KiB rows
+    Workload("h_max_fp8", S=2, T=8, H=262144, K=3, E=12, R=4, Nmax=9, dtype="fp8"),  # 256 KiB rows + 2048 scales
+    Workload("h_max_expand", S=1, T=8, H=262144, K=2, E=8, R=4, Nmax=8, expand=True, alignment=3),
+    Workload("s_max", S=65535, T=1, H=8, K=1, E=2, R=2, Nmax=1),                # layout grid y = 65535
+]
+
+
+@pytest.mark.parametrize("w", MAX_CASES, ids=lambda w: w.name)
+def test_maximum_sizes(w):
+    """The largest hidden size (H = 262144) in both layouts and dtypes, and the
+    largest number of sources (S = 65535, receiver tables far beyond LDS)."""
+    _full_case(w, 4321, dict(masked_frac=0.1, dup_frac=0.2))
+
+
 def _random_large_workload(rng):
     """Larger random shapes: up to 3000 tokens per source, H up to 7168, up to
     64 ranks and 1024 experts, staging kept under 4 GiB."""
