@@ -431,6 +431,16 @@ def test_maximum_sizes(w):
     _full_case(w, 4321, dict(masked_frac=0.1, dup_frac=0.2))
 
 
+@pytest.mark.parametrize("mode", ["staging", "direct", "expand"])
+def test_grid_stride_loops(mode):
+    """4.5 M tokens of 16-byte rows at top-2: about 8.5 M receive rows, more work
+    units than the 2^20-workgroup grids hold, so every kernel's grid-stride
+    loop (scatter, copy epilogue and its pipelined next-row path, metadata-only
+    and expand epilogues, combine) runs more than one iteration."""
+    w = Workload(f"many_rows_{mode}", S=1, T=4_500_000, H=8, K=2, E=2, R=2, Nmax=4_500_000, expand=mode == "expand")
+    _full_case(w, 99, dict(masked_frac=0.05), direct=mode == "direct")
+
+
 def _random_large_workload(rng):
     """Larger random shapes: up to 3000 tokens per source, H up to 7168, up to
     64 ranks and 1024 experts, staging kept under 4 GiB."""
