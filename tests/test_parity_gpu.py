@@ -292,6 +292,30 @@ def test_dispatch_is_bitwise_reproducible():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("cfg_id", [2, 5])
+def test_combine_is_bitwise_reproducible(cfg_id):
+    """The combine sums each output element in one lane in a fixed order, so
+    repeated runs, and runs on layouts computed with different workgroup counts,
+    give bitwise equal outputs (the property the deterministic path exists for)."""
+    w = WORKLOADS[cfg_id]
+    inputs = generate(w, seed_for(cfg_id))
+    dev = upload(w, inputs)
+    say(f"[case] {w.name} combine reproducibility")
+    rows = None
+    outs = []
+    for cus in (0, 0, 37):
+        cfg, L = run_layout(w, dev, num_layout_cus=cus)
+        if rows is None:
+            rows = int(ep.ep_query_sizes(cfg).recv_rows)
+            y = seeded_y(rows, w.H, 11)
+        out = torch.empty((w.S * w.T, w.H), dtype=torch.bfloat16, device="cuda")
+        ep.ep_combine(cfg, L, dev["topk_idx"], dev["topk_weights"], y, out)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+
+
 def test_phases_split_equals_all():
     w = WORKLOADS[2]
     inputs = generate(w, seed_for(2, 1))
