@@ -324,6 +324,9 @@ __device__ __forceinline__ void locate_row(const int32_t *recv_base, const int32
         cnt += popc(ballot(l < R && recv_base[l] <= i));
     }
     d = cnt - 1;
+    s = 0;
+    j = -1;         // callers skip rows with j outside [0, Nmax)
+    if (d < 0) return;  // only for tables that no layout wrote (recv_base[0] is 0)
     const int off = i - recv_base[d];
     const int32_t *ps = recv_psum + (int64_t)d * (S + 1);
     cnt = 0;
@@ -332,6 +335,7 @@ __device__ __forceinline__ void locate_row(const int32_t *recv_base, const int32
         cnt += popc(ballot(l < S && ps[l] <= off));
     }
     s = cnt - 1;
+    if (s < 0) return;  // likewise (recv_psum[d][0] is 0)
     j = off - ps[s];
 }
 
