@@ -48,8 +48,9 @@ constexpr int kRowsPerGroup = EP_COMBINE_ROWS;
 // In the expand layout (one row per lane, 8 rows per token at top-8) the
 // launch asks for enough LDS that at most three workgroups are resident per CU
 // (3 waves per SIMD instead of the 4 the registers allow): measured on MI355X
-// at 16 x 2048 tokens, H = 7168, 754 -> 705 us (2 per SIMD: 737 us); the
-// compact layout's combine measured 3-7% slower so, and keeps all 4.
+// at 16 x 2048 tokens, H = 7168, 754 -> 705 us (2 per SIMD: 737 us).  The
+// compact layout's combine keeps all 4: capped the same way it measured 3-7%
+// slower.
 #ifndef EP_COMBINE_EXPAND_LDS
 #define EP_COMBINE_EXPAND_LDS lds_to_cap_residency(3)
 #endif

@@ -91,9 +91,9 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 // its per-row chain (locate, record, the lanes' expand rows) needs many waves
 // in flight.  Measured on MI355X at 16 x 2048 tokens: 2048 / 16384 / 65536
 // workgroups 1349 / 1327 / 1280 us.  Its launch also asks for enough LDS that
-// at most two workgroups (2 waves per SIMD, as the compact epilogue's
-// registers allow) are resident per CU: 1284 -> 1228 us there, while 3 waves
-// per SIMD measured the same as the 4 its registers allow.
+// at most two workgroups are resident per CU (2 waves per SIMD, the occupancy
+// the compact epilogue's registers give it): 1284 -> 1228 us there, while 3
+// waves per SIMD measured the same as the 4 its registers allow.
 #ifndef EP_EXPAND_LDS
 #define EP_EXPAND_LDS lds_to_cap_residency(2)
 #endif
