@@ -362,21 +362,22 @@ def test_identity_expert_round_trip(cfg_id):
     assert bool((err <= 1e-2 * want.abs() + 1e-5).all()), float(err.max())
 
 
-GRAPH_CASES = [WORKLOADS[1], WORKLOADS[2],
-               Workload("expand_a4_fp8_graph", S=3, T=70, H=128, K=4, E=16, R=4, Nmax=70, expand=True, alignment=4,
-                        dtype="fp8")]
+GRAPH_CASES = [(WORKLOADS[1], False), (WORKLOADS[2], False), (WORKLOADS[2], True),
+               (Workload("expand_a4_fp8_graph", S=3, T=70, H=128, K=4, E=16, R=4, Nmax=70, expand=True, alignment=4,
+                         dtype="fp8"), False)]
 
 
-@pytest.mark.parametrize("w", GRAPH_CASES, ids=lambda w: w.name)
-def test_graph_replay_matches_eager(w):
+@pytest.mark.parametrize("w,direct", GRAPH_CASES, ids=lambda c: getattr(c, "name", "direct" if c else "staging"))
+def test_graph_replay_matches_eager(w, direct):
     """A step (layout, dispatch, combine) captured in a HIP graph and replayed
     several times, with eager work and synchronisation between the replays,
     gives the eager result every time (the library enqueues kernels only;
-    the expand case covers the launches that request LDS to cap residency)."""
+    the expand case covers the launches that request LDS to cap residency,
+    the Direct Recv X case its pipelined scatter and metadata-only epilogue)."""
     inputs = generate(w, 4242)
     dev = upload(w, inputs)
-    say(f"[case] {w.name} graph replay")
-    cfg, L = run_layout(w, dev)
+    say(f"[case] {w.name} graph replay direct={direct}")
+    cfg, L = run_layout(w, dev, direct=direct)
     R = ep.alloc_recv(cfg)
     rows = int(ep.ep_query_sizes(cfg).recv_rows)
     y = seeded_y(rows, w.H, 3)
