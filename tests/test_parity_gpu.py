@@ -21,8 +21,8 @@ pytestmark = pytest.mark.gpu
 import combine_ep_layout_07_amd.ep as ep  # noqa: E402
 import oracle  # noqa: E402
 from combine_ep_layout_07_amd.workloads import WORKLOADS, Workload, generate, seed_for  # noqa: E402
-from tests.gpu_harness import (compare_combine, compare_dispatch, compare_tables, layout_host, run_layout,  # noqa: E402
-                               say, seeded_y, upload)
+from tests.gpu_harness import (bf16_to_f64, compare_combine, compare_dispatch, compare_tables, layout_host,  # noqa: E402
+                               run_layout, say, seeded_y, upload)
 
 
 def _full_case(w, seed, edge=None, num_layout_cus=0, check_combine=True, combine_sample=None, direct=False):
@@ -314,6 +314,38 @@ def test_combine_is_bitwise_reproducible(cfg_id):
         outs.append(out)
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
     assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+
+
+@pytest.mark.parametrize("w", [WORKLOADS[1], Workload("expand_specials", S=2, T=100, H=256, K=4, E=16, R=4, Nmax=100,
+                                                     expand=True)], ids=lambda w: w.name)
+def test_combine_special_values(w):
+    """Expert outputs with NaN, +-Inf, -0, subnormals and large finite values:
+    non-finite results match the oracle's class (NaN, +Inf, -Inf; NaN payloads
+    may differ), finite ones stay within the combine tolerance."""
+    inputs = generate(w, 555)
+    dev = upload(w, inputs)
+    say(f"[case] {w.name} combine special values")
+    cfg, L = run_layout(w, dev)
+    lay_o = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment)
+    rows = int(ep.ep_query_sizes(cfg).recv_rows)
+    y_h = seeded_y(rows, w.H, 21).view(torch.int16).cpu().numpy().view(np.uint16).copy()
+    rng = np.random.default_rng(7)
+    specials = np.array([0x7FC0, 0x7F80, 0xFF80, 0x8000, 0x0001, 0x007F, 0x8005, 0x7149, 0xF149], np.uint16)
+    pick = rng.random(y_h.shape) < 0.002
+    y_h[pick] = specials[rng.integers(0, specials.size, int(pick.sum()))]
+    y = torch.from_numpy(y_h.view(np.int16)).to("cuda").view(torch.bfloat16)
+    out = torch.empty((w.S * w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    ep.ep_combine(cfg, L, dev["topk_idx"], dev["topk_weights"], y, out)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+    ref = oracle.combine(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.expand, inputs["topk_idx"], inputs["topk_weights"],
+                         lay_o, y_h).reshape(-1)
+    g, o = bf16_to_f64(got), bf16_to_f64(ref)
+    assert np.isnan(o).any() and np.isinf(o).any(), "the draw must reach NaN and Inf outputs"
+    assert (np.isnan(g) == np.isnan(o)).all()
+    assert (np.isposinf(g) == np.isposinf(o)).all() and (np.isneginf(g) == np.isneginf(o)).all()
+    fin = np.isfinite(o)
+    compare_combine(got[fin], ref[fin])
 
 
 def test_phases_split_equals_all():
