@@ -227,12 +227,18 @@ int ep_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev
                 const ep_layout_t *layout, const ep_recv_t *recv, int32_t phases, void *stream);
 
 /* Combine ([UNO] Changes: the reduce epilogue brings expert outputs back to
- * token order): out[s][t] = bf16(sum over valid lanes k, ascending, of
- * w[s][t][k] * Y(s,t,k)), accumulated in fp32 and rounded to nearest-even
- * once.  Y is, in the compact layout, row recv_base[d] + recv_psum[d][s] +
- * run of y_dev for the lane's rank d (lanes sharing a rank weight the same
- * row); in the expand layout, row expand_pos[s][t][k].  A token with no valid
- * lane gives +0.
+ * token order): out[s][t] = bf16(sum over valid lanes k of w[s][t][k] *
+ * Y(s,t,k)), accumulated in fp32 and rounded to nearest-even once.  Y is, in
+ * the compact layout, row recv_base[d] + recv_psum[d][s] + run of y_dev for
+ * the lane's rank d (lanes sharing a rank weight the same row); in the expand
+ * layout, row expand_pos[s][t][k].  A token with no valid lane gives +0.
+ * Arithmetic order (fixed, so results are bitwise reproducible): in the
+ * compact layout the weights of the lanes that share a rank are first summed
+ * in fp32 in ascending lane order, then each distinct row is applied with one
+ * fp32 fused multiply-add, rows in the order of their owner (lowest) lanes; in
+ * the expand layout each valid lane's row is applied with one fused
+ * multiply-add in ascending lane order.  The result is therefore within one
+ * bf16 rounding of the exact sum, not bitwise that of a per-lane fp32 loop.
  *   y_dev   bf16 [rows][H] in the receive row order (at least recv_rows rows)
  *   out_dev bf16 [S][T][H] */
 int ep_combine(const ep_config_t *cfg, const ep_layout_t *layout, const int64_t *topk_idx_dev,

@@ -212,16 +212,3 @@ def combine_tokens(S, T, H, K, E, R, Nmax, expand: bool, topk_idx: np.ndarray, t
         raise ValueError(f"epo_combine_tokens rejected the arguments (rc={rc})")
     return out
 
-
-def run_workload(w, inputs: Dict[str, np.ndarray], y: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
-    """Layout + dispatch (+ combine when ``y`` is given) for a ``workloads.Workload``."""
-    lay = layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment, w.n_out)
-    res = dict(lay)
-    if "x" in inputs:
-        res.update(dispatch(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.dtype == "fp8", w.expand, w.alignment,
-                            inputs["x"], inputs.get("x_sf"), inputs["topk_idx"], inputs["topk_weights"], lay,
-                            w.n_out))
-    if y is not None:
-        res["out"] = combine(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.expand, inputs["topk_idx"],
-                             inputs["topk_weights"], lay, y, w.n_out)
-    return res

@@ -325,8 +325,9 @@ def exact_combine_row(y_rows, weights):
     return np.array(out, np.uint16)
 
 
-def combine_rows_for_token(S, T, K, E, R, Nmax, topk, lay, s, t, expand):
-    """(row, k) pairs of Y that token (s, t) combines: the owner's receive row per rank, or the lane's expand row."""
+def combine_rows_for_token(S, T, K, E, R, Nmax, topk, lay, s, t, expand, n_out=1):
+    """(row, k) pairs of Y that token (s, t) combines: the owner's receive row per rank, or the lane's expand row
+    (the owner's slot minus its row base, s or, on the hybrid path, s's scale-out index, times Nmax)."""
     El = E // R
     topk = np.asarray(topk).reshape(S, T, K)
     pairs = []
@@ -339,7 +340,7 @@ def combine_rows_for_token(S, T, K, E, R, Nmax, topk, lay, s, t, expand):
         else:
             d = e // El
             k0 = next(k2 for k2 in range(K) if _valid(int(topk[s, t, k2]), E) and int(topk[s, t, k2]) // El == d)
-            j = int(np.asarray(lay["dst_slot"]).reshape(S, T, K)[s, t, k0]) - s * Nmax
+            j = int(np.asarray(lay["dst_slot"]).reshape(S, T, K)[s, t, k0]) - row_base(s, S, n_out) * Nmax
             rb = np.asarray(lay["recv_base"]).ravel()
             rp = np.asarray(lay["recv_psum"]).reshape(R, S + 1)
             pairs.append((int(rb[d] + rp[d, s] + j), k))

@@ -257,3 +257,64 @@ def test_hybrid_dispatch_rows_and_combine(expand):
     a = oracle.combine(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, expand, d["topk_idx"], d["topk_weights"], lay, y, 2)
     b = oracle.combine(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, expand, d["topk_idx"], d["topk_weights"], dlay, y)
     assert (a == b).all()
+
+
+def combine_tokens_pin(w, seed):
+    """oracle.combine_tokens against the exact rational combine of each selected
+    token, and bitwise against the rows of the full oracle.combine it samples.
+
+    The selection is unsorted, repeats tokens and includes a token with no
+    valid lane (its row is +0); a selected index g names token (s, t) with
+    g = s*T + t (the global source token index)."""
+    d = generate(w, seed, masked_frac=0.2, dup_frac=0.3)
+    topk = d["topk_idx"].copy()
+    topk[w.S - 1, min(1, w.T - 1), :] = -1  # a token with no valid lane
+    lay = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, topk, w.expand, w.alignment, w.n_out)
+    rows = oracle.recv_rows(w.S, w.T, w.K, w.E, w.R, lay, w.expand)
+    H = 16
+    y = draw_expert_outputs(max(rows, 1), H, seed + 1)
+    n = w.S * w.T
+    rng = np.random.default_rng(seed)
+    empty_tok = (w.S - 1) * w.T + min(1, w.T - 1)
+    sel = np.concatenate([rng.permutation(n)[: max(1, n // 2)], rng.integers(0, n, 5), [empty_tok, n - 1, 0]])
+    got = oracle.combine_tokens(w.S, w.T, H, w.K, w.E, w.R, w.Nmax, w.expand, topk, d["topk_weights"], lay, y, sel,
+                                w.n_out)
+    assert got.shape == (sel.size, H)
+    for i, g in enumerate(sel):
+        s, t = divmod(int(g), w.T)
+        pairs = combine_rows_for_token(w.S, w.T, w.K, w.E, w.R, w.Nmax, topk, lay, s, t, w.expand, w.n_out)
+        want = exact_combine_row([y[r] for r, _ in pairs], [d["topk_weights"][s, t, k] for _, k in pairs]) \
+            if pairs else np.zeros(H, np.uint16)
+        assert (got[i] == want).all(), f"combine_tokens row {i} (token {g} = ({s}, {t})) differs"
+    assert (got[sel == empty_tok] == 0).all()
+    full = oracle.combine(w.S, w.T, H, w.K, w.E, w.R, w.Nmax, w.expand, topk, d["topk_weights"], lay, y,
+                          w.n_out).reshape(n, H)
+    assert (got == full[sel]).all()
+
+
+COMBINE_TOKENS_CASES = [
+    Workload("ct_direct", S=3, T=19, H=16, K=4, E=16, R=4, Nmax=21),
+    Workload("ct_hybrid", S=6, T=11, H=16, K=3, E=12, R=6, Nmax=12, n_out=2),
+    Workload("ct_hybrid3", S=6, T=7, H=16, K=4, E=16, R=4, Nmax=7, n_out=3),
+    Workload("ct_expand", S=2, T=17, H=16, K=3, E=12, R=6, Nmax=17, expand=True, alignment=4),
+    Workload("ct_expand_hybrid", S=4, T=9, H=16, K=4, E=16, R=4, Nmax=9, expand=True, alignment=2, n_out=2),
+]
+
+
+@pytest.mark.parametrize("w", COMBINE_TOKENS_CASES, ids=lambda w: w.name)
+def test_combine_tokens_matches_exact_and_full_combine(w):
+    combine_tokens_pin(w, 1234)
+
+
+def test_combine_tokens_edge_arguments():
+    w = COMBINE_TOKENS_CASES[0]
+    d = generate(w, 3)
+    lay = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, d["topk_idx"])
+    y = draw_expert_outputs(int(lay["recv_base"][-1]), 8, 2)
+    empty = oracle.combine_tokens(w.S, w.T, 8, w.K, w.E, w.R, w.Nmax, False, d["topk_idx"], d["topk_weights"], lay,
+                                  y, np.zeros(0, np.int64))
+    assert empty.shape == (0, 8)
+    for bad in (-1, w.S * w.T):
+        with pytest.raises(ValueError):
+            oracle.combine_tokens(w.S, w.T, 8, w.K, w.E, w.R, w.Nmax, False, d["topk_idx"], d["topk_weights"], lay,
+                                  y, np.array([0, bad], np.int64))
