@@ -80,17 +80,19 @@ int64_t recv_rows(const ep::Shape &sh) {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
-int check_layout_ptrs(const ep::Shape &sh, const ep_layout_t *L) {
+// need_scratch: the caller's scratch_dev is used (every call but
+// ep_layout_no_alloc, which takes the library's own).
+int check_layout_ptrs(const ep::Shape &sh, const ep_layout_t *L, bool need_scratch = true) {
     if (!L) return EP_ERR_INVALID_ARG;
     const bool need_tok = (int64_t)sh.S * sh.T * sh.K > 0;
     if ((need_tok && !L->dst_slot_dev) || !L->tokens_per_rank_dev || !L->tokens_per_expert_dev ||
-        !L->recv_psum_dev || !L->recv_base_dev || !L->error_flags_dev || !L->scratch_dev)
+        !L->recv_psum_dev || !L->recv_base_dev || !L->error_flags_dev || (need_scratch && !L->scratch_dev))
         return EP_ERR_INVALID_ARG;
     if (sh.expand && (!L->expert_base_dev || (need_tok && !L->expand_pos_dev))) return EP_ERR_INVALID_ARG;
     if (sh.n_out > 1 && !L->recv_psum_scaleup_dev) return EP_ERR_INVALID_ARG;
     const void *ps[] = {L->dst_slot_dev, L->tokens_per_rank_dev, L->tokens_per_expert_dev, L->recv_psum_dev,
-                        L->recv_base_dev, L->expert_base_dev, L->expand_pos_dev, L->error_flags_dev, L->scratch_dev,
-                        L->recv_psum_scaleup_dev};
+                        L->recv_base_dev, L->expert_base_dev, L->expand_pos_dev, L->error_flags_dev,
+                        need_scratch ? L->scratch_dev : nullptr, L->recv_psum_scaleup_dev};
     for (const void *p : ps)
         if (!aligned(p, 4)) return EP_ERR_INVALID_ARG;
     return EP_OK;
@@ -147,15 +149,27 @@ int ep_query_sizes(const ep_config_t *cfg, ep_sizes_t *sz) {
     return EP_OK;
 }
 
-int ep_layout(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layout_t *layout, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// ep_layout and ep_layout_no_alloc: the same launches on the caller's scratch
+// or on the library's own (own_scratch).
+int layout_call(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layout_t *layout, void *stream,
+                bool own_scratch) {
     ep::Shape sh;
     int rc = make_shape(cfg, &sh);
     if (rc != EP_OK) return rc;
-    if ((rc = check_layout_ptrs(sh, layout)) != EP_OK) return rc;
+    if ((rc = check_layout_ptrs(sh, layout, !own_scratch)) != EP_OK) return rc;
     if ((int64_t)sh.S * sh.T * sh.K > 0 && (!topk_idx_dev || !aligned(topk_idx_dev, 8))) return EP_ERR_INVALID_ARG;
     ep::LayoutArgs a;
     a.sh = sh;
     a.g = ep::layout_geometry(sh, cfg->num_layout_cus);
+    void *scratch = layout->scratch_dev;
+    if (own_scratch) {
+        if (ep::layout_scratch_bytes(sh, a.g) > EP_NO_ALLOC_SCRATCH_BYTES) return EP_ERR_CAPACITY;
+        if (ep::no_alloc_scratch(&scratch) != hipSuccess) return EP_ERR_HIP;
+    }
     a.topk_idx = topk_idx_dev;
     a.dst_slot = layout->dst_slot_dev;
     a.tokens_per_rank = layout->tokens_per_rank_dev;
@@ -167,12 +181,25 @@ int ep_layout(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layo
     a.error_flags = layout->error_flags_dev;
     a.recv_psum_scaleup = layout->recv_psum_scaleup_dev;
     const int64_t units = (int64_t)sh.S * a.g.blocks_per_src;
-    a.blk_cnt_rank = static_cast<int32_t *>(layout->scratch_dev);
+    a.blk_cnt_rank = static_cast<int32_t *>(scratch);
     a.blk_cnt_expert = a.blk_cnt_rank + units * sh.R;
     a.blk_flags = a.blk_cnt_expert + units * sh.E;
     a.blk_pre_expert = sh.expand ? a.blk_flags + units : nullptr;
     a.cnt_expert = sh.expand ? a.blk_pre_expert + units * sh.E : nullptr;
     return ep::launch_layout(a, (hipStream_t)stream) == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_layout(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layout_t *layout, void *stream) {
+    return layout_call(cfg, topk_idx_dev, layout, stream, false);
+}
+
+int ep_layout_no_alloc(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layout_t *layout,
+                       void *stream) {
+    return layout_call(cfg, topk_idx_dev, layout, stream, true);
 }
 
 int ep_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev, const int64_t *topk_idx_dev,

@@ -97,6 +97,9 @@ struct CombineArgs {
 };
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream);
+// Device address of the library's own layout scratch (EP_NO_ALLOC_SCRATCH_BYTES
+// bytes) on the current device; looked up once per device, thread-safe.
+hipError_t no_alloc_scratch(void **ptr);
 hipError_t launch_scatter(const DispatchArgs &a, hipStream_t stream);
 hipError_t launch_epilogue(const DispatchArgs &a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);

@@ -32,6 +32,9 @@
 //     (recv_psum, recv_base, expert_base, error_flags);
 //   k_layout_single: for one source whose items fit one workgroup, all of the
 //     above in one launch (the unit's counts are the source's totals).
+#include <mutex>
+
+#include "ep.h"
 #include "ep_device.h"
 #include "ep_kernels.h"
 
@@ -739,6 +742,36 @@ hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
     else
         hipLaunchKernelGGL(k_layout_slot<false>, slot_grid, dim3(kLayoutThreads), slot_lds_bytes(a.sh), stream, a);
     return hipGetLastError();
+}
+
+// Layout scratch owned by the library, for ep_layout_no_alloc (callers that
+// cannot allocate device memory).  Each GPU the library runs on holds its own
+// copy until the process ends; host code never uses the array's name as an
+// address (in host code it is only a stand-in for the symbol), only the device
+// address hipGetSymbolAddress returns for the current device, looked up once
+// per device and kept.  No word needs clearing: every scratch word a layout
+// reads was written earlier in the same layout.
+static __device__ __align__(256) uint8_t scratch[EP_NO_ALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t no_alloc_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    static std::mutex mu;
+    static void *addr[kMaxDevices];
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace ep

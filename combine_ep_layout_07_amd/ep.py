@@ -69,11 +69,13 @@ def _load():
     P = ctypes.c_void_p
     lib.ep_query_sizes.argtypes = [ctypes.POINTER(EpConfig), ctypes.POINTER(EpSizes)]
     lib.ep_layout.argtypes = [ctypes.POINTER(EpConfig), P, ctypes.POINTER(EpLayoutT), P]
+    lib.ep_layout_no_alloc.argtypes = [ctypes.POINTER(EpConfig), P, ctypes.POINTER(EpLayoutT), P]
     lib.ep_dispatch.argtypes = [ctypes.POINTER(EpConfig), P, P, P, P, ctypes.POINTER(EpLayoutT),
                                 ctypes.POINTER(EpRecvT), ctypes.c_int32, P]
     lib.ep_combine.argtypes = [ctypes.POINTER(EpConfig), ctypes.POINTER(EpLayoutT), P, P, P, P, P]
     lib.ep_combine_bias.argtypes = [ctypes.POINTER(EpConfig), ctypes.POINTER(EpLayoutT), P, P, P, P, P, P, P]
-    for f in ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_combine", "ep_combine_bias", "ep_version"):
+    for f in ("ep_query_sizes", "ep_layout", "ep_layout_no_alloc", "ep_dispatch", "ep_combine", "ep_combine_bias",
+              "ep_version"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ep_status_string.argtypes = [ctypes.c_int]
     lib.ep_status_string.restype = ctypes.c_char_p
@@ -233,6 +235,17 @@ def ep_layout(cfg: EpConfig, topk_idx: torch.Tensor, layout: LayoutBuffers, stre
                         _stream(stream))
     if rc != EP_OK:
         raise EpError(rc, "ep_layout")
+
+
+def ep_layout_no_alloc(cfg: EpConfig, topk_idx: torch.Tensor, layout: LayoutBuffers, stream=None) -> None:
+    """ep_layout on the library's own per-GPU scratch (layout.scratch is not used)."""
+    S, T, K = cfg.num_src_ranks, cfg.num_tokens, cfg.num_topk
+    if topk_idx.dtype != torch.int64:
+        raise ValueError("topk_idx must be int64")
+    rc = _lib.ep_layout_no_alloc(ctypes.byref(cfg), _ptr(topk_idx, "topk_idx", S * T * K * 8),
+                                 ctypes.byref(layout.struct), _stream(stream))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_layout_no_alloc")
 
 
 def ep_dispatch(cfg: EpConfig, x: torch.Tensor, x_sf: Optional[torch.Tensor], topk_idx: torch.Tensor,

@@ -214,6 +214,26 @@ int ep_query_sizes(const ep_config_t *cfg, ep_sizes_t *sizes);
 int ep_layout(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layout_t *layout,
               void *stream);
 
+/* Size of the layout scratch the library keeps on each GPU for
+ * ep_layout_no_alloc. */
+#define EP_NO_ALLOC_SCRATCH_BYTES (4u << 20)
+
+/* ep_layout for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same launches and the same tables as ep_layout, but the scratch is an
+ * EP_NO_ALLOC_SCRATCH_BYTES array the library holds on each GPU it runs on
+ * until the process ends, so layout->scratch_dev is ignored (may be NULL).
+ * The call allocates and frees nothing.  A configuration whose
+ * ep_sizes_t.layout_scratch exceeds EP_NO_ALLOC_SCRATCH_BYTES returns
+ * EP_ERR_CAPACITY before anything is enqueued; EP_ERR_HIP if the array's
+ * device address cannot be obtained.  Every call on one GPU uses that GPU's
+ * one array: calls that overlap on one GPU (on different streams, or from
+ * different host threads without ordering) race and may produce wrong tables,
+ * so order them (for example, one stream).  The array needs no clearing
+ * between calls. */
+int ep_layout_no_alloc(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layout_t *layout,
+                       void *stream);
+
 /* Dispatch: scatter ([DET] Direct vs hybrid dispatch: senders replay the
  * layout's slots) of every token's row, scales and metadata into the staging
  * rows, then the copy epilogue ([DRX] Background) into the receive buffers.

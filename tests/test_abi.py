@@ -144,6 +144,25 @@ def test_misaligned_pointer_rejected():
 
 
 @fake_pointers
+def test_no_alloc_layout_rejects_scratch_beyond_its_array():
+    """ep_layout_no_alloc: a configuration whose layout scratch exceeds the
+    library's array is refused before anything is enqueued (or any HIP call);
+    the caller's scratch pointer is not required."""
+    fake = 0x200000
+    L = ep.EpLayoutT(*[ctypes.c_void_p(fake + 256 * i) for i in range(10)])
+    L.scratch_dev = None
+    L.expert_base_dev = L.expand_pos_dev = L.recv_psum_scaleup_dev = None
+    cfg = ep.make_config(1, 4096, 7168, 8, 1024, 64, 4096, num_layout_cus=1024)
+    assert ep.ep_query_sizes(cfg).layout_scratch > 4 << 20
+    assert ep._lib.ep_layout_no_alloc(ctypes.byref(cfg), ctypes.c_void_p(fake), ctypes.byref(L), None) == \
+        ep.EP_ERR_CAPACITY
+    assert ep._lib.ep_layout(ctypes.byref(cfg), ctypes.c_void_p(fake), ctypes.byref(L), None) == \
+        ep.EP_ERR_INVALID_ARG  # ep_layout needs the caller's scratch
+    bad = ep.make_config(1, 16, 64, 2, 8, 4, 8)  # Nmax < T: the same checks as ep_layout come first
+    assert ep._lib.ep_layout_no_alloc(ctypes.byref(bad), None, ctypes.byref(L), None) == ep.EP_ERR_CAPACITY
+
+
+@fake_pointers
 def test_dispatch_rejects_short_receive_capacity():
     cfg = ep.make_config(1, 16, 64, 2, 8, 4, 16)
     fake = 0x100000
