@@ -71,26 +71,38 @@ def _counter_csv(path, counter, rows):
 
 
 def test_counter_summary_round_trip(tmp_path, monkeypatch):
-    src = tmp_path / "k.hip"
-    src.write_text("int k;\n")
-    out = tmp_path / "traffic.md"
-    monkeypatch.setattr(bench, "EPILOGUE_SOURCES", [str(src)])
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    """Per-kernel traffic from two counter CSVs, scaled by the calibration copy,
+    read back for the roofline, and invalidated by a code change to the
+    kernel's sources (not by a comment)."""
+    csrc = tmp_path / "csrc"
+    csrc.mkdir()
+    for f in ("ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_device.h", "ep_kernels.h"):
+        (csrc / f).write_text("int k;\n")
+    monkeypatch.setattr(bench, "CSRC", str(csrc))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     cal_kib = bench.COPY_CAL_BYTES / 1024
-    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    epi = "void ep::(anonymous namespace)::k_epilogue_pf<14>(ep::DispatchArgs, int)"
+    comb = "void ep::(anonymous namespace)::k_combine<2>(ep::CombineArgs)"
+    fetch, write, js = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "b.json"
     # FETCH_SIZE reads half the copy's bytes (scale 2), WRITE_SIZE all of them (scale 1).
     _counter_csv(fetch, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", cal_kib / 2), ("__amd_rocclr_copyBuffer", 4.0),
-                                       ("void ep::k_epilogue<14>(ep::DispatchArgs, int)", 1000.0),
-                                       ("void ep::k_epilogue<14>(ep::DispatchArgs, int)", 1002.0)])
-    _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", cal_kib),
-                                       ("void ep::k_epilogue<14>(ep::DispatchArgs, int)", 3000.0)])
-    bench.summarize_counters(str(fetch), str(write), str(out), command="rocprofv3 --pmc ...")
+                                       (epi, 1000.0), (epi, 1002.0), (comb, 500.0)])
+    _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", cal_kib), (epi, 3000.0), (comb, 100.0)])
+    js.write_text("[bench] progress\n" + json.dumps({
+        "config": {"workload": "dsv3_share: test"},
+        "alg_bytes_per_step": {"layout": 1, "scatter": 2, "epilogue": 5000 * 1024, "combine": 1100 * 1024}}) + "\n")
+    out = tmp_path / "dsv3_share_traffic.md"
+    bench.summarize_counters(str(fetch), str(write), str(js), str(out), command="rocprofv3 --pmc ...")
     want = (1001.0 * 2 + 3000.0) * 1024
-    assert bench.read_traffic(0) == pytest.approx(want)
-    src.write_text("int k;  // a comment keeps the counters valid\n")
-    assert bench.read_traffic(0) == pytest.approx(want)
-    src.write_text("int k2;\n")
-    assert bench.read_traffic(0) is None
+    assert bench.read_traffic("dsv3_share", "epilogue") == pytest.approx(want)
+    assert bench.read_traffic("dsv3_share", "combine") == pytest.approx((500.0 * 2 + 100.0) * 1024)
+    assert "| 1.0004 |" in out.read_text()  # epilogue traffic / algorithmic bytes
+    (csrc / "ep_dispatch.hip").write_text("int k;  // a comment keeps the counters valid\n")
+    assert bench.read_traffic("dsv3_share", "epilogue") == pytest.approx(want)
+    (csrc / "ep_dispatch.hip").write_text("int k2;\n")
+    assert bench.read_traffic("dsv3_share", "epilogue") is None
+    assert bench.read_traffic("dsv3_share", "combine") is not None  # combine's sources did not change
+    assert bench.read_traffic("other_workload", "epilogue") is None
 
 
 def test_algorithmic_bytes_padding_and_bias_terms():
@@ -104,7 +116,7 @@ def test_algorithmic_bytes_padding_and_bias_terms():
     assert b2["combine"] - b0["combine"] == 2 * 4096 * 7168 * 2
 
 
-def test_epilogue_runs_split_back_to_back_from_in_step(tmp_path):
+def test_kernel_runs_split_back_to_back_from_in_step(tmp_path):
     p = tmp_path / "kt_kernel_trace.csv"
     epi, sc, cb = ("void ep::k_epilogue_pf<14>(ep::DispatchArgs, int)", "void ep::k_scatter<14>(ep::DispatchArgs)",
                    "void ep::k_combine<2>(ep::CombineArgs)")
@@ -117,7 +129,7 @@ def test_epilogue_runs_split_back_to_back_from_in_step(tmp_path):
         w.writeheader()
         for name, a, b in reversed(seq):
             w.writerow({"Kernel_Name": name, "Start_Timestamp": a * 1000, "End_Timestamp": b * 1000})
-    g = bench.epilogue_runs(str(p))
+    g = bench.kernel_runs(str(p), lambda n: "k_epilogue_pf" in n)
     assert g["in_step"] == {"n": 2, "avg_us": 120.0}
     assert g["back_to_back"]["n"] == 3
     assert g["back_to_back"]["avg_us"] == pytest.approx(130.0)
@@ -143,11 +155,32 @@ def test_trace_summary_end_to_end(tmp_path):
     js.write_text("[bench] progress\n" + json.dumps({
         "config": {"workload": "dsv3_share: test"}, "value": 5900.0, "ms_per_step": 0.282,
         "stage_us": {"epilogue": 130.0, "epilogue_back_to_back": 134.5},
-        "roofline": {"achieved": 5731.0, "alg_bytes_per_launch": 770844464, "timing": "events"}}) + "\n")
+        "roofline": {"kernel": "k_epilogue_pf (epilogue)", "stage": "epilogue", "achieved": 5731.0, "frac": 0.716,
+                     "alg_bytes_per_launch": 770844464, "timing": "events"}}) + "\n")
     bench.summarize_trace(str(stats), str(js), str(md), command="rocprofv3 --kernel-trace --stats ...")
     text = md.read_text()
     assert "| `void ep::k_epilogue_pf<14>(ep::DispatchArgs, int)` | 3 | 128.00 |" in text
     assert "at::native" not in text                                   # library kernels only
     assert "| back to back (roofline loop) | 2 | 134.00 | 134.00 | 134.5 |" in text
-    assert "| inside steps (after the scatter) | 1 | 120.00 |" in text
-    assert "6022.2 GB/s = 75.3% of 8 TB/s" in text                     # 770844464 B / 128 us
+    assert "| inside steps | 1 | 120.00 |" in text
+    assert "5752.6 GB/s = 71.9% of 8 TB/s" in text                     # 770844464 B / 134 us (back to back)
+
+
+def test_cpu_baseline_legs_on_the_tiny_workload(monkeypatch):
+    """Both CPU legs run the unthreaded oracle; the all-cores leg uses the
+    threads the host grants and checks every thread's result against the
+    one-thread pass."""
+    from combine_ep_layout_07_amd.workloads import generate, seed_for
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    w = WORKLOADS[1]
+    inputs = generate(w, seed_for(1))
+    import oracle
+    lay = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"])
+    n = int(lay["recv_base"][-1])
+    r = bench.cpu_baseline(w, inputs, n, int(((inputs["topk_idx"] >= 0) & (inputs["topk_idx"] < w.E)).sum()),
+                           budget_s=0.3)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s"
+    assert r["cores"] == min(3, r["host"]["affinity_cpus"]) and r["host"]["threads"] == r["cores"]
+    assert r["single_thread"]["cores"] == 1 and r["single_thread"]["value"] > 0 and r["value"] > 0
+    assert "bitwise equal to the one-thread pass" in r["sample"]
+    assert r["host"]["model"] and r["host"]["os_cpu_count"] >= 1
