@@ -8,6 +8,7 @@
 // status code instead of an abort.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "ep.h"
@@ -26,7 +27,7 @@ int bits_for(int n) {
 // Validate a configuration and derive the kernel shape.
 int make_shape(const ep_config_t *c, ep::Shape *sh) {
     if (!c || !sh) return EP_ERR_INVALID_ARG;
-    if ((c->flags & ~EP_FLAG_DIRECT_RECV_X) != 0) return EP_ERR_INVALID_ARG;
+    if ((c->flags & ~(EP_FLAG_DIRECT_RECV_X | EP_FLAG_LAYOUT_ONE_LAUNCH)) != 0) return EP_ERR_INVALID_ARG;
     if ((c->flags & EP_FLAG_DIRECT_RECV_X) && c->expand) return EP_ERR_UNSUPPORTED;
     if (c->num_src_ranks < 1 || c->num_tokens < 0 || c->hidden < 1 || c->num_topk < 1 || c->num_experts < 1 ||
         c->num_ranks < 1 || c->num_max_tokens_per_rank < 0 || c->num_layout_cus < 0 || c->expert_alignment < 1 ||
@@ -186,6 +187,30 @@ int layout_call(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_la
     a.blk_flags = a.blk_cnt_expert + units * sh.E;
     a.blk_pre_expert = sh.expand ? a.blk_flags + units : nullptr;
     a.cnt_expert = sh.expand ? a.blk_pre_expert + units * sh.E : nullptr;
+    // The one-launch layout's exchange words follow the counts, 8-byte aligned.
+    a.sync = nullptr;
+    if (!sh.expand) {
+        const uintptr_t end = reinterpret_cast<uintptr_t>(a.blk_flags + units);
+        a.sync = reinterpret_cast<uint64_t *>((end + 7) & ~static_cast<uintptr_t>(7));
+    }
+    a.one_launch = (cfg->flags & EP_FLAG_LAYOUT_ONE_LAUNCH) ? 1 : 0;
+    // Bounds of the exchange's waits (each poll is one device-scope load and
+    // a short sleep, about a microsecond): 2^21 polls for the coordinator and
+    // for each unit.  EP_LAYOUT_SYNC_TEST forces a time-out, for tests of the
+    // error path only: 1 = the coordinator waits for words no unit writes;
+    // 2 = every unit does.
+    a.spin_master = 1u << 21;
+    a.spin_unit = 1u << 21;
+    a.sync_test = 0;
+    if (const char *t = getenv("EP_LAYOUT_SYNC_TEST")) {
+        if (t[0] == '1') {
+            a.sync_test = 1;
+            a.spin_master = 64;
+        } else if (t[0] == '2') {
+            a.sync_test = 2;
+            a.spin_unit = 64;
+        }
+    }
     return ep::launch_layout(a, (hipStream_t)stream) == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 

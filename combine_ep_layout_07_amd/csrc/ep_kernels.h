@@ -64,7 +64,17 @@ struct LayoutArgs {
     int32_t *blk_flags;       // scratch [S*B]
     int32_t *blk_pre_expert;  // scratch [S*B][E], expand only: valid lanes of the earlier units per expert
     int32_t *cnt_expert;      // scratch [E], expand only: valid lanes per expert over all sources
+    // One-launch layout (compact layout): the grid-wide exchange's words in
+    // scratch, 8-byte aligned: [0] epoch, [1 + u] arrival word of unit u.
+    // None of them needs initialising (see ep_layout.hip).
+    uint64_t *sync;
+    uint32_t spin_master, spin_unit;  // polls before the coordinator / a unit gives up
+    int sync_test;                    // 0; 1 or 2 force a time-out (tests of the error path)
+    int one_launch;                   // compact layout: one launch with a grid-wide exchange, where it fits
 };
+
+// Words of the one-launch layout's exchange for `units` units.
+constexpr uint64_t layout_sync_words(uint64_t units) { return 1 + units; }
 
 struct DispatchArgs {
     Shape sh;
@@ -97,6 +107,9 @@ struct CombineArgs {
 };
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream);
+// Whether launch_layout takes the one-launch form for these arguments on the
+// current device.
+bool layout_is_one_launch(const LayoutArgs &a);
 // Device address of the library's own layout scratch (EP_NO_ALLOC_SCRATCH_BYTES
 // bytes) on the current device; looked up once per device, thread-safe.
 hipError_t no_alloc_scratch(void **ptr);

@@ -31,8 +31,17 @@
 //     column prefix; one extra workgroup writes the receiver tables
 //     (recv_psum, recv_base, expert_base, error_flags);
 //   k_layout_single: for one source whose items fit one workgroup, all of the
-//     above in one launch (the unit's counts are the source's totals).
+//     above in one launch (the unit's counts are the source's totals);
+//   k_layout_fused: the compact layout in one launch, the page's cooperative
+//     two-pass form: every unit counts and publishes its counts, one
+//     coordinating workgroup waits for all of them and releases the units,
+//     which then rank their items from the counts they kept in LDS; the
+//     coordinator builds the receiver tables meanwhile.  Used when the whole
+//     grid fits on the device at once (checked on the host); otherwise, and
+//     for the expand layout, the separate launches above run.
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "ep.h"
 #include "ep_device.h"
@@ -105,7 +114,11 @@ LayoutGeom layout_geometry(const Shape &sh, int num_layout_cus) {
 
 uint64_t layout_scratch_bytes(const Shape &sh, const LayoutGeom &g) {
     const uint64_t units = (uint64_t)sh.S * g.blocks_per_src;
-    return (units * (uint64_t)(sh.R + sh.E + 1 + (sh.expand ? sh.E : 0)) + (sh.expand ? sh.E : 0)) * sizeof(int32_t);
+    const uint64_t counts =
+        (units * (uint64_t)(sh.R + sh.E + 1 + (sh.expand ? sh.E : 0)) + (sh.expand ? sh.E : 0)) * sizeof(int32_t);
+    // the compact layout's one-launch exchange: 8-byte words after the counts
+    // (plus up to 4 bytes to align them)
+    return sh.expand ? counts : counts + 4 + layout_sync_words(units) * sizeof(uint64_t);
 }
 
 namespace {
@@ -532,7 +545,7 @@ __device__ __forceinline__ void build_receiver_tables(const LayoutArgs &a, bool 
         a.recv_base[R] = run;
         int any = 0;
         for (int q = 0; q < kLayoutWaves; ++q) any |= part[64 + q];
-        a.error_flags[0] = any ? 1 : 0;
+        __hip_atomic_store(a.error_flags, any ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -633,6 +646,207 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_slot(LayoutArgs a) {
     }
 }
 
+// ------------------------------------------------ one-launch layout
+// Grid-wide exchange.  Each launch derives fresh 64-bit tokens from an epoch
+// word that the coordinator advances at the end of every launch, so nothing
+// needs resetting between launches (nor initialising: a stale or arbitrary
+// word equals a token of this launch with probability 2^-64), HIP-graph
+// replays get new tokens, and no memset is involved.  A unit publishes its
+// counts, then stores its arrival token; every unit waits for the arrivals of
+// all units of its source (it needs their counts for its base and its share of
+// the source's totals), and the coordinator waits for all arrivals before it
+// builds the receiver tables.  Every wait is bounded: a unit that times out
+// stores a give-up token in its arrival word, skips the slot pass and sets
+// bit 1 of error_flags; a coordinator that times out (or sees a give-up)
+// skips the tables and sets bit 1.  The tables of such a call are not valid.
+enum : uint64_t { kTokArrive = 1, kTokGiveUp = 2 };
+
+// A 64-bit mix of (epoch, unit, kind): the SplitMix64 finaliser applied to a
+// combination of the three.
+__device__ __forceinline__ uint64_t sync_token(uint64_t epoch, uint64_t unit, uint64_t kind) {
+    uint64_t z = epoch * 0x9E3779B97F4A7C15ull + (unit + 1) * 0xD1B54A32D192ED03ull + kind * 0xA0761D6478BD642Full;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ uint64_t sync_load(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void sync_store(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Bounded wait of the whole workgroup for the arrivals of units [u0, u1):
+// thread i polls units u0 + i, u0 + i + 256, ...  `flip` (tests only) makes
+// the awaited word one that nobody writes.  Returns nonzero (in every thread)
+// if some unit gave up or a poll ran out of its `limit`.
+__device__ __forceinline__ int wait_arrivals(const LayoutArgs &a, uint64_t e1, int64_t u0, int64_t u1, uint32_t limit,
+                                             uint64_t flip) {
+    int late = 0;
+    for (int64_t u = u0 + threadIdx.x; u < u1 && !late; u += kLayoutThreads) {
+        const uint64_t want = sync_token(e1, (uint64_t)u, kTokArrive) ^ flip;
+        const uint64_t gave = sync_token(e1, (uint64_t)u, kTokGiveUp);
+        for (uint32_t n = 0;; ++n) {
+            const uint64_t v = sync_load(a.sync + 1 + u);
+            if (v == want) break;
+            if (v == gave || n >= limit) {
+                late = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    return __syncthreads_or(late);
+}
+
+// After the workgroup's waits: make the other units' counts visible to every
+// wave of this workgroup (one device-scope acquire, then a barrier).
+__device__ __forceinline__ void acquire_counts() {
+    if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __syncthreads();
+}
+
+// The coordinating workgroup: waits for every unit's arrival, builds the
+// receiver tables and writes error_flags (bit 0 from the units' invalid-id
+// flags, bit 1 on a time-out); finally advances the epoch for the next launch.
+__device__ void fused_coordinator(const LayoutArgs &a, int *lds, uint64_t *epoch_sh) {
+    const int tid = threadIdx.x;
+    const int64_t U = (int64_t)a.sh.S * a.g.blocks_per_src;
+    if (tid == 0) *epoch_sh = sync_load(a.sync);
+    __syncthreads();
+    const uint64_t e1 = *epoch_sh + 1;
+    const int late = wait_arrivals(a, e1, 0, U, a.spin_master, a.sync_test == 1 ? 1ull : 0ull);
+    acquire_counts();
+    // Every unit published its counts before it arrived, so the tables are
+    // exact whenever all arrivals were seen; a time-out leaves them untouched.
+    if (!late) build_receiver_tables(a, false, lds);
+    if (tid == 0) {
+        if (late) __hip_atomic_store(a.error_flags, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // A unit that gives up stores its give-up token and then sets bit 1;
+        // with a full fence on both sides, either that token is seen by the
+        // re-check below or its bit lands after the store of error_flags.
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+    }
+    __syncthreads();
+    int gave = 0;
+    for (int64_t u = tid; u < U; u += kLayoutThreads)
+        gave |= sync_load(a.sync + 1 + u) == sync_token(e1, (uint64_t)u, kTokGiveUp);
+    if (__syncthreads_or(gave) && tid == 0)
+        __hip_atomic_fetch_or(a.error_flags, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) sync_store(a.sync, e1);  // every unit read the epoch before it arrived
+}
+
+// The compact layout in one launch ([DET] Approach: a cooperative two-pass
+// scan with a grid-wide exchange).  Grid (B + 1) x S: unit (b, s) counts its
+// tokens per wave into LDS (kept for the slot pass), publishes the unit
+// totals, arrives, waits for the other units of its source, then turns the
+// earlier units' totals and its own per-wave counts into running bases and
+// ranks its items; workgroup (B, 0) coordinates and builds the receiver
+// tables, the rest of that column exits at once.  The host launches it only
+// when the whole grid fits on the device at once.
+__global__ void __launch_bounds__(kLayoutThreads) k_layout_fused(LayoutArgs a) {
+    const Shape &sh = a.sh;
+    const int b = blockIdx.x, s = blockIdx.y, B = a.g.blocks_per_src;
+    const int w = threadIdx.x / kWave, tid = threadIdx.x;
+    const int R = sh.R, E = sh.E;
+    extern __shared__ int lds[];
+    __shared__ uint64_t epoch_sh;
+    __shared__ int wave_bad[kLayoutWaves];
+    if (b == B) {
+        if (s == 0) fused_coordinator(a, lds, &epoch_sh);
+        return;
+    }
+    const int64_t me = (int64_t)s * B + b;
+    int *cnt_d = lds;                        // [waves][R] per-wave counts, then running bases
+    int *cnt_e = cnt_d + kLayoutWaves * R;   // [waves][E]
+    int *base_d = cnt_e + kLayoutWaves * E;  // [R]   this unit's base per destination
+    int *col = base_d + R + E;               // [R+E] per-source totals of this unit's share of columns
+
+    int t0, t1;
+    wave_range(a, b, w, t0, t1);
+    const StepCtx c = make_ctx(sh.K);
+    const bool single = t1 - t0 <= kBatch * c.tps;
+    const int64_t *topk_src = a.topk_idx + (int64_t)s * sh.T * sh.K;
+    int64_t first[kBatch] = {};
+    if (single) load_batch(sh, topk_src, t0, t1, c, first);  // kept in registers for the slot pass
+    if (tid == 0) epoch_sh = sync_load(a.sync);
+    for (int i = tid; i < kLayoutWaves * (R + E) + R + E + (R + E); i += kLayoutThreads) lds[i] = 0;
+    __syncthreads();
+
+    // Pass 1: per-wave counts, then the unit totals for the other units.
+    const bool bad = wave_count(sh, topk_src, t0, t1, cnt_d + w * R, cnt_e + w * E, true, c, first, single);
+    if (lane_id() == 0) wave_bad[w] = bad ? 1 : 0;
+    __syncthreads();
+    for (int d = tid; d < R; d += kLayoutThreads) {
+        int v = 0;
+        for (int q = 0; q < kLayoutWaves; ++q) v += cnt_d[q * R + d];
+        a.blk_cnt_rank[me * R + d] = v;
+    }
+    for (int e = tid; e < E; e += kLayoutThreads) {
+        int v = 0;
+        for (int q = 0; q < kLayoutWaves; ++q) v += cnt_e[q * E + e];
+        a.blk_cnt_expert[me * E + e] = v;
+    }
+    if (tid == 0) {
+        int any = 0;
+        for (int q = 0; q < kLayoutWaves; ++q) any |= wave_bad[q];
+        a.blk_flags[me] = any;
+    }
+    // Publish: after the barrier every wave's stores have reached this CU's
+    // L2; one device-scope release makes them visible before the arrival.
+    __syncthreads();
+    const uint64_t e1 = epoch_sh + 1;
+    if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        sync_store(a.sync + 1 + me, sync_token(e1, (uint64_t)me, kTokArrive));
+    }
+    const int64_t u0 = (int64_t)s * B;
+    if (wait_arrivals(a, e1, u0, u0 + B, a.spin_unit, a.sync_test == 2 ? 1ull : 0ull)) {
+        if (tid == 0) {
+            sync_store(a.sync + 1 + me, sync_token(e1, (uint64_t)me, kTokGiveUp));
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+            __hip_atomic_fetch_or(a.error_flags, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return;
+    }
+    acquire_counts();
+
+    // Pass 2: this unit's base per destination (what the earlier units of the
+    // source send there) and its share of the per-source totals.
+    const int32_t *src_rank = a.blk_cnt_rank + (int64_t)s * B * R;
+    ColumnLoads lb, lc;
+    column_issue(lb, b, R, [&](int d, int64_t &stride) {
+        stride = R;
+        return src_rank + d;
+    });
+    const int ncol = b < R + E ? (R + E - b + B - 1) / B : 0;
+    auto col_src = [&](int j, int64_t &stride) -> const int32_t * {
+        const int cidx = b + j * B;
+        if (cidx < R) {
+            stride = R;
+            return a.blk_cnt_rank + (int64_t)s * B * R + cidx;
+        }
+        stride = E;
+        return a.blk_cnt_expert + (int64_t)s * B * E + (cidx - R);
+    };
+    const bool col_early = ncol <= kLayoutThreads;
+    column_issue(lc, B, col_early ? ncol : 0, col_src);
+    column_finish(lb, base_d);
+    __syncthreads();
+    wave_bases(cnt_d, R, base_d);
+    __syncthreads();
+    rank_items(a, false, s, t0, t1, c, first, single, cnt_d + w * R, cnt_e + w * E);
+    if (col_early) column_finish(lc, col);
+    else column_sums(B, ncol, col, col_src);
+    __syncthreads();
+    for (int j = tid; j < ncol; j += kLayoutThreads) {
+        const int cidx = b + j * B;
+        if (cidx < R) a.tokens_per_rank[(int64_t)s * R + cidx] = col[j];
+        else a.tokens_per_expert[(int64_t)s * E + cidx - R] = col[j];
+    }
+}
+
 // The whole layout in one workgroup of NW waves, for one small source: the
 // workgroup's own counts are the source's totals, so the receiver tables and
 // the expert segment bases need no other workgroup, and the layout takes one
@@ -708,9 +922,43 @@ size_t slot_lds_bytes(const Shape &sh) {
     return sizeof(int) * ((size_t)kLayoutWaves * (sh.R + sh.E) + sh.R + sh.E + (sh.R + sh.E) + kLayoutThreads);
 }
 
+constexpr int kMaxDevices = 64;
+
+// Workgroups of k_layout_fused with `lds` bytes of dynamic LDS that the
+// current device holds at once (0 if unknown): resident workgroups per CU
+// times the CUs, looked up once per (device, LDS size).
+int64_t fused_capacity(size_t lds) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    static std::mutex mu;
+    static int cus[kMaxDevices];
+    static std::map<std::pair<int, size_t>, int64_t> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(dev, lds);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    if (!cus[dev] && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_layout_fused, kLayoutThreads, lds) != hipSuccess)
+        return 0;
+    return cache[key] = (int64_t)per_cu * cus[dev];
+}
+
 }  // namespace
 
+bool layout_is_one_launch(const LayoutArgs &a) {
+    if (a.sh.expand || a.g.single || !a.one_launch) return false;
+    const int64_t grid = ((int64_t)a.g.blocks_per_src + 1) * a.sh.S;
+    return grid <= fused_capacity(slot_lds_bytes(a.sh));
+}
+
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
+    if (layout_is_one_launch(a)) {
+        hipLaunchKernelGGL(k_layout_fused, dim3(a.g.blocks_per_src + 1, a.sh.S), dim3(kLayoutThreads),
+                           slot_lds_bytes(a.sh), stream, a);
+        return hipGetLastError();
+    }
     if (a.g.single) {
         const int nw = a.g.single;
         const size_t lds = single_lds_bytes(a.sh, nw);
@@ -749,11 +997,10 @@ hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
 // copy until the process ends; host code never uses the array's name as an
 // address (in host code it is only a stand-in for the symbol), only the device
 // address hipGetSymbolAddress returns for the current device, looked up once
-// per device and kept.  No word needs clearing: every scratch word a layout
-// reads was written earlier in the same layout.
+// per device and kept.  No word needs clearing: every count a layout reads
+// was written earlier in the same layout, and the one-launch layout's
+// exchange words are valid whatever they hold.
 static __device__ __align__(256) uint8_t scratch[EP_NO_ALLOC_SCRATCH_BYTES];
-
-constexpr int kMaxDevices = 64;
 
 hipError_t no_alloc_scratch(void **ptr) {
     int dev = -1;

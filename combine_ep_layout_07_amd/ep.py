@@ -26,7 +26,7 @@ LIB_PATH = os.environ.get("EP_LIBRARY") or os.path.join(_HERE, "libep.so")
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_CAPACITY, EP_ERR_UNSUPPORTED, EP_ERR_HIP = 0, -1, -2, -3, -4
 EP_DTYPE_BF16, EP_DTYPE_FP8_E4M3FN = 0, 1
 EP_PHASE_SCATTER, EP_PHASE_EPILOGUE, EP_PHASE_ALL = 1, 2, 3
-EP_FLAG_DIRECT_RECV_X = 1
+EP_FLAG_DIRECT_RECV_X, EP_FLAG_LAYOUT_ONE_LAUNCH = 1, 2
 
 
 class EpError(RuntimeError):
@@ -95,16 +95,16 @@ def ep_version() -> int:
 
 def make_config(S: int, T: int, H: int, K: int, E: int, R: int, Nmax: int, dtype: str = "bf16",
                 expand: bool = False, alignment: int = 1, num_layout_cus: int = 0,
-                direct_recv_x: bool = False, num_scaleout_ranks: int = 1) -> EpConfig:
+                direct_recv_x: bool = False, num_scaleout_ranks: int = 1, layout_one_launch: bool = False) -> EpConfig:
+    flags = (EP_FLAG_DIRECT_RECV_X if direct_recv_x else 0) | (EP_FLAG_LAYOUT_ONE_LAUNCH if layout_one_launch else 0)
     return EpConfig(S, T, H, K, E, R, Nmax, EP_DTYPE_FP8_E4M3FN if dtype == "fp8" else EP_DTYPE_BF16,
-                    int(bool(expand)), alignment, num_layout_cus, EP_FLAG_DIRECT_RECV_X if direct_recv_x else 0,
-                    num_scaleout_ranks)
+                    int(bool(expand)), alignment, num_layout_cus, flags, num_scaleout_ranks)
 
 
-def config_for(w, num_layout_cus: int = 0, direct_recv_x: bool = False) -> EpConfig:
+def config_for(w, num_layout_cus: int = 0, direct_recv_x: bool = False, layout_one_launch: bool = False) -> EpConfig:
     """EpConfig of a ``workloads.Workload``."""
     return make_config(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.dtype, w.expand, w.alignment, num_layout_cus,
-                       direct_recv_x, getattr(w, "n_out", 1))
+                       direct_recv_x, getattr(w, "n_out", 1), layout_one_launch)
 
 
 def ep_query_sizes(cfg: EpConfig) -> EpSizes:

@@ -31,7 +31,8 @@
  *   - argument errors are detected on the host before anything is enqueued
  *     and return a negative ep_status; a failed launch returns EP_ERR_HIP;
  *   - data errors found on the device (a top-k id >= E) set bit 0 of
- *     *error_flags and the lane is then treated as masked (id < 0);
+ *     *error_flags and the lane is then treated as masked (id < 0); bit 1
+ *     reports a timed-out one-launch layout (EP_FLAG_LAYOUT_ONE_LAUNCH);
  *   - calls on different streams with disjoint buffers may run concurrently.
  */
 #ifndef EP_H
@@ -74,7 +75,18 @@ enum ep_flags {
      * and the epilogue produces recv_sf and the metadata tensors but copies no
      * hidden bytes.  staging_x is not used (may be NULL).  Compact layout only
      * (EP_ERR_UNSUPPORTED with expand), as on the page. */
-    EP_FLAG_DIRECT_RECV_X = 1
+    EP_FLAG_DIRECT_RECV_X = 1,
+    /* ep_layout of the compact layout as one launch, the form [DET] Approach
+     * describes (a cooperative two-pass scan whose passes exchange their
+     * counts grid-wide), used when its whole grid fits on the device at once
+     * (checked on the host before the launch; otherwise the separate count
+     * and slot launches run).  Same tables as the default two launches, which
+     * measured faster on MI355X (8.3 against 9-11 us back to back at 4096
+     * tokens, top-8 of 256 on 16 ranks): the device's kernel boundary is
+     * cheaper than the exchange.  Its waits are bounded (far above any normal
+     * duration); a layout whose exchange times out sets bit 1 of
+     * *error_flags, and its tables are then not valid. */
+    EP_FLAG_LAYOUT_ONE_LAUNCH = 2
 };
 
 /* Limits (checked on the host): 1 <= R <= 64, 1 <= K <= 32, E % R == 0,

@@ -107,8 +107,10 @@ def test_hybrid_topology_validation():
 
 def test_flags_validation():
     cfg = ep.make_config(1, 16, 64, 2, 8, 4, 16)
-    cfg.flags = 2  # unknown option bit
+    cfg.flags = 4  # unknown option bit
     assert _rc(cfg) == ep.EP_ERR_INVALID_ARG
+    cfg.flags = ep.EP_FLAG_DIRECT_RECV_X | ep.EP_FLAG_LAYOUT_ONE_LAUNCH
+    assert _rc(cfg) == ep.EP_OK
     # Direct Recv X supports the compact layout only (as on the direct recv_x page)
     assert _rc(ep.make_config(1, 16, 64, 2, 8, 4, 16, expand=True, direct_recv_x=True)) == ep.EP_ERR_UNSUPPORTED
     d = ep.ep_query_sizes(ep.make_config(1, 4096, 7168, 8, 256, 16, 4096, direct_recv_x=True))
@@ -204,7 +206,11 @@ def test_layout_scratch_grows_with_num_layout_cus():
     assert 0 < a.layout_scratch < b.layout_scratch
     # any int32 request is clamped to at least one token per wave: 4096 tokens give at most 1024 units
     c = ep.ep_query_sizes(ep.make_config(1, 4096, 7168, 8, 256, 16, 4096, num_layout_cus=2**31 - 1))
-    assert c.layout_scratch == 1024 * (16 + 256 + 1) * 4
+    # counts per unit, then the one-launch layout's exchange words (8-byte
+    # aligned: up to 4 bytes of padding, the epoch, one per unit)
+    assert c.layout_scratch == 1024 * (16 + 256 + 1) * 4 + 4 + (1 + 1024) * 8
+    ex = ep.ep_query_sizes(ep.make_config(16, 2048, 7168, 8, 256, 16, 2048, "bf16", True))
+    assert ex.layout_scratch % 4 == 0  # the expand layout has no exchange words
 
 
 def test_binding_checks_element_sizes():

@@ -301,6 +301,66 @@ def test_layout_independent_of_workgroup_count(cfg_id):
             compare_tables(tabs, ref)
 
 
+ONE_LAUNCH = [WORKLOADS[2], WORKLOADS[4], Workload("ragged_sources", S=3, T=301, H=64, K=6, E=24, R=6, Nmax=310),
+              Workload("hybrid_2x8_small", S=16, T=96, H=64, K=8, E=256, R=16, Nmax=96, n_out=2),
+              Workload("k32_r64", S=2, T=500, H=64, K=32, E=1024, R=64, Nmax=500)]
+
+
+@pytest.mark.parametrize("w", ONE_LAUNCH, ids=lambda w: w.name)
+def test_one_launch_layout_equals_two_launches(w):
+    """The compact layout's one-launch form (count pass, grid-wide exchange,
+    slot pass in one kernel) and its default two-launch form give the
+    oracle's tables for several workgroup counts; three layouts in a row on
+    one scratch buffer (each launch derives fresh exchange tokens) stay exact."""
+    inputs = generate(w, 71, with_x=False, masked_frac=0.1, invalid_frac=0.02, dup_frac=0.2)
+    inputs["x"] = np.zeros((w.S, w.T, 16), np.uint8)
+    dev = upload(w, inputs)
+    lay_o = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment, w.n_out)
+    for cus in (0, 7, 300):
+        for one in (True, False):
+            say(f"[case] {w.name} layout cus={cus} one_launch={one}")
+            cfg = ep.config_for(w, cus, layout_one_launch=one)
+            L = ep.alloc_layout(cfg)
+            for _ in range(3):
+                for t in L.tables().values():
+                    t.fill_(-7)
+                ep.ep_layout(cfg, dev["topk_idx"], L)
+                torch.cuda.synchronize()
+                compare_tables(layout_host(L), lay_o)
+
+
+@pytest.mark.parametrize("mode", ["1", "2"])
+def test_one_launch_layout_time_out_is_reported(mode, monkeypatch):
+    """A forced time-out of the one-launch layout's exchange (EP_LAYOUT_SYNC_TEST:
+    1 = the coordinator waits for words no unit writes, 2 = every unit does and
+    gives up) ends the kernel normally with bit 1 of error_flags set (which
+    also shows that the one-launch form ran); the next layout on the same
+    scratch is exact again, and the default two-launch form never waits."""
+    w = WORKLOADS[2]
+    inputs = generate(w, seed_for(2), with_x=False)
+    inputs["x"] = np.zeros((w.S, w.T, 16), np.uint8)
+    dev = upload(w, inputs)
+    lay_o = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"])
+    cfg = ep.config_for(w, layout_one_launch=True)
+    L = ep.alloc_layout(cfg)
+    monkeypatch.setenv("EP_LAYOUT_SYNC_TEST", mode)
+    say(f"[case] forced layout exchange time-out, mode {mode}")
+    ep.ep_layout(cfg, dev["topk_idx"], L)
+    torch.cuda.synchronize()
+    assert int(L.error_flags.item()) & 2, "the time-out must be reported"
+    cfg2 = ep.config_for(w)
+    L2 = ep.alloc_layout(cfg2)
+    ep.ep_layout(cfg2, dev["topk_idx"], L2)
+    torch.cuda.synchronize()
+    assert int(L2.error_flags.item()) == 0
+    compare_tables(layout_host(L2), lay_o)
+    monkeypatch.delenv("EP_LAYOUT_SYNC_TEST")
+    ep.ep_layout(cfg, dev["topk_idx"], L)
+    torch.cuda.synchronize()
+    assert int(L.error_flags.item()) == 0
+    compare_tables(layout_host(L), lay_o)
+
+
 @pytest.mark.parametrize("name", list(SINGLE))
 def test_one_launch_layout_parity(name):
     """The one-launch layout (8 and 16 waves) against the oracle, with edge lanes."""
