@@ -274,6 +274,8 @@ int ep_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev
     a.recv_topk_weights = recv->recv_topk_weights_dev;
     a.recv_capacity_rows = recv->recv_capacity_rows;
     hipStream_t st = (hipStream_t)stream;
+    if (phases == EP_PHASE_ALL && ep::dispatch_is_one_launch(a))
+        return ep::launch_dispatch_fused(a, st) == hipSuccess ? EP_OK : EP_ERR_HIP;
     if ((phases & EP_PHASE_SCATTER) && ep::launch_scatter(a, st) != hipSuccess) return EP_ERR_HIP;
     if ((phases & EP_PHASE_EPILOGUE) && ep::launch_epilogue(a, st) != hipSuccess) return EP_ERR_HIP;
     return EP_OK;

@@ -105,6 +105,10 @@ __device__ __forceinline__ uint64_t token_rows(const CombineArgs &a, int64_t g, 
         if (sh.expand) pos = a.expand_pos[g * sh.K + lane];
         else slot = a.dst_slot[g * sh.K + lane];
     }
+    // Lane l < R fetches the base of source s in destination l's receive
+    // rows together with the ids, so that no load waits for a decoded rank.
+    int base_l = 0;
+    if (!sh.expand && lane < sh.R) base_l = a.recv_base[lane] + a.recv_psum[(int64_t)lane * (sh.S + 1) + s];
     const uint64_t vmask = ballot(valid);
     row = -1;
     wrow = 0.0f;
@@ -116,8 +120,8 @@ __device__ __forceinline__ uint64_t token_rows(const CombineArgs &a, int64_t g, 
         const uint64_t peers = match_key((uint32_t)d, sh.bits_R, vmask);
         const int owner = peers ? __builtin_ctzll(peers) : 0;
         const bool is_owner = valid && owner == lane;
-        if (is_owner)
-            row = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s] + (slot - row_base(sh, s) * sh.Nmax);
+        const int base_d = shfl(base_l, d);
+        if (is_owner) row = base_d + (slot - row_base(sh, s) * sh.Nmax);
         for (uint64_t m = vmask; m; m &= m - 1) {
             const int k = __builtin_ctzll(m);
             const float wk = __int_as_float(read_lane(__float_as_int(w), k));

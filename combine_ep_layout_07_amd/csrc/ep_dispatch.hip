@@ -81,6 +81,18 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #ifndef EP_SCATTER_BLOCKS
 #define EP_SCATTER_BLOCKS (1 << 20)
 #endif
+// Compact-layout problems of at most this many tokens (all sources) with
+// rows of at most EP_FUSED_DISPATCH_MAX_ROW bytes dispatch in one launch
+// (k_dispatch_fused) when both phases are asked for.  Measured on MI355X:
+// 128 tokens of 512-byte rows (top-4 of 32 on 8 ranks) 20.1 -> 17.7 us per
+// step; with 14 KiB rows the token-serial copy loses (128 tokens: 31.9 ->
+// 46.8 us per step, 2048 tokens: 142.8 -> 152.1 us).
+#ifndef EP_FUSED_DISPATCH_MAX_TOKENS
+#define EP_FUSED_DISPATCH_MAX_TOKENS 512
+#endif
+#ifndef EP_FUSED_DISPATCH_MAX_ROW
+#define EP_FUSED_DISPATCH_MAX_ROW 1024
+#endif
 #ifndef EP_DIRECT_INFLIGHT_BYTES
 #define EP_DIRECT_INFLIGHT_BYTES 7340032
 #endif
@@ -383,6 +395,71 @@ __device__ __forceinline__ void epilogue_row(const DispatchArgs &a, int d, int s
         const bool on_d = (unsigned)e < (unsigned)sh.E && rank_of(sh, e) == d;
         a.recv_topk_idx[(int64_t)i * sh.K + k] = on_d ? e - d * sh.El : -1;
         a.recv_topk_weights[(int64_t)i * sh.K + k] = on_d ? __int_as_float(meta[1 + sh.K + k]) : 0.0f;
+    }
+}
+
+// ------------------------------------------ small dispatch, one launch
+// Scatter and copy epilogue of a small compact-layout problem in one launch:
+// below a few hundred tokens the fixed cost of a second launch exceeds the
+// copy itself.  Each wave takes one token, stores its row and record to the
+// staging rows of its destinations (as k_scatter), waits until its own stores
+// have completed, then copies those same staging rows, row and record, to
+// their compact receive rows recv_base[d] + recv_psum[d][s] + j (as the copy
+// epilogue does): the epilogue's work is split by sending token instead of by
+// receive row, with the same reads and writes.  Whole rows in one pass.
+template <int CPL>
+__global__ void __launch_bounds__(kThreads) k_dispatch_fused(DispatchArgs a) {
+    const Shape &sh = a.sh;
+    const int lane = lane_id();
+    const int64_t n_tok = (int64_t)sh.S * sh.T;
+    const int nchunks = sh.row_bytes / 16;
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t g = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; g < n_tok; g += nwaves) {
+        const int s = (int)(g / sh.T), t = (int)(g - (int64_t)s * sh.T);
+        int e = -1, slot = -1, wbits = 0, recv_row0 = 0;
+        if (lane < sh.K) {
+            const int64_t e64 = a.topk_idx[g * sh.K + lane];
+            e = (e64 >= 0 && e64 < sh.E) ? (int)e64 : -1;
+            slot = a.dst_slot[g * sh.K + lane];
+            wbits = __float_as_int(a.topk_weights[g * sh.K + lane]);
+        }
+        const uint8_t *src = a.x + g * sh.row_bytes;
+        u32x4 v[CPL];
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+            const int c = q * kWave + lane;
+            if (c < nchunks) v[q] = ld16<EP_SCATTER_NT_LOAD>(src + (int64_t)c * 16);
+        }
+        const uint64_t owners = ballot(lane < sh.K && slot >= 0);
+        if (lane < sh.K && slot >= 0) {
+            const int d = rank_of(sh, e);
+            recv_row0 = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s];
+        }
+        for (uint64_t m = owners; m; m &= m - 1) {
+            const int k = __builtin_ctzll(m);
+            const int d = rank_of(sh, read_lane(e, k));
+            const int j = read_lane(slot, k) - row_base(sh, s) * sh.Nmax;
+            if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for a layout of this topk_idx
+            uint8_t *dst = a.staging_x + (staging_region(sh, d, s) * sh.Nmax + j) * sh.row_bytes;
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) {
+                const int c = q * kWave + lane;
+                if (c < nchunks) st16<EP_SCATTER_NT_STORE>(dst + (int64_t)c * 16, v[q]);
+            }
+        }
+        store_records(a, g, s, t, e, slot, wbits, owners, lane);
+        // The copy below reads what this wave has just stored: wait until its
+        // stores have completed (no other wave touches these staging rows).
+        __builtin_amdgcn_s_waitcnt(0);
+        for (uint64_t m = owners; m; m &= m - 1) {
+            const int k = __builtin_ctzll(m);
+            const int d = rank_of(sh, read_lane(e, k));
+            const int j = read_lane(slot, k) - row_base(sh, s) * sh.Nmax;
+            if ((unsigned)j >= (unsigned)sh.Nmax) continue;
+            const int64_t i = (int64_t)read_lane(recv_row0, k) + j;
+            if (i >= a.recv_capacity_rows) continue;
+            epilogue_row<CPL>(a, d, s, j, (int)i, lane, 0, nchunks);
+        }
     }
 }
 
@@ -690,7 +767,26 @@ struct EpilogueL {
     }
 };
 
+template <int CPL>
+struct FusedL {
+    static hipError_t run(const DispatchArgs &a, hipStream_t st) {
+        const int64_t tokens = (int64_t)a.sh.S * a.sh.T;
+        hipLaunchKernelGGL(k_dispatch_fused<CPL>, dim3(grid_for(tokens, EP_SCATTER_BLOCKS)), dim3(kThreads), 0, st, a);
+        return hipGetLastError();
+    }
+};
+
 }  // namespace
+
+bool dispatch_is_one_launch(const DispatchArgs &a) {
+    const int64_t tokens = (int64_t)a.sh.S * a.sh.T;
+    return !a.sh.expand && !a.sh.direct && tokens > 0 && tokens <= EP_FUSED_DISPATCH_MAX_TOKENS &&
+           a.sh.row_bytes <= EP_FUSED_DISPATCH_MAX_ROW;
+}
+
+hipError_t launch_dispatch_fused(const DispatchArgs &a, hipStream_t stream) {
+    return dispatch_cpl<FusedL>(chunks_per_lane(a.sh), a, stream);
+}
 
 hipError_t launch_scatter(const DispatchArgs &a, hipStream_t stream) {
     if ((int64_t)a.sh.S * a.sh.T == 0) return hipSuccess;

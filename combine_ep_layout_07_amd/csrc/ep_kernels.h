@@ -114,6 +114,9 @@ bool layout_is_one_launch(const LayoutArgs &a);
 // bytes) on the current device; looked up once per device, thread-safe.
 hipError_t no_alloc_scratch(void **ptr);
 hipError_t launch_scatter(const DispatchArgs &a, hipStream_t stream);
+// Both dispatch phases of a small compact-layout problem in one launch.
+bool dispatch_is_one_launch(const DispatchArgs &a);
+hipError_t launch_dispatch_fused(const DispatchArgs &a, hipStream_t stream);
 hipError_t launch_epilogue(const DispatchArgs &a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 

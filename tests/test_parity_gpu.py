@@ -457,6 +457,31 @@ def test_phases_split_equals_all():
     assert torch.equal(R1.recv_topk_idx[:n], R2.recv_topk_idx[:n])
 
 
+@pytest.mark.parametrize("w", [WORKLOADS[1], SMALL[7],
+                               Workload("hybrid_small_fused", S=6, T=80, H=128, K=6, E=24, R=6, Nmax=80, n_out=3),
+                               Workload("k32_fused", S=1, T=300, H=512, K=32, E=1024, R=64, Nmax=300)],
+                         ids=lambda w: w.name)
+def test_small_dispatch_one_launch_equals_two(w):
+    """A small compact-layout problem dispatches in one launch when both
+    phases are asked for; its staging rows, records, receive rows and
+    metadata equal those of the two phases enqueued separately, and the
+    oracle's (edge lanes included)."""
+    inputs = generate(w, 808, masked_frac=0.1, invalid_frac=0.02, dup_frac=0.2)
+    dev = upload(w, inputs)
+    say(f"[case] {w.name} one-launch dispatch")
+    cfg, L = run_layout(w, dev)
+    R1, R2 = ep.alloc_recv(cfg), ep.alloc_recv(cfg)
+    ep.ep_dispatch(cfg, dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_weights"], L, R1, ep.EP_PHASE_ALL)
+    ep.ep_dispatch(cfg, dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_weights"], L, R2, ep.EP_PHASE_SCATTER)
+    ep.ep_dispatch(cfg, dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_weights"], L, R2, ep.EP_PHASE_EPILOGUE)
+    torch.cuda.synchronize()
+    lay_o = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment, w.n_out)
+    want = oracle.dispatch(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.dtype == "fp8", False, 1, inputs["x"],
+                           inputs.get("x_sf"), inputs["topk_idx"], inputs["topk_weights"], lay_o, w.n_out)
+    compare_dispatch(w, lay_o, R1, want)
+    compare_dispatch(w, lay_o, R2, want)
+
+
 @pytest.mark.parametrize("cfg_id", [2, 3, 5])
 def test_identity_expert_round_trip(cfg_id):
     """dispatch -> identity expert -> combine gives bf16(sum(w) * x), any size."""
