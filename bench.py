@@ -232,9 +232,10 @@ def cpu_baseline(w, inputs, n_rows, v_rows, budget_s=10.0):
 
 
 COPY_CAL_BYTES = 256 * 2**20
+COPY_CAL_REPS = 5
 
 
-def copy_calibration(reps=5):
+def copy_calibration(reps=COPY_CAL_REPS):
     """A plain device-to-device copy of COPY_CAL_BYTES, the reference the HBM
     byte counters are scaled by (it reads and writes exactly that many bytes)."""
     import torch
@@ -289,13 +290,17 @@ def summarize_counters(fetch_csv: str, write_csv: str, bench_json: str, out_md: 
     b = _last_json(bench_json)
     alg = b["alg_bytes_per_step"]
 
-    def pick_largest(acc, key):
-        vals = [v for k, vs in acc.items() if key in k for v in vs]
-        return float(max(vals)) if vals else float("nan")
+    def calibration(path, counter):
+        # The calibration copies (torch's device-to-device copy runs the
+        # runtime's copyBuffer kernel) are the run's last COPY_CAL_REPS copy
+        # dispatches; earlier ones (the benchmark's own buffer copies) differ
+        # in size.  Median over them.
+        rows = [r for r in _counter_rows(path) if r.get("Counter_Name") == counter and "copyBuffer" in r["Kernel_Name"]]
+        rows.sort(key=lambda r: int(r.get("Dispatch_Id") or 0))
+        vals = [float(r["Counter_Value"]) for r in rows[-COPY_CAL_REPS:]]
+        return float(np.median(vals)) if vals else float("nan")
 
-    # The calibration copy (torch's device-to-device copy runs the runtime's
-    # copyBuffer kernel) is the largest copy dispatch of the run.
-    cf, cw = pick_largest(fetch, "copyBuffer"), pick_largest(write, "copyBuffer")
+    cf, cw = calibration(fetch_csv, "FETCH_SIZE"), calibration(write_csv, "WRITE_SIZE")
     f_scale = COPY_CAL_BYTES / (cf * 1024.0)
     w_scale = COPY_CAL_BYTES / (cw * 1024.0)
     lines = [

@@ -64,10 +64,10 @@ def test_source_digest_ignores_comments_only(tmp_path):
 
 def _counter_csv(path, counter, rows):
     with open(path, "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
         w.writeheader()
-        for name, value in rows:
-            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+        for i, (name, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
 
 
 def test_counter_summary_round_trip(tmp_path, monkeypatch):
@@ -84,10 +84,13 @@ def test_counter_summary_round_trip(tmp_path, monkeypatch):
     epi = "void ep::(anonymous namespace)::k_epilogue_pf<14>(ep::DispatchArgs, int)"
     comb = "void ep::(anonymous namespace)::k_combine<2>(ep::CombineArgs)"
     fetch, write, js = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "b.json"
-    # FETCH_SIZE reads half the copy's bytes (scale 2), WRITE_SIZE all of them (scale 1).
-    _counter_csv(fetch, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", cal_kib / 2), ("__amd_rocclr_copyBuffer", 4.0),
-                                       (epi, 1000.0), (epi, 1002.0), (comb, 500.0)])
-    _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", cal_kib), (epi, 3000.0), (comb, 100.0)])
+    # FETCH_SIZE reads half the copy's bytes (scale 2), WRITE_SIZE all of them (scale 1); the run's
+    # last five copies are the calibration, an earlier (larger) copy is the benchmark's own.
+    cal = [("__amd_rocclr_copyBuffer", None)] * bench.COPY_CAL_REPS
+    _counter_csv(fetch, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 3 * cal_kib), (epi, 1000.0), (epi, 1002.0),
+                                       (comb, 500.0)] + [(n, cal_kib / 2) for n, _ in cal])
+    _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 6 * cal_kib), (epi, 3000.0), (comb, 100.0)]
+                 + [(n, cal_kib) for n, _ in cal])
     js.write_text("[bench] progress\n" + json.dumps({
         "config": {"workload": "dsv3_share: test"},
         "alg_bytes_per_step": {"layout": 1, "scatter": 2, "epilogue": 5000 * 1024, "combine": 1100 * 1024}}) + "\n")
