@@ -91,6 +91,12 @@ __device__ __forceinline__ void fma_row(float (&acc)[CPL][8], const u32x4 (&v)[C
 // expand layout; the owner (lowest valid lane) of each rank otherwise, whose
 // weight becomes the lane-ordered fp32 sum over the lanes of its rank.
 // Returns the mask of row lanes; row / wrow hold each row lane's row and weight.
+// With EARLY_BASES, lane l < R fetches the base of source s in destination l's
+// receive rows together with the ids, so that no load waits for a decoded
+// rank: one dependent load fewer, which matters for short rows only (for
+// 14 KiB rows the four extra registers cost a wave per SIMD: measured 2-3%
+// slower at 4096 tokens, H = 7168).
+template <bool EARLY_BASES>
 __device__ __forceinline__ uint64_t token_rows(const CombineArgs &a, int64_t g, int lane, int &row, float &wrow) {
     const Shape &sh = a.sh;
     const int s = (int)(g / sh.T);
@@ -105,10 +111,9 @@ __device__ __forceinline__ uint64_t token_rows(const CombineArgs &a, int64_t g, 
         if (sh.expand) pos = a.expand_pos[g * sh.K + lane];
         else slot = a.dst_slot[g * sh.K + lane];
     }
-    // Lane l < R fetches the base of source s in destination l's receive
-    // rows together with the ids, so that no load waits for a decoded rank.
     int base_l = 0;
-    if (!sh.expand && lane < sh.R) base_l = a.recv_base[lane] + a.recv_psum[(int64_t)lane * (sh.S + 1) + s];
+    if (EARLY_BASES && !sh.expand && lane < sh.R)
+        base_l = a.recv_base[lane] + a.recv_psum[(int64_t)lane * (sh.S + 1) + s];
     const uint64_t vmask = ballot(valid);
     row = -1;
     wrow = 0.0f;
@@ -120,8 +125,12 @@ __device__ __forceinline__ uint64_t token_rows(const CombineArgs &a, int64_t g, 
         const uint64_t peers = match_key((uint32_t)d, sh.bits_R, vmask);
         const int owner = peers ? __builtin_ctzll(peers) : 0;
         const bool is_owner = valid && owner == lane;
-        const int base_d = shfl(base_l, d);
-        if (is_owner) row = base_d + (slot - row_base(sh, s) * sh.Nmax);
+        if (EARLY_BASES) {
+            const int base_d = shfl(base_l, d);
+            if (is_owner) row = base_d + (slot - row_base(sh, s) * sh.Nmax);
+        } else if (is_owner) {
+            row = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s] + (slot - row_base(sh, s) * sh.Nmax);
+        }
         for (uint64_t m = vmask; m; m &= m - 1) {
             const int k = __builtin_ctzll(m);
             const float wk = __int_as_float(read_lane(__float_as_int(w), k));
@@ -156,7 +165,7 @@ __global__ void __launch_bounds__(kThreads) k_combine(CombineArgs a) {
         if (c_lo >= c_hi) continue;
         int row;
         float wrow;
-        const uint64_t rows_mask = token_rows(a, g, lane, row, wrow);
+        const uint64_t rows_mask = token_rows<CPL == 1>(a, g, lane, row, wrow);
         const int wbits = __float_as_int(wrow);
         uint16_t *out = a.out + g * sh.H;
         for (int c0 = c_lo; c0 < c_hi; c0 += CPL * kWave) {

@@ -22,7 +22,7 @@ def _resource_remarks(src):
                                             "-Rpass-analysis=kernel-resource-usage"])
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
-    usage, name = {}, None
+    usage, occupancy, name = {}, {}, None
     for line in r.stderr.splitlines():
         m = re.search(r"remark:\s+Function Name: (\S+)", line)
         if m:
@@ -31,18 +31,42 @@ def _resource_remarks(src):
         m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
         if m and name:
             usage[name] = int(m.group(1))
-    return src, usage
+        m = re.search(r"remark:\s+Occupancy \[waves/SIMD\]: (\d+)", line)
+        if m and name:
+            occupancy[name] = int(m.group(1))
+    return src, (usage, occupancy)
 
 
 @pytest.fixture(scope="module")
-def scratch_by_kernel():
+def remarks_by_source():
     with cf.ThreadPoolExecutor(len(KERNEL_SOURCES)) as ex:
         return dict(ex.map(_resource_remarks, KERNEL_SOURCES))
 
 
 @pytest.mark.parametrize("src", KERNEL_SOURCES)
-def test_no_kernel_uses_scratch(scratch_by_kernel, src):
-    usage = scratch_by_kernel[src]
+def test_no_kernel_uses_scratch(remarks_by_source, src):
+    usage = remarks_by_source[src][0]
     assert usage, f"no kernel resource remarks for {src}"
     spilled = {k: v for k, v in usage.items() if v}
     assert not spilled, f"kernels using scratch memory in {src}: {spilled}"
+
+
+# Waves per SIMD the register allocation must leave to the streaming kernels
+# at the workloads' row sizes (14 KiB rows: 14 chunks per lane; the combine's
+# 2-chunk passes): measured optimum of each, a register increase that drops
+# one of them below it cost 2-3% (combine) or more.
+MIN_OCCUPANCY = {
+    ("ep_dispatch.hip", "k_scatterILi14E"): 4,
+    ("ep_dispatch.hip", "k_epilogue_pfILi14E"): 2,
+    ("ep_dispatch.hip", "k_epilogue_expandILi14E"): 4,
+    ("ep_combine.hip", "k_combineILi2E"): 4,
+}
+
+
+@pytest.mark.parametrize("src,kernel", sorted(MIN_OCCUPANCY))
+def test_streaming_kernels_keep_their_occupancy(remarks_by_source, src, kernel):
+    occ = remarks_by_source[src][1]
+    hits = {k: v for k, v in occ.items() if kernel in k}
+    assert hits, f"{kernel} not found in {src}"
+    for k, v in hits.items():
+        assert v >= MIN_OCCUPANCY[(src, kernel)], f"{k}: {v} waves per SIMD"
