@@ -22,7 +22,8 @@
  * Conventions for every call:
  *   - pointers named *_dev are device pointers the caller allocated (for
  *     example with torch.empty(..., device="cuda")); the library never
- *     allocates, frees or keeps state between calls;
+ *     allocates or frees, and keeps nothing between calls but the per-GPU
+ *     array of ep_layout_no_alloc and cached device properties;
  *   - all arrays are dense row-major; rows of x, staging and recv are 16-byte
  *     aligned (the base pointers must be 16-byte aligned, and the row size in
  *     bytes is a multiple of 16);
