@@ -1,7 +1,9 @@
 """Benchmark of the deterministic EP dispatch + combine hot path on one MI355X.
 
-One step = ep_layout + ep_dispatch (scatter + copy epilogue) + ep_combine over
-one batch of seeded synthetic input already resident in HBM.  The headline is
+One step = layout + dispatch (scatter + copy epilogue) + combine over one batch
+of seeded synthetic input already resident in HBM, enqueued as
+ep_layout_dispatch (ep_layout then ep_dispatch; one kernel for a small single
+source) and ep_combine.  The headline is
 the DeepSeek-V3-like share of the deterministic-dispatch page's benchmark
 (T=4096 tokens, hidden 7168 bf16, top-8 of 256 experts on 16 ranks, Nmax=4096,
 compact layout).  Prints ONE JSON line: effective HBM GB/s on the algorithmic
@@ -39,11 +41,12 @@ N_SETS = 2  # buffer sets the timed steps rotate over
 # stored HBM counters.
 STAGE_SOURCES = {
     "layout": ["ep_layout.hip", "ep_device.h", "ep_kernels.h"],
-    "scatter": ["ep_dispatch.hip", "ep_device.h", "ep_kernels.h"],
-    "epilogue": ["ep_dispatch.hip", "ep_device.h", "ep_kernels.h"],
+    "scatter": ["ep_dispatch.hip", "ep_rows.h", "ep_device.h", "ep_kernels.h"],
+    "epilogue": ["ep_dispatch.hip", "ep_rows.h", "ep_device.h", "ep_kernels.h"],
     "combine": ["ep_combine.hip", "ep_device.h", "ep_kernels.h"],
 }
-ALL_SOURCES = ["ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_api.cpp", "ep_device.h", "ep_kernels.h"]
+ALL_SOURCES = ["ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_api.cpp", "ep_device.h", "ep_kernels.h",
+               "ep_rows.h"]
 
 
 def alg_bytes(w, n_rows: int, v_rows: int, direct: bool = False, pad_rows: int = 0, n_bias: int = 0) -> dict:
@@ -496,8 +499,7 @@ def measure_workload(w, inputs, steps, warmup, direct=False, n_sets=N_SETS):
     }
 
     def step(b):
-        ep.ep_layout(cfg, topk, b.L, stream)
-        ep.ep_dispatch(cfg, b.x, b.x_sf, topk, wts, b.L, b.R, ep.EP_PHASE_ALL, stream)
+        ep.ep_layout_dispatch(cfg, b.x, b.x_sf, topk, wts, b.L, b.R, stream)
         ep.ep_combine(cfg, b.L, topk, wts, b.y, b.out, stream)
 
     for i in range(max(warmup, n_sets)):
@@ -602,8 +604,7 @@ def graph_replay(m, steps, warmup):
     with torch.cuda.stream(gs):
         for b in m["sets"]:
             def on(b=b):
-                ep.ep_layout(cfg, topk, b.L, gs)
-                ep.ep_dispatch(cfg, b.x, b.x_sf, topk, wts, b.L, b.R, ep.EP_PHASE_ALL, gs)
+                ep.ep_layout_dispatch(cfg, b.x, b.x_sf, topk, wts, b.L, b.R, gs)
                 ep.ep_combine(cfg, b.L, topk, wts, b.y, b.out, gs)
             on()
             torch.cuda.synchronize()
@@ -662,9 +663,10 @@ def measure_extras(steps: int, warmup: int) -> dict:
             ep.ep_layout(cfg, topk, b.L, stream)
 
         def step(b):
-            if name != "cached_layout":
-                ep.ep_layout(cfg, topk, b.L, stream)
-            ep.ep_dispatch(cfg, b.x, None, topk, wts, b.L, b.R, ep.EP_PHASE_ALL, stream)
+            if name == "cached_layout":
+                ep.ep_dispatch(cfg, b.x, None, topk, wts, b.L, b.R, ep.EP_PHASE_ALL, stream)
+            else:
+                ep.ep_layout_dispatch(cfg, b.x, None, topk, wts, b.L, b.R, stream)
             if name == "bias2":
                 ep.ep_combine_bias(cfg, b.L, topk, wts, b.y, bias[0], bias[1], b.out, stream)
             else:

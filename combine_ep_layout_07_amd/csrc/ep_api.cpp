@@ -154,16 +154,16 @@ int ep_query_sizes(const ep_config_t *cfg, ep_sizes_t *sz) {
 
 namespace {
 
-// ep_layout and ep_layout_no_alloc: the same launches on the caller's scratch
-// or on the library's own (own_scratch).
-int layout_call(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layout_t *layout, void *stream,
-                bool own_scratch) {
+// Validated launch arguments of a layout on the caller's scratch or on the
+// library's own (own_scratch).
+int make_layout_args(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layout_t *layout,
+                     bool own_scratch, ep::LayoutArgs *out) {
     ep::Shape sh;
     int rc = make_shape(cfg, &sh);
     if (rc != EP_OK) return rc;
     if ((rc = check_layout_ptrs(sh, layout, !own_scratch)) != EP_OK) return rc;
     if ((int64_t)sh.S * sh.T * sh.K > 0 && (!topk_idx_dev || !aligned(topk_idx_dev, 8))) return EP_ERR_INVALID_ARG;
-    ep::LayoutArgs a;
+    ep::LayoutArgs &a = *out;
     a.sh = sh;
     a.g = ep::layout_geometry(sh, cfg->num_layout_cus);
     void *scratch = layout->scratch_dev;
@@ -211,30 +211,26 @@ int layout_call(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_la
             a.spin_unit = 64;
         }
     }
+    return EP_OK;
+}
+
+int layout_call(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layout_t *layout, void *stream,
+                bool own_scratch) {
+    ep::LayoutArgs a;
+    const int rc = make_layout_args(cfg, topk_idx_dev, layout, own_scratch, &a);
+    if (rc != EP_OK) return rc;
     return ep::launch_layout(a, (hipStream_t)stream) == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 
-}  // namespace
-
-extern "C" {
-
-int ep_layout(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layout_t *layout, void *stream) {
-    return layout_call(cfg, topk_idx_dev, layout, stream, false);
-}
-
-int ep_layout_no_alloc(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layout_t *layout,
-                       void *stream) {
-    return layout_call(cfg, topk_idx_dev, layout, stream, true);
-}
-
-int ep_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev, const int64_t *topk_idx_dev,
-                const float *topk_weights_dev, const ep_layout_t *layout, const ep_recv_t *recv, int32_t phases,
-                void *stream) {
+// Validated launch arguments of a dispatch.
+int make_dispatch_args(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev, const int64_t *topk_idx_dev,
+                       const float *topk_weights_dev, const ep_layout_t *layout, const ep_recv_t *recv,
+                       ep::DispatchArgs *out) {
     ep::Shape sh;
     int rc = make_shape(cfg, &sh);
     if (rc != EP_OK) return rc;
     if ((rc = check_layout_ptrs(sh, layout)) != EP_OK) return rc;
-    if (!recv || phases < 1 || phases > EP_PHASE_ALL) return EP_ERR_INVALID_ARG;
+    if (!recv) return EP_ERR_INVALID_ARG;
     const bool tok = (int64_t)sh.S * sh.T > 0;
     if (tok) {
         if (!x_dev || !aligned(x_dev, 16) || !topk_idx_dev || !aligned(topk_idx_dev, 8) || !topk_weights_dev ||
@@ -252,7 +248,7 @@ int ep_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev
             return EP_ERR_INVALID_ARG;
     }
     if (recv->recv_capacity_rows < recv_rows(sh)) return EP_ERR_CAPACITY;
-    ep::DispatchArgs a;
+    ep::DispatchArgs &a = *out;
     a.sh = sh;
     a.x = static_cast<const uint8_t *>(x_dev);
     a.x_sf = x_sf_dev;
@@ -273,12 +269,54 @@ int ep_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev
     a.recv_topk_idx = recv->recv_topk_idx_dev;
     a.recv_topk_weights = recv->recv_topk_weights_dev;
     a.recv_capacity_rows = recv->recv_capacity_rows;
-    hipStream_t st = (hipStream_t)stream;
+    return EP_OK;
+}
+
+int dispatch_launches(const ep::DispatchArgs &a, int32_t phases, hipStream_t st) {
     if (phases == EP_PHASE_ALL && ep::dispatch_is_one_launch(a))
         return ep::launch_dispatch_fused(a, st) == hipSuccess ? EP_OK : EP_ERR_HIP;
     if ((phases & EP_PHASE_SCATTER) && ep::launch_scatter(a, st) != hipSuccess) return EP_ERR_HIP;
     if ((phases & EP_PHASE_EPILOGUE) && ep::launch_epilogue(a, st) != hipSuccess) return EP_ERR_HIP;
     return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_layout(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layout_t *layout, void *stream) {
+    return layout_call(cfg, topk_idx_dev, layout, stream, false);
+}
+
+int ep_layout_no_alloc(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layout_t *layout,
+                       void *stream) {
+    return layout_call(cfg, topk_idx_dev, layout, stream, true);
+}
+
+int ep_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev, const int64_t *topk_idx_dev,
+                const float *topk_weights_dev, const ep_layout_t *layout, const ep_recv_t *recv, int32_t phases,
+                void *stream) {
+    if (phases < 1 || phases > EP_PHASE_ALL) return EP_ERR_INVALID_ARG;
+    ep::DispatchArgs a;
+    const int rc = make_dispatch_args(cfg, x_dev, x_sf_dev, topk_idx_dev, topk_weights_dev, layout, recv, &a);
+    if (rc != EP_OK) return rc;
+    return dispatch_launches(a, phases, (hipStream_t)stream);
+}
+
+int ep_layout_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev,
+                       const int64_t *topk_idx_dev, const float *topk_weights_dev, const ep_layout_t *layout,
+                       const ep_recv_t *recv, void *stream) {
+    ep::LayoutArgs la;
+    int rc = make_layout_args(cfg, topk_idx_dev, layout, false, &la);
+    if (rc != EP_OK) return rc;
+    ep::DispatchArgs da;
+    if ((rc = make_dispatch_args(cfg, x_dev, x_sf_dev, topk_idx_dev, topk_weights_dev, layout, recv, &da)) != EP_OK)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (ep::layout_dispatch_is_one_launch(la, da))
+        return ep::launch_layout_dispatch(la, da, st) == hipSuccess ? EP_OK : EP_ERR_HIP;
+    if (ep::launch_layout(la, st) != hipSuccess) return EP_ERR_HIP;
+    return dispatch_launches(da, EP_PHASE_ALL, st);
 }
 
 int ep_combine(const ep_config_t *cfg, const ep_layout_t *layout, const int64_t *topk_idx_dev,

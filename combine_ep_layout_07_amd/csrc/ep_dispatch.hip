@@ -30,6 +30,7 @@
 
 #include "ep_device.h"
 #include "ep_kernels.h"
+#include "ep_rows.h"
 
 namespace ep {
 namespace {
@@ -37,26 +38,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
 
-// Cache hints of the streamed rows (1 = non-temporal: the row is touched once
-// by this kernel and not again soon).  Measured on MI355X at T=4096, H=7168:
-// non-temporal loads and stores in the copy epilogue keep its 770 MB stream
-// from leaving dirty or useless lines in L2 and the Infinity Cache, which
-// speeds up both the epilogue and the combine that follows; non-temporal
-// staging stores in the scatter slow the scatter down more than they help.
-#ifndef EP_SCATTER_NT_LOAD
-#define EP_SCATTER_NT_LOAD 0
-#endif
-#ifndef EP_SCATTER_NT_STORE
-#define EP_SCATTER_NT_STORE 0
-#endif
 #ifndef EP_DIRECT_NT_STORE
 #define EP_DIRECT_NT_STORE 1  // Direct Recv X rows: written once, read by the next stage at the earliest
-#endif
-#ifndef EP_EPILOGUE_NT_LOAD
-#define EP_EPILOGUE_NT_LOAD 1
-#endif
-#ifndef EP_EPILOGUE_NT_STORE
-#define EP_EPILOGUE_NT_STORE 1
 #endif
 #ifndef EP_SCATTER_SLICES
 #define EP_SCATTER_SLICES 1  // column slices of a token's row, each a separate work unit
@@ -113,46 +96,7 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #define EP_EXPAND_BLOCKS (1 << 20)
 #endif
 
-template <bool NT>
-__device__ __forceinline__ u32x4 ld16(const uint8_t *p) {
-    const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
-    if constexpr (NT) return __builtin_nontemporal_load(q);
-    else return *q;
-}
-template <bool NT>
-__device__ __forceinline__ void st16(uint8_t *p, u32x4 v) {
-    u32x4 *q = reinterpret_cast<u32x4 *>(p);
-    if constexpr (NT) __builtin_nontemporal_store(v, q);
-    else *q = v;
-}
-
 // ----------------------------------------------------------------- scatter
-// Scales and metadata record {t, expert ids, weight bits} of token g for the
-// staging row of every owner lane.  Metadata words i = lane and i = lane + 64
-// (K = 32 needs 65 words): word 0 = t, words 1..K = expert ids, words
-// K+1..2K = weight bits, shuffled with every lane active before any divergent
-// store.
-__device__ __forceinline__ void store_records(const DispatchArgs &a, int64_t g, int s, int t, int e, int slot,
-                                              int wbits, uint64_t owners, int lane) {
-    const Shape &sh = a.sh;
-    const int ev = shfl(e, lane >= 1 ? lane - 1 : 0);
-    const int wv = shfl(wbits, lane - 1 - sh.K >= 0 ? lane - 1 - sh.K : 0);
-    const int hi_src = lane + kWave - 1 - sh.K;
-    const int wv_hi = shfl(wbits, hi_src >= 0 && hi_src < kWave ? hi_src : 0);
-    const int word0 = lane == 0 ? t : (lane <= sh.K ? ev : wv);
-    for (uint64_t m = owners; m; m &= m - 1) {
-        const int k = __builtin_ctzll(m);
-        const int d = rank_of(sh, read_lane(e, k));
-        const int j = read_lane(slot, k) - row_base(sh, s) * sh.Nmax;
-        if ((unsigned)j >= (unsigned)sh.Nmax) continue;
-        const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
-        for (int i = lane; i < sh.sf_per_row; i += kWave)
-            a.staging_sf[row * sh.sf_per_row + i] = a.x_sf[g * sh.sf_per_row + i];
-        if (lane < sh.meta_words) a.staging_meta[row * sh.meta_words + lane] = word0;
-        if (lane + kWave < sh.meta_words) a.staging_meta[row * sh.meta_words + lane + kWave] = wv_hi;
-    }
-}
-
 // One wave per token (s, t): load the row once, store it to row
 // j = slot - row_base(s)*Nmax of source s's region in the staging rows of
 // every owner lane's destination d (with Direct Recv X, used here only for
@@ -361,42 +305,6 @@ __device__ __forceinline__ const int32_t *stage_tables(const DispatchArgs &a, in
 }
 
 // ------------------------------------------------- compact copy epilogue
-// Staging row (d, s, j) to compact receive row i = recv_base[d] +
-// recv_psum[d][s] + j: the hidden row, its scales, and the per-row metadata
-// derived from the record.
-template <int CPL>
-__device__ __forceinline__ void epilogue_row(const DispatchArgs &a, int d, int s, int j, int i, int lane, int c_lo,
-                                             int c_hi) {
-    const Shape &sh = a.sh;
-    const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
-    const uint8_t *src = a.staging_x + row * sh.row_bytes;
-    uint8_t *dst = a.recv_x + (int64_t)i * sh.row_bytes;
-    for (int c0 = c_lo; c0 < c_hi; c0 += CPL * kWave) {
-        u32x4 v[CPL];
-#pragma unroll
-        for (int q = 0; q < CPL; ++q) {
-            const int c = c0 + q * kWave + lane;
-            if (c < c_hi) v[q] = ld16<EP_EPILOGUE_NT_LOAD>(src + (int64_t)c * 16);
-        }
-#pragma unroll
-        for (int q = 0; q < CPL; ++q) {
-            const int c = c0 + q * kWave + lane;
-            if (c < c_hi) st16<EP_EPILOGUE_NT_STORE>(dst + (int64_t)c * 16, v[q]);
-        }
-    }
-    if (c_lo != 0) return;  // slice 0 also moves the scales and the metadata
-    for (int q = lane; q < sh.sf_per_row; q += kWave)
-        a.recv_sf[(int64_t)i * sh.sf_per_row + q] = a.staging_sf[row * sh.sf_per_row + q];
-    const int32_t *meta = a.staging_meta + row * sh.meta_words;
-    const int t = meta[0];
-    if (lane == 0) a.recv_src_idx[i] = s * sh.T + t;
-    for (int k = lane; k < sh.K; k += kWave) {
-        const int e = meta[1 + k];
-        const bool on_d = (unsigned)e < (unsigned)sh.E && rank_of(sh, e) == d;
-        a.recv_topk_idx[(int64_t)i * sh.K + k] = on_d ? e - d * sh.El : -1;
-        a.recv_topk_weights[(int64_t)i * sh.K + k] = on_d ? __int_as_float(meta[1 + sh.K + k]) : 0.0f;
-    }
-}
 
 // ------------------------------------------ small dispatch, one launch
 // Scatter and copy epilogue of a small compact-layout problem in one launch:
@@ -416,13 +324,17 @@ __global__ void __launch_bounds__(kThreads) k_dispatch_fused(DispatchArgs a) {
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
     for (int64_t g = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; g < n_tok; g += nwaves) {
         const int s = (int)(g / sh.T), t = (int)(g - (int64_t)s * sh.T);
-        int e = -1, slot = -1, wbits = 0, recv_row0 = 0;
+        int e = -1, slot = -1, wbits = 0;
         if (lane < sh.K) {
             const int64_t e64 = a.topk_idx[g * sh.K + lane];
             e = (e64 >= 0 && e64 < sh.E) ? (int)e64 : -1;
             slot = a.dst_slot[g * sh.K + lane];
             wbits = __float_as_int(a.topk_weights[g * sh.K + lane]);
         }
+        // Lane l < R fetches source s's first compact receive row in
+        // destination l with the ids, so that no load waits for a rank.
+        int base_l = 0;
+        if (lane < sh.R) base_l = a.recv_base[lane] + a.recv_psum[(int64_t)lane * (sh.S + 1) + s];
         const uint8_t *src = a.x + g * sh.row_bytes;
         u32x4 v[CPL];
 #pragma unroll
@@ -431,10 +343,7 @@ __global__ void __launch_bounds__(kThreads) k_dispatch_fused(DispatchArgs a) {
             if (c < nchunks) v[q] = ld16<EP_SCATTER_NT_LOAD>(src + (int64_t)c * 16);
         }
         const uint64_t owners = ballot(lane < sh.K && slot >= 0);
-        if (lane < sh.K && slot >= 0) {
-            const int d = rank_of(sh, e);
-            recv_row0 = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s];
-        }
+        const int recv_row0 = shfl(base_l, e >= 0 ? rank_of(sh, e) : 0);
         for (uint64_t m = owners; m; m &= m - 1) {
             const int k = __builtin_ctzll(m);
             const int d = rank_of(sh, read_lane(e, k));
@@ -458,7 +367,7 @@ __global__ void __launch_bounds__(kThreads) k_dispatch_fused(DispatchArgs a) {
             if ((unsigned)j >= (unsigned)sh.Nmax) continue;
             const int64_t i = (int64_t)read_lane(recv_row0, k) + j;
             if (i >= a.recv_capacity_rows) continue;
-            epilogue_row<CPL>(a, d, s, j, (int)i, lane, 0, nchunks);
+            epilogue_row_one_pass<CPL>(a, d, s, j, (int)i, lane);
         }
     }
 }

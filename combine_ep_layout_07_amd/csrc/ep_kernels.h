@@ -117,6 +117,9 @@ hipError_t launch_scatter(const DispatchArgs &a, hipStream_t stream);
 // Both dispatch phases of a small compact-layout problem in one launch.
 bool dispatch_is_one_launch(const DispatchArgs &a);
 hipError_t launch_dispatch_fused(const DispatchArgs &a, hipStream_t stream);
+// Layout and both dispatch phases of one small source in one launch.
+bool layout_dispatch_is_one_launch(const LayoutArgs &a, const DispatchArgs &da);
+hipError_t launch_layout_dispatch(const LayoutArgs &a, const DispatchArgs &da, hipStream_t stream);
 hipError_t launch_epilogue(const DispatchArgs &a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 

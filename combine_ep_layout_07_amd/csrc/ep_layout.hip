@@ -46,6 +46,7 @@
 #include "ep.h"
 #include "ep_device.h"
 #include "ep_kernels.h"
+#include "ep_rows.h"
 
 namespace ep {
 
@@ -915,6 +916,151 @@ __global__ void __launch_bounds__(NW * kWave) k_layout_single(LayoutArgs a) {
     rank_items(a, expand, 0, t0, t1, c, first, one_batch, cnt_d + w * R, cnt_e + w * E);
 }
 
+// ------------------------------------------ layout and dispatch, one launch
+// The pages' dispatch replays the slots its prologue computed ([DET]
+// Approach); for one small source (compact layout) both run in one launch.
+// Every workgroup computes the whole layout of the source in LDS, exactly as
+// k_layout_single does (a few hundred items: cheaper than a second launch);
+// workgroup 0 alone writes the tables to memory.  Then each workgroup
+// dispatches its own NW tokens, one wave per token, as k_dispatch_fused does:
+// the token's row (loaded before the layout work, so its latency overlaps
+// it) and record go to the staging rows of its destinations, and once the
+// wave's stores have completed it copies those staging rows to their compact
+// receive rows.  The slots of the workgroup's tokens come from LDS.
+template <int NW, int CPL>
+__global__ void __launch_bounds__(NW * kWave) k_layout_dispatch_small(LayoutArgs a, DispatchArgs da) {
+    constexpr int NT = NW * kWave;
+    const Shape &sh = a.sh;
+    const int w = threadIdx.x / kWave, tid = threadIdx.x, lane = lane_id();
+    const int R = sh.R, E = sh.E, K = sh.K;
+    const bool writer = blockIdx.x == 0;
+    extern __shared__ int lds[];
+    int *cnt_d = lds;               // [NW][R] per-wave counts, then running bases
+    int *cnt_e = cnt_d + NW * R;    // [NW][E]
+    int *zero_d = cnt_e + NW * E;   // [R]    the base per destination: 0
+    int *part = zero_d + R + E;     // [NT]   totals per destination
+    int *flag = part + NT;          // [NW]
+    int *rbase = flag + NW;         // [R]    first compact receive row of each destination
+    int *slots = rbase + R;         // [NW][K] slots of this workgroup's tokens
+
+    // This workgroup's tokens, one per wave: issue the token's loads first.
+    const int g0 = blockIdx.x * NW;
+    const int g = g0 + w;
+    const bool has_tok = g < sh.T;
+    const int nchunks = sh.row_bytes / 16;
+    u32x4 v[CPL];
+    int e = -1, wbits = 0;
+    if (has_tok) {
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+            const int c = q * kWave + lane;
+            if (c < nchunks) v[q] = ld16<EP_SCATTER_NT_LOAD>(da.x + (int64_t)g * sh.row_bytes + (int64_t)c * 16);
+        }
+        if (lane < K) {
+            const int64_t e64 = a.topk_idx[(int64_t)g * K + lane];
+            e = (e64 >= 0 && e64 < sh.E) ? (int)e64 : -1;
+            wbits = __float_as_int(da.topk_weights[(int64_t)g * K + lane]);
+        }
+    }
+
+    // The layout of the whole source (k_layout_single's steps).
+    const int cw = (sh.T + NW - 1) / NW;
+    const int t0 = min(w * cw, sh.T), t1 = min(t0 + cw, sh.T);
+    const StepCtx c = make_ctx(K);
+    const bool one_batch = t1 - t0 <= kBatch * c.tps;
+    int64_t first[kBatch] = {};
+    if (one_batch) load_batch(sh, a.topk_idx, t0, t1, c, first);
+    for (int i = tid; i < NW * (R + E) + R; i += NT) lds[i] = 0;
+    for (int i = tid; i < NW * K; i += NT) slots[i] = -1;
+    __syncthreads();
+    const bool bad = wave_count(sh, a.topk_idx, t0, t1, cnt_d + w * R, cnt_e + w * E, true, c, first, one_batch);
+    if (lane_id() == 0) flag[w] = bad ? 1 : 0;
+    __syncthreads();
+    for (int d = tid; d < R; d += NT) {
+        int tot = 0;
+        for (int q = 0; q < NW; ++q) tot += cnt_d[q * R + d];
+        part[d] = tot;
+        if (writer) {
+            a.tokens_per_rank[d] = tot;
+            a.recv_psum[2 * d] = 0;
+            a.recv_psum[2 * d + 1] = tot;
+        }
+    }
+    if (writer) {
+        for (int ex = tid; ex < E; ex += NT) {
+            int tot = 0;
+            for (int q = 0; q < NW; ++q) tot += cnt_e[q * E + ex];
+            a.tokens_per_expert[ex] = tot;
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int d = 0; d < R; ++d) {
+            rbase[d] = run;
+            run += part[d];
+        }
+        if (writer) {
+            for (int d = 0; d < R; ++d) a.recv_base[d] = rbase[d];
+            a.recv_base[R] = run;
+            int any = 0;
+            for (int q = 0; q < NW; ++q) any |= flag[q];
+            a.error_flags[0] = any ? 1 : 0;
+        }
+    }
+    wave_bases<NW>(cnt_d, R, zero_d);
+    __syncthreads();
+    {
+        int *run_d = cnt_d + w * R;
+        walk_steps(sh, a.topk_idx, t0, t1, c, first, one_batch, false, [&](const Item &it) {
+            const int rd = it.owner ? run_d[it.d] : 0;
+            if (it.in) {
+                const int slot = it.owner ? rd + it.rank_d : -1;  // row base 0: one source
+                if (writer) a.dst_slot[(int64_t)it.t * K + it.k] = slot;
+                if (it.t >= g0 && it.t < g0 + NW) slots[(it.t - g0) * K + it.k] = slot;
+            }
+            if (it.last_d) run_d[it.d] = rd + it.rank_d + 1;
+        });
+    }
+    __syncthreads();
+    if (!has_tok) return;
+
+    // Dispatch of token g: staging rows and record, then its receive rows.
+    const int slot = lane < K ? slots[w * K + lane] : -1;
+    const uint64_t owners = ballot(lane < K && slot >= 0);
+    for (uint64_t m = owners; m; m &= m - 1) {
+        const int k = __builtin_ctzll(m);
+        const int d = rank_of(sh, read_lane(e, k));
+        const int j = read_lane(slot, k);
+        if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true: j < T <= Nmax
+        uint8_t *dst = da.staging_x + ((int64_t)d * sh.Nmax + j) * sh.row_bytes;
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+            const int cc = q * kWave + lane;
+            if (cc < nchunks) st16<EP_SCATTER_NT_STORE>(dst + (int64_t)cc * 16, v[q]);
+        }
+    }
+    store_records(da, g, 0, g, e, slot, wbits, owners, lane);
+    // The copy below reads what this wave has just stored (no other wave
+    // touches these staging rows): wait until its stores have completed.
+    __builtin_amdgcn_s_waitcnt(0);
+    for (uint64_t m = owners; m; m &= m - 1) {
+        const int k = __builtin_ctzll(m);
+        const int d = rank_of(sh, read_lane(e, k));
+        const int j = read_lane(slot, k);
+        if ((unsigned)j >= (unsigned)sh.Nmax) continue;
+        const int64_t i = (int64_t)rbase[d] + j;
+        if (i >= da.recv_capacity_rows) continue;
+        epilogue_row_one_pass<CPL>(da, d, 0, j, (int)i, lane);
+    }
+}
+
+constexpr int kSmallWaves = 16;  // waves per workgroup of k_layout_dispatch_small
+
+size_t small_dispatch_lds_bytes(const Shape &sh) {
+    return single_lds_bytes(sh, kSmallWaves) + sizeof(int) * ((size_t)sh.R + (size_t)kSmallWaves * sh.K);
+}
+
 size_t count_lds_bytes(const Shape &sh) {
     return sizeof(int) * ((size_t)kLayoutWaves * (sh.R + sh.E) + kLayoutWaves);
 }
@@ -951,6 +1097,20 @@ bool layout_is_one_launch(const LayoutArgs &a) {
     if (a.sh.expand || a.g.single || !a.one_launch) return false;
     const int64_t grid = ((int64_t)a.g.blocks_per_src + 1) * a.sh.S;
     return grid <= fused_capacity(slot_lds_bytes(a.sh));
+}
+
+bool layout_dispatch_is_one_launch(const LayoutArgs &a, const DispatchArgs &da) {
+    const Shape &sh = a.sh;
+    return sh.S == 1 && !sh.expand && !sh.direct && sh.T > 0 &&
+           (int64_t)sh.T * sh.K <= EP_LAYOUT_SINGLE_MAX_ITEMS && sh.row_bytes <= kWave * 16 &&
+           small_dispatch_lds_bytes(sh) <= 65536 && da.recv_capacity_rows >= (int64_t)sh.T * (sh.K < sh.R ? sh.K : sh.R);
+}
+
+hipError_t launch_layout_dispatch(const LayoutArgs &a, const DispatchArgs &da, hipStream_t stream) {
+    const int blocks = (a.sh.T + kSmallWaves - 1) / kSmallWaves;
+    hipLaunchKernelGGL((k_layout_dispatch_small<kSmallWaves, 1>), dim3(blocks), dim3(kSmallWaves * kWave),
+                       small_dispatch_lds_bytes(a.sh), stream, a, da);
+    return hipGetLastError();
 }
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {

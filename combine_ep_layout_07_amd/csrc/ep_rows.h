@@ -1,0 +1,151 @@
+// ep_rows.h -- row-copy helpers shared by the dispatch kernels (scatter, copy
+// epilogue) and the layout-and-dispatch kernel of small problems: 16-byte
+// loads and stores with cache hints, the staging record of a token, and the
+// copy of one staging row to its compact receive row.
+#pragma once
+
+#include "ep_device.h"
+#include "ep_kernels.h"
+
+namespace ep {
+
+// Cache hints of the streamed rows (1 = non-temporal: the row is touched once
+// by this kernel and not again soon).  Measured on MI355X at T=4096, H=7168:
+// non-temporal loads and stores in the copy epilogue keep its 770 MB stream
+// from leaving dirty or useless lines in L2 and the Infinity Cache, which
+// speeds up both the epilogue and the combine that follows; non-temporal
+// staging stores in the scatter slow the scatter down more than they help.
+#ifndef EP_SCATTER_NT_LOAD
+#define EP_SCATTER_NT_LOAD 0
+#endif
+#ifndef EP_SCATTER_NT_STORE
+#define EP_SCATTER_NT_STORE 0
+#endif
+#ifndef EP_EPILOGUE_NT_LOAD
+#define EP_EPILOGUE_NT_LOAD 1
+#endif
+#ifndef EP_EPILOGUE_NT_STORE
+#define EP_EPILOGUE_NT_STORE 1
+#endif
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const uint8_t *p) {
+    const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+    if constexpr (NT) return __builtin_nontemporal_load(q);
+    else return *q;
+}
+template <bool NT>
+__device__ __forceinline__ void st16(uint8_t *p, u32x4 v) {
+    u32x4 *q = reinterpret_cast<u32x4 *>(p);
+    if constexpr (NT) __builtin_nontemporal_store(v, q);
+    else *q = v;
+}
+
+// Scales and metadata record {t, expert ids, weight bits} of token g for the
+// staging row of every owner lane.  Metadata words i = lane and i = lane + 64
+// (K = 32 needs 65 words): word 0 = t, words 1..K = expert ids, words
+// K+1..2K = weight bits, shuffled with every lane active before any divergent
+// store.
+__device__ __forceinline__ void store_records(const DispatchArgs &a, int64_t g, int s, int t, int e, int slot,
+                                              int wbits, uint64_t owners, int lane) {
+    const Shape &sh = a.sh;
+    const int ev = shfl(e, lane >= 1 ? lane - 1 : 0);
+    const int wv = shfl(wbits, lane - 1 - sh.K >= 0 ? lane - 1 - sh.K : 0);
+    const int hi_src = lane + kWave - 1 - sh.K;
+    const int wv_hi = shfl(wbits, hi_src >= 0 && hi_src < kWave ? hi_src : 0);
+    const int word0 = lane == 0 ? t : (lane <= sh.K ? ev : wv);
+    for (uint64_t m = owners; m; m &= m - 1) {
+        const int k = __builtin_ctzll(m);
+        const int d = rank_of(sh, read_lane(e, k));
+        const int j = read_lane(slot, k) - row_base(sh, s) * sh.Nmax;
+        if ((unsigned)j >= (unsigned)sh.Nmax) continue;
+        const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
+        for (int i = lane; i < sh.sf_per_row; i += kWave)
+            a.staging_sf[row * sh.sf_per_row + i] = a.x_sf[g * sh.sf_per_row + i];
+        if (lane < sh.meta_words) a.staging_meta[row * sh.meta_words + lane] = word0;
+        if (lane + kWave < sh.meta_words) a.staging_meta[row * sh.meta_words + lane + kWave] = wv_hi;
+    }
+}
+
+// Staging row (d, s, j) to compact receive row i = recv_base[d] +
+// recv_psum[d][s] + j: the hidden row, its scales, and the per-row metadata
+// derived from the record.
+template <int CPL>
+__device__ __forceinline__ void epilogue_row(const DispatchArgs &a, int d, int s, int j, int i, int lane, int c_lo,
+                                             int c_hi) {
+    const Shape &sh = a.sh;
+    const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
+    const uint8_t *src = a.staging_x + row * sh.row_bytes;
+    uint8_t *dst = a.recv_x + (int64_t)i * sh.row_bytes;
+    for (int c0 = c_lo; c0 < c_hi; c0 += CPL * kWave) {
+        u32x4 v[CPL];
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+            const int c = c0 + q * kWave + lane;
+            if (c < c_hi) v[q] = ld16<EP_EPILOGUE_NT_LOAD>(src + (int64_t)c * 16);
+        }
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+            const int c = c0 + q * kWave + lane;
+            if (c < c_hi) st16<EP_EPILOGUE_NT_STORE>(dst + (int64_t)c * 16, v[q]);
+        }
+    }
+    if (c_lo != 0) return;  // slice 0 also moves the scales and the metadata
+    for (int q = lane; q < sh.sf_per_row; q += kWave)
+        a.recv_sf[(int64_t)i * sh.sf_per_row + q] = a.staging_sf[row * sh.sf_per_row + q];
+    const int32_t *meta = a.staging_meta + row * sh.meta_words;
+    const int t = meta[0];
+    if (lane == 0) a.recv_src_idx[i] = s * sh.T + t;
+    for (int k = lane; k < sh.K; k += kWave) {
+        const int e = meta[1 + k];
+        const bool on_d = (unsigned)e < (unsigned)sh.E && rank_of(sh, e) == d;
+        a.recv_topk_idx[(int64_t)i * sh.K + k] = on_d ? e - d * sh.El : -1;
+        a.recv_topk_weights[(int64_t)i * sh.K + k] = on_d ? __int_as_float(meta[1 + sh.K + k]) : 0.0f;
+    }
+}
+
+// The same copy for a row of one pass (nchunks <= 64 * CPL, scales <= 128)
+// with every load — the row, its scales and its record — issued before the
+// first store: one dependent memory latency in all.  For the small-problem
+// kernels, whose cost is their chain of latencies.
+template <int CPL>
+__device__ __forceinline__ void epilogue_row_one_pass(const DispatchArgs &a, int d, int s, int j, int i, int lane) {
+    const Shape &sh = a.sh;
+    const int nchunks = sh.row_bytes / 16;
+    const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
+    const uint8_t *src = a.staging_x + row * sh.row_bytes;
+    const int32_t *meta = a.staging_meta + row * sh.meta_words;
+    u32x4 v[CPL];
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+        const int c = q * kWave + lane;
+        if (c < nchunks) v[q] = ld16<EP_EPILOGUE_NT_LOAD>(src + (int64_t)c * 16);
+    }
+    float sf[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        if (lane + h * kWave < sh.sf_per_row) sf[h] = a.staging_sf[row * sh.sf_per_row + lane + h * kWave];
+    const int t = meta[0];
+    int e = -1, wbits = 0;
+    if (lane < sh.K) {
+        e = meta[1 + lane];
+        wbits = meta[1 + sh.K + lane];
+    }
+    uint8_t *dst = a.recv_x + (int64_t)i * sh.row_bytes;
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+        const int c = q * kWave + lane;
+        if (c < nchunks) st16<EP_EPILOGUE_NT_STORE>(dst + (int64_t)c * 16, v[q]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        if (lane + h * kWave < sh.sf_per_row) a.recv_sf[(int64_t)i * sh.sf_per_row + lane + h * kWave] = sf[h];
+    if (lane == 0) a.recv_src_idx[i] = s * sh.T + t;
+    if (lane < sh.K) {
+        const bool on_d = (unsigned)e < (unsigned)sh.E && rank_of(sh, e) == d;
+        a.recv_topk_idx[(int64_t)i * sh.K + lane] = on_d ? e - d * sh.El : -1;
+        a.recv_topk_weights[(int64_t)i * sh.K + lane] = on_d ? __int_as_float(wbits) : 0.0f;
+    }
+}
+
+}  // namespace ep

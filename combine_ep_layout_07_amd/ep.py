@@ -72,10 +72,12 @@ def _load():
     lib.ep_layout_no_alloc.argtypes = [ctypes.POINTER(EpConfig), P, ctypes.POINTER(EpLayoutT), P]
     lib.ep_dispatch.argtypes = [ctypes.POINTER(EpConfig), P, P, P, P, ctypes.POINTER(EpLayoutT),
                                 ctypes.POINTER(EpRecvT), ctypes.c_int32, P]
+    lib.ep_layout_dispatch.argtypes = [ctypes.POINTER(EpConfig), P, P, P, P, ctypes.POINTER(EpLayoutT),
+                                       ctypes.POINTER(EpRecvT), P]
     lib.ep_combine.argtypes = [ctypes.POINTER(EpConfig), ctypes.POINTER(EpLayoutT), P, P, P, P, P]
     lib.ep_combine_bias.argtypes = [ctypes.POINTER(EpConfig), ctypes.POINTER(EpLayoutT), P, P, P, P, P, P, P]
-    for f in ("ep_query_sizes", "ep_layout", "ep_layout_no_alloc", "ep_dispatch", "ep_combine", "ep_combine_bias",
-              "ep_version"):
+    for f in ("ep_query_sizes", "ep_layout", "ep_layout_no_alloc", "ep_dispatch", "ep_layout_dispatch", "ep_combine",
+              "ep_combine_bias", "ep_version"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ep_status_string.argtypes = [ctypes.c_int]
     lib.ep_status_string.restype = ctypes.c_char_p
@@ -264,6 +266,25 @@ def ep_dispatch(cfg: EpConfig, x: torch.Tensor, x_sf: Optional[torch.Tensor], to
                           ctypes.byref(layout.struct), ctypes.byref(recv.struct), int(phases), _stream(stream))
     if rc != EP_OK:
         raise EpError(rc, "ep_dispatch")
+
+
+def ep_layout_dispatch(cfg: EpConfig, x: torch.Tensor, x_sf: Optional[torch.Tensor], topk_idx: torch.Tensor,
+                       topk_weights: torch.Tensor, layout: LayoutBuffers, recv: RecvBuffers, stream=None) -> None:
+    """ep_layout then ep_dispatch (both phases) in one call; one kernel for small single sources."""
+    S, T, K, H = cfg.num_src_ranks, cfg.num_tokens, cfg.num_topk, cfg.hidden
+    fp8 = cfg.x_dtype == EP_DTYPE_FP8_E4M3FN
+    rw = H if fp8 else 2 * H
+    if topk_weights.dtype != torch.float32 or topk_idx.dtype != torch.int64:
+        raise ValueError("topk_idx must be int64 and topk_weights float32")
+    _check_elem(x, "x", 1 if fp8 else 2)
+    _check_elem(x_sf, "x_sf", 4)
+    rc = _lib.ep_layout_dispatch(ctypes.byref(cfg), _ptr(x, "x", S * T * rw),
+                                 _ptr(x_sf, "x_sf", S * T * (H // 128) * 4 if fp8 else 0),
+                                 _ptr(topk_idx, "topk_idx", S * T * K * 8),
+                                 _ptr(topk_weights, "topk_weights", S * T * K * 4),
+                                 ctypes.byref(layout.struct), ctypes.byref(recv.struct), _stream(stream))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_layout_dispatch")
 
 
 def ep_combine(cfg: EpConfig, layout: LayoutBuffers, topk_idx: torch.Tensor, topk_weights: torch.Tensor,

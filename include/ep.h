@@ -259,6 +259,18 @@ int ep_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev
                 const int64_t *topk_idx_dev, const float *topk_weights_dev,
                 const ep_layout_t *layout, const ep_recv_t *recv, int32_t phases, void *stream);
 
+/* Layout and dispatch in one call: ep_layout followed by ep_dispatch with
+ * EP_PHASE_ALL, with the same arguments, checks and results (the pages'
+ * dispatch runs its deterministic prologue itself when no cached handle is
+ * given, [DET] Approach and New API).  For one small source in the compact
+ * layout (T*K <= 2048, rows of at most 1 KiB, no Direct Recv X) everything
+ * runs as one kernel: each workgroup lays out the whole source in LDS and
+ * dispatches its share of the tokens; otherwise the layout's and the
+ * dispatch's launches are enqueued as the two calls would. */
+int ep_layout_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev,
+                       const int64_t *topk_idx_dev, const float *topk_weights_dev, const ep_layout_t *layout,
+                       const ep_recv_t *recv, void *stream);
+
 /* Combine ([UNO] Changes: the reduce epilogue brings expert outputs back to
  * token order): out[s][t] = bf16(sum over valid lanes k of w[s][t][k] *
  * Y(s,t,k)), accumulated in fp32 and rounded to nearest-even once.  Y is, in

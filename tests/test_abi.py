@@ -35,8 +35,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_combine", "ep_combine_bias",
-                     "ep_status_string"):
+    for required in ("ep_query_sizes", "ep_layout", "ep_layout_no_alloc", "ep_dispatch", "ep_layout_dispatch",
+                     "ep_combine", "ep_combine_bias", "ep_status_string"):
         assert required in names
 
 
@@ -131,6 +131,11 @@ def test_calls_reject_bad_arguments_before_any_launch():
         ep.EP_ERR_INVALID_ARG
     bad = ep.make_config(1, 16, 64, 2, 8, 4, 8)  # Nmax < T
     assert ep._lib.ep_layout(ctypes.byref(bad), None, ctypes.byref(L), None) == ep.EP_ERR_CAPACITY
+    # the combined call checks both calls' arguments before anything runs
+    assert ep._lib.ep_layout_dispatch(ctypes.byref(bad), None, None, None, None, ctypes.byref(L), ctypes.byref(R),
+                                      None) == ep.EP_ERR_CAPACITY
+    assert ep._lib.ep_layout_dispatch(ctypes.byref(cfg), None, None, None, None, ctypes.byref(L), ctypes.byref(R),
+                                      None) == ep.EP_ERR_INVALID_ARG
 
 
 @fake_pointers

@@ -76,7 +76,7 @@ def test_counter_summary_round_trip(tmp_path, monkeypatch):
     kernel's sources (not by a comment)."""
     csrc = tmp_path / "csrc"
     csrc.mkdir()
-    for f in ("ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_device.h", "ep_kernels.h"):
+    for f in ("ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_device.h", "ep_kernels.h", "ep_rows.h"):
         (csrc / f).write_text("int k;\n")
     monkeypatch.setattr(bench, "CSRC", str(csrc))
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))

@@ -482,6 +482,40 @@ def test_small_dispatch_one_launch_equals_two(w):
     compare_dispatch(w, lay_o, R2, want)
 
 
+LAYOUT_DISPATCH = [WORKLOADS[1], SMALL[1], Workload("one_token", S=1, T=1, H=64, K=4, E=16, R=4, Nmax=1),
+                   Workload("fp8_single", S=1, T=200, H=512, K=6, E=48, R=12, Nmax=205, dtype="fp8"),
+                   Workload("k32_single", S=1, T=64, H=512, K=32, E=512, R=64, Nmax=64),
+                   Workload("ragged_16x", S=1, T=131, H=128, K=8, E=64, R=16, Nmax=131),
+                   WORKLOADS[2], WORKLOADS[5].with_(name="expand_quarter", S=4)]
+
+
+@pytest.mark.parametrize("w", LAYOUT_DISPATCH, ids=lambda w: w.name)
+def test_layout_dispatch_in_one_call(w):
+    """ep_layout_dispatch (one kernel for one small source in the compact
+    layout, the two calls' launches otherwise) gives the same tables, staging
+    rows, records, receive rows and metadata as ep_layout + ep_dispatch, and
+    the oracle's (edge lanes included)."""
+    inputs = generate(w, 909, masked_frac=0.1, invalid_frac=0.02, dup_frac=0.2)
+    dev = upload(w, inputs)
+    say(f"[case] {w.name} ep_layout_dispatch")
+    cfg = ep.config_for(w)
+    L1, R1 = ep.alloc_layout(cfg), ep.alloc_recv(cfg)
+    for t in L1.tables().values():
+        t.fill_(-7)
+    ep.ep_layout_dispatch(cfg, dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_weights"], L1, R1)
+    L2, R2 = ep.alloc_layout(cfg), ep.alloc_recv(cfg)
+    ep.ep_layout(cfg, dev["topk_idx"], L2)
+    ep.ep_dispatch(cfg, dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_weights"], L2, R2)
+    torch.cuda.synchronize()
+    lay_o = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment, w.n_out)
+    compare_tables(layout_host(L1), lay_o)
+    compare_tables(layout_host(L2), lay_o)
+    want = oracle.dispatch(w.S, w.T, w.H, w.K, w.E, w.R, w.Nmax, w.dtype == "fp8", w.expand, w.alignment,
+                           inputs["x"], inputs.get("x_sf"), inputs["topk_idx"], inputs["topk_weights"], lay_o, w.n_out)
+    compare_dispatch(w, lay_o, R1, want)
+    compare_dispatch(w, lay_o, R2, want)
+
+
 @pytest.mark.parametrize("cfg_id", [2, 3, 5])
 def test_identity_expert_round_trip(cfg_id):
     """dispatch -> identity expert -> combine gives bf16(sum(w) * x), any size."""
