@@ -17,11 +17,11 @@ from combine_ep_layout_07_amd.workloads import WORKLOADS, Workload, generate, se
 from tests.gpu_harness import compare_tables, layout_host, say  # noqa: E402
 
 
-def _layout_both(w, seed, num_layout_cus=0):
+def _layout_both(w, seed, num_layout_cus=0, one_launch=False):
     inputs = generate(w, seed, with_x=False, masked_frac=0.1, invalid_frac=0.01, dup_frac=0.2)
     topk = torch.from_numpy(inputs["topk_idx"]).cuda()
-    cfg = ep.config_for(w, num_layout_cus)
-    say(f"[case] {w.name} ep_layout vs ep_layout_no_alloc (cus={num_layout_cus}, "
+    cfg = ep.config_for(w, num_layout_cus, layout_one_launch=one_launch)
+    say(f"[case] {w.name} ep_layout vs ep_layout_no_alloc (cus={num_layout_cus}, one_launch={one_launch}, "
         f"scratch {int(ep.ep_query_sizes(cfg).layout_scratch)} B)")
     want = ep.alloc_layout(cfg)
     ep.ep_layout(cfg, topk, want)
@@ -50,3 +50,11 @@ def test_no_alloc_layout_small_after_large_geometry():
     _layout_both(WORKLOADS[4], seed_for(4), num_layout_cus=1000)
     _layout_both(Workload("hybrid_small", S=6, T=97, H=64, K=6, E=24, R=6, Nmax=100, n_out=3), 5)
     _layout_both(WORKLOADS[1], seed_for(1))
+
+
+def test_no_alloc_one_launch_layout_two_calls_second_smaller():
+    # the one-launch layout keeps its exchange words in the library's array
+    # too (after the counts, so their place moves with the geometry)
+    _layout_both(WORKLOADS[2], seed_for(2), one_launch=True)
+    _layout_both(WORKLOADS[2].with_(name="dsv3_half", T=2048, Nmax=2048), 3, one_launch=True)
+    _layout_both(WORKLOADS[2], seed_for(2), num_layout_cus=300, one_launch=True)
