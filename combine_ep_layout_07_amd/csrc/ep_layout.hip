@@ -62,7 +62,7 @@ constexpr int kScanThreads = 1024;
 
 // LDS of the one-workgroup layout with nw waves: counts [nw][R+E], bases
 // [R+E], scan scratch [64 nw], flags [nw].
-size_t single_lds_bytes(const Shape &sh, int nw) {
+__host__ __device__ inline size_t single_lds_bytes(const Shape &sh, int nw) {
     return sizeof(int) * ((size_t)nw * (sh.R + sh.E) + sh.R + sh.E + (size_t)nw * kWave + nw);
 }
 constexpr int kScanCols = 64;                        // experts per scan workgroup
@@ -848,18 +848,21 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_fused(LayoutArgs a) {
     }
 }
 
-// The whole layout in one workgroup of NW waves, for one small source: the
-// workgroup's own counts are the source's totals, so the receiver tables and
-// the expert segment bases need no other workgroup, and the layout takes one
-// launch instead of two.  Wave w owns tokens [w*cw, (w+1)*cw), cw = ceil(T/NW).
-template <int NW, bool EXPAND>
-__global__ void __launch_bounds__(NW * kWave) k_layout_single(LayoutArgs a) {
+// The layout of one small source by one workgroup of NW waves (wave w owns
+// tokens [w*cw, (w+1)*cw), cw = ceil(T/NW)): the workgroup's own counts are
+// the source's totals, so the receiver tables and the expert segment bases
+// need no other workgroup.  Writes the tables to memory when `writer`, keeps
+// the receive base of every destination in rbase[R] (LDS) when rbase is not
+// null, and hands every item's slot (row base 0: one source) and expand row
+// to on_item(t, k, slot, pos), in each wave's token order.  LDS as
+// single_lds_bytes.
+template <int NW, bool EXPAND, typename OnItem>
+__device__ __forceinline__ void layout_one_workgroup(const LayoutArgs &a, int *lds, bool writer, int *rbase,
+                                                     OnItem &&on_item) {
     constexpr int NT = NW * kWave;
     const Shape &sh = a.sh;
     const int w = threadIdx.x / kWave, tid = threadIdx.x;
     const int R = sh.R, E = sh.E;
-    constexpr bool expand = EXPAND;
-    extern __shared__ int lds[];
     int *cnt_d = lds;               // [NW][R] per-wave counts, then running bases
     int *cnt_e = cnt_d + NW * R;    // [NW][E]
     int *zero_d = cnt_e + NW * E;   // [R]    the base per destination: 0
@@ -881,45 +884,71 @@ __global__ void __launch_bounds__(NW * kWave) k_layout_single(LayoutArgs a) {
     for (int d = tid; d < R; d += NT) {
         int tot = 0;
         for (int q = 0; q < NW; ++q) tot += cnt_d[q * R + d];
-        a.tokens_per_rank[d] = tot;
-        a.recv_psum[2 * d] = 0;
-        a.recv_psum[2 * d + 1] = tot;
+        if (writer) {
+            a.tokens_per_rank[d] = tot;
+            a.recv_psum[2 * d] = 0;
+            a.recv_psum[2 * d + 1] = tot;
+        }
         part[d] = tot;
     }
     for (int e = tid; e < E; e += NT) {
         int tot = 0;
         for (int q = 0; q < NW; ++q) tot += cnt_e[q * E + e];
-        a.tokens_per_expert[e] = tot;
+        if (writer) a.tokens_per_expert[e] = tot;
         seg[e] = (tot + sh.A - 1) / sh.A * sh.A;
     }
     __syncthreads();
     if (tid == 0) {
         int run = 0;
         for (int d = 0; d < R; ++d) {
-            a.recv_base[d] = run;
+            if (writer) a.recv_base[d] = run;
+            if (rbase) rbase[d] = run;
             run += part[d];
         }
-        a.recv_base[R] = run;
-        int any = 0;
-        for (int q = 0; q < NW; ++q) any |= flag[q];
-        a.error_flags[0] = any ? 1 : 0;
+        if (writer) {
+            a.recv_base[R] = run;
+            int any = 0;
+            for (int q = 0; q < NW; ++q) any |= flag[q];
+            a.error_flags[0] = any ? 1 : 0;
+        }
     }
     __syncthreads();
-    if (expand) {
+    if (EXPAND) {
         const int total = block_exclusive_scan<NT>(seg, E, part);
-        for (int e = tid; e < E; e += NT) a.expert_base[e] = seg[e];
-        if (tid == 0) a.expert_base[E] = total;
+        if (writer) {
+            for (int e = tid; e < E; e += NT) a.expert_base[e] = seg[e];
+            if (tid == 0) a.expert_base[E] = total;
+        }
     }
     wave_bases<NW>(cnt_d, R, zero_d);
-    if (expand) wave_bases<NW>(cnt_e, E, seg);
+    if (EXPAND) wave_bases<NW>(cnt_e, E, seg);
     __syncthreads();
-    rank_items(a, expand, 0, t0, t1, c, first, one_batch, cnt_d + w * R, cnt_e + w * E);
+    int *run_d = cnt_d + w * R, *run_e = cnt_e + w * E;
+    walk_steps(sh, a.topk_idx, t0, t1, c, first, one_batch, EXPAND, [&](const Item &it) {
+        const int rd = it.owner ? run_d[it.d] : 0;
+        const int re = (EXPAND && it.valid) ? run_e[it.e] : 0;
+        if (it.in) on_item(it.t, it.k, it.owner ? rd + it.rank_d : -1, (EXPAND && it.valid) ? re + it.rank_e : -1);
+        if (it.last_d) run_d[it.d] = rd + it.rank_d + 1;
+        if (EXPAND && it.last_e) run_e[it.e] = re + it.rank_e + 1;
+    });
+}
+
+// The whole layout in one workgroup of NW waves, for one small source, in one
+// launch instead of two.
+template <int NW, bool EXPAND>
+__global__ void __launch_bounds__(NW * kWave) k_layout_single(LayoutArgs a) {
+    extern __shared__ int lds[];
+    const int K = a.sh.K;
+    layout_one_workgroup<NW, EXPAND>(a, lds, true, nullptr, [&](int t, int k, int slot, int pos) {
+        a.dst_slot[(int64_t)t * K + k] = slot;
+        if (EXPAND) a.expand_pos[(int64_t)t * K + k] = pos;
+    });
 }
 
 // ------------------------------------------ layout and dispatch, one launch
 // The pages' dispatch replays the slots its prologue computed ([DET]
 // Approach); for one small source (compact layout) both run in one launch.
-// Every workgroup computes the whole layout of the source in LDS, exactly as
+// Every workgroup computes the whole layout of the source in LDS, as
 // k_layout_single does (a few hundred items: cheaper than a second launch);
 // workgroup 0 alone writes the tables to memory.  Then each workgroup
 // dispatches its own NW tokens, one wave per token, as k_dispatch_fused does:
@@ -932,16 +961,11 @@ __global__ void __launch_bounds__(NW * kWave) k_layout_dispatch_small(LayoutArgs
     constexpr int NT = NW * kWave;
     const Shape &sh = a.sh;
     const int w = threadIdx.x / kWave, tid = threadIdx.x, lane = lane_id();
-    const int R = sh.R, E = sh.E, K = sh.K;
+    const int K = sh.K;
     const bool writer = blockIdx.x == 0;
     extern __shared__ int lds[];
-    int *cnt_d = lds;               // [NW][R] per-wave counts, then running bases
-    int *cnt_e = cnt_d + NW * R;    // [NW][E]
-    int *zero_d = cnt_e + NW * E;   // [R]    the base per destination: 0
-    int *part = zero_d + R + E;     // [NT]   totals per destination
-    int *flag = part + NT;          // [NW]
-    int *rbase = flag + NW;         // [R]    first compact receive row of each destination
-    int *slots = rbase + R;         // [NW][K] slots of this workgroup's tokens
+    int *rbase = lds + single_lds_bytes(sh, NW) / sizeof(int);  // [R]     first receive row per destination
+    int *slots = rbase + sh.R;                                    // [NW][K] slots of this workgroup's tokens
 
     // This workgroup's tokens, one per wave: issue the token's loads first.
     const int g0 = blockIdx.x * NW;
@@ -962,66 +986,11 @@ __global__ void __launch_bounds__(NW * kWave) k_layout_dispatch_small(LayoutArgs
             wbits = __float_as_int(da.topk_weights[(int64_t)g * K + lane]);
         }
     }
-
-    // The layout of the whole source (k_layout_single's steps).
-    const int cw = (sh.T + NW - 1) / NW;
-    const int t0 = min(w * cw, sh.T), t1 = min(t0 + cw, sh.T);
-    const StepCtx c = make_ctx(K);
-    const bool one_batch = t1 - t0 <= kBatch * c.tps;
-    int64_t first[kBatch] = {};
-    if (one_batch) load_batch(sh, a.topk_idx, t0, t1, c, first);
-    for (int i = tid; i < NW * (R + E) + R; i += NT) lds[i] = 0;
-    for (int i = tid; i < NW * K; i += NT) slots[i] = -1;
-    __syncthreads();
-    const bool bad = wave_count(sh, a.topk_idx, t0, t1, cnt_d + w * R, cnt_e + w * E, true, c, first, one_batch);
-    if (lane_id() == 0) flag[w] = bad ? 1 : 0;
-    __syncthreads();
-    for (int d = tid; d < R; d += NT) {
-        int tot = 0;
-        for (int q = 0; q < NW; ++q) tot += cnt_d[q * R + d];
-        part[d] = tot;
-        if (writer) {
-            a.tokens_per_rank[d] = tot;
-            a.recv_psum[2 * d] = 0;
-            a.recv_psum[2 * d + 1] = tot;
-        }
-    }
-    if (writer) {
-        for (int ex = tid; ex < E; ex += NT) {
-            int tot = 0;
-            for (int q = 0; q < NW; ++q) tot += cnt_e[q * E + ex];
-            a.tokens_per_expert[ex] = tot;
-        }
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int d = 0; d < R; ++d) {
-            rbase[d] = run;
-            run += part[d];
-        }
-        if (writer) {
-            for (int d = 0; d < R; ++d) a.recv_base[d] = rbase[d];
-            a.recv_base[R] = run;
-            int any = 0;
-            for (int q = 0; q < NW; ++q) any |= flag[q];
-            a.error_flags[0] = any ? 1 : 0;
-        }
-    }
-    wave_bases<NW>(cnt_d, R, zero_d);
-    __syncthreads();
-    {
-        int *run_d = cnt_d + w * R;
-        walk_steps(sh, a.topk_idx, t0, t1, c, first, one_batch, false, [&](const Item &it) {
-            const int rd = it.owner ? run_d[it.d] : 0;
-            if (it.in) {
-                const int slot = it.owner ? rd + it.rank_d : -1;  // row base 0: one source
-                if (writer) a.dst_slot[(int64_t)it.t * K + it.k] = slot;
-                if (it.t >= g0 && it.t < g0 + NW) slots[(it.t - g0) * K + it.k] = slot;
-            }
-            if (it.last_d) run_d[it.d] = rd + it.rank_d + 1;
-        });
-    }
+    for (int i = tid; i < NW * K; i += NT) slots[i] = -1;  // ordered by the layout's first barrier
+    layout_one_workgroup<NW, false>(a, lds, writer, rbase, [&](int t, int k, int slot, int) {
+        if (writer) a.dst_slot[(int64_t)t * K + k] = slot;
+        if (t >= g0 && t < g0 + NW) slots[(t - g0) * K + k] = slot;
+    });
     __syncthreads();
     if (!has_tok) return;
 
