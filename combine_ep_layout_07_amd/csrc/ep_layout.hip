@@ -698,14 +698,11 @@ __device__ __forceinline__ int wait_arrivals(const LayoutArgs &a, uint64_t e1, i
             __builtin_amdgcn_s_sleep(1);
         }
     }
+    // Each thread that saw arrivals acquires them (pairs with the arriving
+    // workgroup's release); the barrier inside __syncthreads_or then orders
+    // every later read of the workgroup after those acquires.
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     return __syncthreads_or(late);
-}
-
-// After the workgroup's waits: make the other units' counts visible to every
-// wave of this workgroup (one device-scope acquire, then a barrier).
-__device__ __forceinline__ void acquire_counts() {
-    if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    __syncthreads();
 }
 
 // The coordinating workgroup: waits for every unit's arrival, builds the
@@ -718,7 +715,6 @@ __device__ void fused_coordinator(const LayoutArgs &a, int *lds, uint64_t *epoch
     __syncthreads();
     const uint64_t e1 = *epoch_sh + 1;
     const int late = wait_arrivals(a, e1, 0, U, a.spin_master, a.sync_test == 1 ? 1ull : 0ull);
-    acquire_counts();
     // Every unit published its counts before it arrived, so the tables are
     // exact whenever all arrivals were seen; a time-out leaves them untouched.
     if (!late) build_receiver_tables(a, false, lds);
@@ -811,7 +807,6 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_fused(LayoutArgs a) {
         }
         return;
     }
-    acquire_counts();
 
     // Pass 2: this unit's base per destination (what the earlier units of the
     // source send there) and its share of the per-source totals.

@@ -59,7 +59,7 @@ int main(int argc, char **argv) {
         c.expand = (int32_t)(next_u64() % 3);
         c.expert_alignment = pick(As);
         c.num_layout_cus = pick(Cs);
-        c.flags = (int32_t)(next_u64() % 3);
+        c.flags = (int32_t)(next_u64() % 5);  // Direct Recv X, one-launch layout, both, and an unknown bit
         c.num_scaleout_ranks = (int32_t)(next_u64() % 4);
         ep_sizes_t s;
         if (ep_query_sizes(&c, &s) != EP_OK) continue;
@@ -71,7 +71,9 @@ int main(int argc, char **argv) {
             return 1;
         }
         if (ep_layout(&c, nullptr, nullptr, nullptr) == EP_OK ||
+            ep_layout_no_alloc(&c, nullptr, nullptr, nullptr) == EP_OK ||
             ep_dispatch(&c, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, EP_PHASE_ALL, nullptr) == EP_OK ||
+            ep_layout_dispatch(&c, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) == EP_OK ||
             ep_combine(&c, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) == EP_OK) {
             printf("configuration %ld: a call accepted missing buffers\n", it);
             return 1;
