@@ -181,7 +181,7 @@ def test_cpu_baseline_legs_on_the_tiny_workload(monkeypatch):
     lay = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"])
     n = int(lay["recv_base"][-1])
     r = bench.cpu_baseline(w, inputs, n, int(((inputs["topk_idx"] >= 0) & (inputs["topk_idx"] < w.E)).sum()),
-                           budget_s=0.3)
+                           budget_s=0.3, all_cores_wall_s=0.2)
     assert r["kind"] == "oracle" and r["unit"] == "GB/s"
     assert r["cores"] == min(3, r["host"]["affinity_cpus"]) and r["host"]["threads"] == r["cores"]
     assert r["single_thread"]["cores"] == 1 and r["single_thread"]["value"] > 0 and r["value"] > 0
