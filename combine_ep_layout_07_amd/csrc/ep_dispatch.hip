@@ -15,9 +15,10 @@
 // every lane has CPL independent 16-byte loads in flight.
 //   k_scatter        one wave per token, its row stored to every owner's
 //                    staging row (plus scales and the metadata record);
-//   k_scatter_pf     Direct Recv X: rows straight to the receive rows, each
-//                    wave pipelining several tokens (next row loaded before
-//                    the current stores);
+//   k_scatter_pf     the same with each wave pipelining several tokens (next
+//                    row loaded before the current stores): Direct Recv X
+//                    (rows straight to the receive rows) and staging scatters
+//                    of at most 1 GiB of rows;
 //   k_epilogue_pf    compact epilogue, pipelined the same way over receive
 //                    rows (k_epilogue for rows wider than one pass);
 //   k_epilogue_meta  Direct Recv X: scales and metadata only, one thread per
@@ -60,9 +61,19 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #endif
 // The staging scatter runs one wave per token with no grid-stride cap
 // (measured at 16 x 2048 tokens: 708 us capped at 2048 workgroups, 674 us
-// uncapped; the same at 4096 tokens, which never reaches the cap).
+// uncapped; the same at 4096 tokens, which never reaches the cap) -- or, when
+// its staging rows come to at most EP_SCATTER_PIPELINE_MAX_BYTES, the
+// pipelined kernel with two tokens per wave (2 waves per SIMD instead of 4).
+// Measured on MI355X, steps with consecutive steps on alternating buffers:
+// 4096 tokens H = 7168 bf16 283 -> 277.5-278.5 us per step (scatter 73 ->
+// 70 us), the same in fp8 187 -> 185 us, 8192 tokens H = 4096 Zipf 235 ->
+// 234 us, but 16 x 2048 tokens (3 GB of staging rows) 2626 -> 2644 us
+// (scatter 676 -> 706 us, as slow with one token per wave at that occupancy).
 #ifndef EP_SCATTER_BLOCKS
 #define EP_SCATTER_BLOCKS (1 << 20)
+#endif
+#ifndef EP_SCATTER_PIPELINE_MAX_BYTES
+#define EP_SCATTER_PIPELINE_MAX_BYTES (1ll << 30)
 #endif
 // Compact-layout problems of at most this many tokens (all sources) with
 // rows of at most EP_FUSED_DISPATCH_MAX_ROW bytes dispatch in one launch
@@ -213,16 +224,16 @@ __device__ __forceinline__ void scatter_token(const DispatchArgs &a, int64_t g, 
     store_records(a, g, s, t, e, slot, wbits, owners, lane);
 }
 
-// Software-pipelined scatter, used for Direct Recv X: each wave takes tokens
-// g, g + nwaves, ... and loads the next token's ids, slots, weights and row
-// before storing the current one, so its reads overlap its writes; the grid
-// is sized so that the resident waves hold about EP_DIRECT_INFLIGHT_BYTES of
-// rows.  Measured on MI355X (Direct Recv X steps at T=4096, H=7168: 175 ->
-// 166 us; fp8 and H=4096 rows 1-2% faster): with the receive rows written
+// Software-pipelined scatter: each wave takes tokens g, g + nwaves, ... and
+// loads the next token's ids, slots, weights and row before storing the
+// current one, so its reads overlap its writes.  For Direct Recv X the grid is
+// sized so that the resident waves hold about EP_DIRECT_INFLIGHT_BYTES of rows
+// (measured on MI355X, Direct Recv X steps at T=4096, H=7168: 175 -> 166 us;
+// fp8 and H=4096 rows 1-2% faster: with the receive rows written
 // non-temporally straight to HBM, fewer waves that overlap their own reads
-// and writes beat one wave per token.  The staging scatter keeps one wave per
-// token: it gains from writes the Infinity Cache absorbs and measured no
-// faster pipelined.  Needs the whole row in one pass (64 * CPL chunks).
+// and writes beat one wave per token); the staging scatter uses it with two
+// tokens per wave when its rows come to at most EP_SCATTER_PIPELINE_MAX_BYTES
+// (see there).  Needs the whole row in one pass (64 * CPL chunks).
 template <int CPL>
 __global__ void __launch_bounds__(kThreads) k_scatter_pf(DispatchArgs a) {
     const Shape &sh = a.sh;
@@ -646,6 +657,15 @@ struct ScatterL {
                              ((int64_t)a.sh.row_bytes * kWavesPerBlock);
             blocks = blocks < 1 ? 1 : (blocks > EP_COPY_BLOCKS ? EP_COPY_BLOCKS : blocks);
             hipLaunchKernelGGL(k_scatter_pf<CPL>, dim3(grid_for(units, (int)blocks)), dim3(kThreads), 0, st, a);
+            return hipGetLastError();
+        }
+        // Staging rows of at most EP_SCATTER_PIPELINE_MAX_BYTES in all (an
+        // upper bound, S*T*min(K,R) rows): the pipelined kernel, two tokens
+        // per wave.
+        const int64_t bound = (int64_t)a.sh.S * a.sh.T * (a.sh.K < a.sh.R ? a.sh.K : a.sh.R) * a.sh.row_bytes;
+        if (a.slices == 1 && nchunks <= CPL * kWave && bound <= (int64_t)EP_SCATTER_PIPELINE_MAX_BYTES) {
+            hipLaunchKernelGGL(k_scatter_pf<CPL>, dim3(grid_for((units + 1) / 2, EP_SCATTER_BLOCKS)), dim3(kThreads), 0,
+                               st, a);
             return hipGetLastError();
         }
         hipLaunchKernelGGL(k_scatter<CPL>, dim3(grid_for(units, EP_SCATTER_BLOCKS)), dim3(kThreads), 0, st, a);
