@@ -320,12 +320,12 @@ __device__ __forceinline__ const int32_t *stage_tables(const DispatchArgs &a, in
 // ------------------------------------------ small dispatch, one launch
 // Scatter and copy epilogue of a small compact-layout problem in one launch:
 // below a few hundred tokens the fixed cost of a second launch exceeds the
-// copy itself.  Each wave takes one token, stores its row and record to the
-// staging rows of its destinations (as k_scatter), waits until its own stores
-// have completed, then copies those same staging rows, row and record, to
-// their compact receive rows recv_base[d] + recv_psum[d][s] + j (as the copy
-// epilogue does): the epilogue's work is split by sending token instead of by
-// receive row, with the same reads and writes.  Whole rows in one pass.
+// copy itself, and what remains is a chain of memory latencies.  Each wave
+// takes one token and writes, for each destination d, its staging row and
+// record (as k_scatter) and the compact receive row recv_base[d] +
+// recv_psum[d][s] + j that the copy epilogue would fill from that staging row
+// -- the same bytes, here from the registers that hold the token, so no
+// staging row is read back.  Whole rows in one pass, scales <= 64 per row.
 template <int CPL>
 __global__ void __launch_bounds__(kThreads) k_dispatch_fused(DispatchArgs a) {
     const Shape &sh = a.sh;
@@ -354,31 +354,19 @@ __global__ void __launch_bounds__(kThreads) k_dispatch_fused(DispatchArgs a) {
             if (c < nchunks) v[q] = ld16<EP_SCATTER_NT_LOAD>(src + (int64_t)c * 16);
         }
         const uint64_t owners = ballot(lane < sh.K && slot >= 0);
+        const float sf = lane < sh.sf_per_row ? a.x_sf[g * sh.sf_per_row + lane] : 0.0f;
         const int recv_row0 = shfl(base_l, e >= 0 ? rank_of(sh, e) : 0);
+        int word0, wv_hi;
+        record_words(sh, t, e, wbits, lane, word0, wv_hi);
         for (uint64_t m = owners; m; m &= m - 1) {
             const int k = __builtin_ctzll(m);
             const int d = rank_of(sh, read_lane(e, k));
             const int j = read_lane(slot, k) - row_base(sh, s) * sh.Nmax;
             if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for a layout of this topk_idx
-            uint8_t *dst = a.staging_x + (staging_region(sh, d, s) * sh.Nmax + j) * sh.row_bytes;
-#pragma unroll
-            for (int q = 0; q < CPL; ++q) {
-                const int c = q * kWave + lane;
-                if (c < nchunks) st16<EP_SCATTER_NT_STORE>(dst + (int64_t)c * 16, v[q]);
-            }
-        }
-        store_records(a, g, s, t, e, slot, wbits, owners, lane);
-        // The copy below reads what this wave has just stored: wait until its
-        // stores have completed (no other wave touches these staging rows).
-        __builtin_amdgcn_s_waitcnt(0);
-        for (uint64_t m = owners; m; m &= m - 1) {
-            const int k = __builtin_ctzll(m);
-            const int d = rank_of(sh, read_lane(e, k));
-            const int j = read_lane(slot, k) - row_base(sh, s) * sh.Nmax;
-            if ((unsigned)j >= (unsigned)sh.Nmax) continue;
             const int64_t i = (int64_t)read_lane(recv_row0, k) + j;
-            if (i >= a.recv_capacity_rows) continue;
-            epilogue_row_one_pass<CPL>(a, d, s, j, (int)i, lane);
+            if (i >= a.recv_capacity_rows) continue;  // never true: the call checked the capacity
+            token_rows<CPL>(a, d, s, t, staging_region(sh, d, s) * sh.Nmax + j, i, lane, v, sf, word0, wv_hi, e,
+                            wbits);
         }
     }
 }
@@ -624,6 +612,8 @@ int epilogue_chunks_per_lane(const Shape &sh) {
     return (((nchunks + slices - 1) / slices + kWave - 1) / kWave * kWave) / kWave;
 }
 
+constexpr int kMaxCpl = 16;  // 16-byte chunks per lane of the widest instantiation
+
 template <template <int> class Launcher, typename... Args>
 hipError_t dispatch_cpl(int need, Args &&...args) {
     if (need <= 1) return Launcher<1>::run(args...);
@@ -632,7 +622,7 @@ hipError_t dispatch_cpl(int need, Args &&...args) {
     if (need <= 7) return Launcher<7>::run(args...);
     if (need <= 8) return Launcher<8>::run(args...);
     if (need <= 14) return Launcher<14>::run(args...);
-    return Launcher<16>::run(args...);
+    return Launcher<kMaxCpl>::run(args...);
 }
 
 int grid_for(int64_t work_waves, int max_blocks = EP_COPY_BLOCKS) {
@@ -710,11 +700,12 @@ struct FusedL {
 bool dispatch_is_one_launch(const DispatchArgs &a) {
     const int64_t tokens = (int64_t)a.sh.S * a.sh.T;
     return !a.sh.expand && !a.sh.direct && tokens > 0 && tokens <= EP_FUSED_DISPATCH_MAX_TOKENS &&
-           a.sh.row_bytes <= EP_FUSED_DISPATCH_MAX_ROW;
+           a.sh.row_bytes <= EP_FUSED_DISPATCH_MAX_ROW && a.sh.row_bytes <= kWave * 16 * kMaxCpl &&
+           a.sh.sf_per_row <= kWave;
 }
 
 hipError_t launch_dispatch_fused(const DispatchArgs &a, hipStream_t stream) {
-    return dispatch_cpl<FusedL>(chunks_per_lane(a.sh), a, stream);
+    return dispatch_cpl<FusedL>((a.sh.row_bytes / 16 + kWave - 1) / kWave, a, stream);  // whole rows
 }
 
 hipError_t launch_scatter(const DispatchArgs &a, hipStream_t stream) {

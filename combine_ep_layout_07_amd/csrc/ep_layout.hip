@@ -947,10 +947,11 @@ __global__ void __launch_bounds__(NW * kWave) k_layout_single(LayoutArgs a) {
 // k_layout_single does (a few hundred items: cheaper than a second launch);
 // workgroup 0 alone writes the tables to memory.  Then each workgroup
 // dispatches its own NW tokens, one wave per token, as k_dispatch_fused does:
-// the token's row (loaded before the layout work, so its latency overlaps
-// it) and record go to the staging rows of its destinations, and once the
-// wave's stores have completed it copies those staging rows to their compact
-// receive rows.  The slots of the workgroup's tokens come from LDS.
+// the token's row and scales (loaded before the layout work, so their latency
+// overlaps it) and its record go to the staging rows of its destinations and,
+// from the same registers, to the compact receive rows the copy epilogue
+// would fill from them.  The slots of the workgroup's tokens and the first
+// receive row of each destination come from LDS.
 template <int NW, int CPL>
 __global__ void __launch_bounds__(NW * kWave) k_layout_dispatch_small(LayoutArgs a, DispatchArgs da) {
     constexpr int NT = NW * kWave;
@@ -969,7 +970,9 @@ __global__ void __launch_bounds__(NW * kWave) k_layout_dispatch_small(LayoutArgs
     const int nchunks = sh.row_bytes / 16;
     u32x4 v[CPL];
     int e = -1, wbits = 0;
+    float sf = 0.0f;
     if (has_tok) {
+        if (lane < sh.sf_per_row) sf = da.x_sf[(int64_t)g * sh.sf_per_row + lane];
 #pragma unroll
         for (int q = 0; q < CPL; ++q) {
             const int c = q * kWave + lane;
@@ -989,33 +992,19 @@ __global__ void __launch_bounds__(NW * kWave) k_layout_dispatch_small(LayoutArgs
     __syncthreads();
     if (!has_tok) return;
 
-    // Dispatch of token g: staging rows and record, then its receive rows.
+    // Dispatch of token g: its staging rows and receive rows, with records.
     const int slot = lane < K ? slots[w * K + lane] : -1;
     const uint64_t owners = ballot(lane < K && slot >= 0);
+    int word0, wv_hi;
+    record_words(sh, g, e, wbits, lane, word0, wv_hi);
     for (uint64_t m = owners; m; m &= m - 1) {
         const int k = __builtin_ctzll(m);
         const int d = rank_of(sh, read_lane(e, k));
         const int j = read_lane(slot, k);
         if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true: j < T <= Nmax
-        uint8_t *dst = da.staging_x + ((int64_t)d * sh.Nmax + j) * sh.row_bytes;
-#pragma unroll
-        for (int q = 0; q < CPL; ++q) {
-            const int cc = q * kWave + lane;
-            if (cc < nchunks) st16<EP_SCATTER_NT_STORE>(dst + (int64_t)cc * 16, v[q]);
-        }
-    }
-    store_records(da, g, 0, g, e, slot, wbits, owners, lane);
-    // The copy below reads what this wave has just stored (no other wave
-    // touches these staging rows): wait until its stores have completed.
-    __builtin_amdgcn_s_waitcnt(0);
-    for (uint64_t m = owners; m; m &= m - 1) {
-        const int k = __builtin_ctzll(m);
-        const int d = rank_of(sh, read_lane(e, k));
-        const int j = read_lane(slot, k);
-        if ((unsigned)j >= (unsigned)sh.Nmax) continue;
         const int64_t i = (int64_t)rbase[d] + j;
-        if (i >= da.recv_capacity_rows) continue;
-        epilogue_row_one_pass<CPL>(da, d, 0, j, (int)i, lane);
+        if (i >= da.recv_capacity_rows) continue;  // never true: the call checked the capacity
+        token_rows<CPL>(da, d, 0, g, (int64_t)d * sh.Nmax + j, i, lane, v, sf, word0, wv_hi, e, wbits);
     }
 }
 
@@ -1067,6 +1056,7 @@ bool layout_dispatch_is_one_launch(const LayoutArgs &a, const DispatchArgs &da) 
     const Shape &sh = a.sh;
     return sh.S == 1 && !sh.expand && !sh.direct && sh.T > 0 &&
            (int64_t)sh.T * sh.K <= EP_LAYOUT_SINGLE_MAX_ITEMS && sh.row_bytes <= kWave * 16 &&
+           sh.sf_per_row <= kWave &&
            small_dispatch_lds_bytes(sh) <= 65536 && da.recv_capacity_rows >= (int64_t)sh.T * (sh.K < sh.R ? sh.K : sh.R);
 }
 

@@ -1,7 +1,8 @@
 // ep_rows.h -- row-copy helpers shared by the dispatch kernels (scatter, copy
 // epilogue) and the layout-and-dispatch kernel of small problems: 16-byte
-// loads and stores with cache hints, the staging record of a token, and the
-// copy of one staging row to its compact receive row.
+// loads and stores with cache hints, the staging record of a token, the copy
+// of one staging row to its compact receive row, and a small-problem token's
+// staging and receive rows written from registers.
 #pragma once
 
 #include "ep_device.h"
@@ -41,19 +42,26 @@ __device__ __forceinline__ void st16(uint8_t *p, u32x4 v) {
     else *q = v;
 }
 
-// Scales and metadata record {t, expert ids, weight bits} of token g for the
-// staging row of every owner lane.  Metadata words i = lane and i = lane + 64
-// (K = 32 needs 65 words): word 0 = t, words 1..K = expert ids, words
-// K+1..2K = weight bits, shuffled with every lane active before any divergent
-// store.
-__device__ __forceinline__ void store_records(const DispatchArgs &a, int64_t g, int s, int t, int e, int slot,
-                                              int wbits, uint64_t owners, int lane) {
-    const Shape &sh = a.sh;
+// The metadata record {t, expert ids, weight bits} of token t that this lane
+// stores: words i = lane (word0) and i = lane + 64 (wv_hi; K = 32 needs 65
+// words), where word 0 = t, words 1..K = expert ids, words K+1..2K = weight
+// bits.  Shuffled, so every lane must be active.
+__device__ __forceinline__ void record_words(const Shape &sh, int t, int e, int wbits, int lane, int &word0,
+                                             int &wv_hi) {
     const int ev = shfl(e, lane >= 1 ? lane - 1 : 0);
     const int wv = shfl(wbits, lane - 1 - sh.K >= 0 ? lane - 1 - sh.K : 0);
     const int hi_src = lane + kWave - 1 - sh.K;
-    const int wv_hi = shfl(wbits, hi_src >= 0 && hi_src < kWave ? hi_src : 0);
-    const int word0 = lane == 0 ? t : (lane <= sh.K ? ev : wv);
+    wv_hi = shfl(wbits, hi_src >= 0 && hi_src < kWave ? hi_src : 0);
+    word0 = lane == 0 ? t : (lane <= sh.K ? ev : wv);
+}
+
+// Scales and metadata record of token g for the staging row of every owner
+// lane, with every lane active before any divergent store.
+__device__ __forceinline__ void store_records(const DispatchArgs &a, int64_t g, int s, int t, int e, int slot,
+                                              int wbits, uint64_t owners, int lane) {
+    const Shape &sh = a.sh;
+    int word0, wv_hi;
+    record_words(sh, t, e, wbits, lane, word0, wv_hi);
     for (uint64_t m = owners; m; m &= m - 1) {
         const int k = __builtin_ctzll(m);
         const int d = rank_of(sh, read_lane(e, k));
@@ -104,47 +112,41 @@ __device__ __forceinline__ void epilogue_row(const DispatchArgs &a, int d, int s
     }
 }
 
-// The same copy for a row of one pass (nchunks <= 64 * CPL, scales <= 128)
-// with every load — the row, its scales and its record — issued before the
-// first store: one dependent memory latency in all.  For the small-problem
-// kernels, whose cost is their chain of latencies.
+// Token (s, t)'s copy on destination d in the small-problem kernels, written
+// from the wave's registers: its staging row `row` and its compact receive
+// row i get the hidden row v (one pass), the scales sf (lane q < sf_per_row <=
+// 64 holds scale q) and their records (record_words, and the receive row's
+// local ids and weights as the copy epilogue derives them).  Stores only:
+// the receive row is the staging row's copy without a load between them.
 template <int CPL>
-__device__ __forceinline__ void epilogue_row_one_pass(const DispatchArgs &a, int d, int s, int j, int i, int lane) {
+__device__ __forceinline__ void token_rows(const DispatchArgs &a, int d, int s, int t, int64_t row, int64_t i,
+                                           int lane, const u32x4 (&v)[CPL], float sf, int word0, int wv_hi, int e,
+                                           int wbits) {
     const Shape &sh = a.sh;
     const int nchunks = sh.row_bytes / 16;
-    const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
-    const uint8_t *src = a.staging_x + row * sh.row_bytes;
-    const int32_t *meta = a.staging_meta + row * sh.meta_words;
-    u32x4 v[CPL];
+    uint8_t *stg = a.staging_x + row * sh.row_bytes;
+    uint8_t *dst = a.recv_x + i * sh.row_bytes;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
         const int c = q * kWave + lane;
-        if (c < nchunks) v[q] = ld16<EP_EPILOGUE_NT_LOAD>(src + (int64_t)c * 16);
+        if (c < nchunks) st16<EP_SCATTER_NT_STORE>(stg + (int64_t)c * 16, v[q]);
     }
-    float sf[2] = {0.0f, 0.0f};
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-        if (lane + h * kWave < sh.sf_per_row) sf[h] = a.staging_sf[row * sh.sf_per_row + lane + h * kWave];
-    const int t = meta[0];
-    int e = -1, wbits = 0;
-    if (lane < sh.K) {
-        e = meta[1 + lane];
-        wbits = meta[1 + sh.K + lane];
-    }
-    uint8_t *dst = a.recv_x + (int64_t)i * sh.row_bytes;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
         const int c = q * kWave + lane;
         if (c < nchunks) st16<EP_EPILOGUE_NT_STORE>(dst + (int64_t)c * 16, v[q]);
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-        if (lane + h * kWave < sh.sf_per_row) a.recv_sf[(int64_t)i * sh.sf_per_row + lane + h * kWave] = sf[h];
+    if (lane < sh.sf_per_row) {
+        a.staging_sf[row * sh.sf_per_row + lane] = sf;
+        a.recv_sf[i * sh.sf_per_row + lane] = sf;
+    }
+    if (lane < sh.meta_words) a.staging_meta[row * sh.meta_words + lane] = word0;
+    if (lane + kWave < sh.meta_words) a.staging_meta[row * sh.meta_words + lane + kWave] = wv_hi;
     if (lane == 0) a.recv_src_idx[i] = s * sh.T + t;
     if (lane < sh.K) {
         const bool on_d = (unsigned)e < (unsigned)sh.E && rank_of(sh, e) == d;
-        a.recv_topk_idx[(int64_t)i * sh.K + lane] = on_d ? e - d * sh.El : -1;
-        a.recv_topk_weights[(int64_t)i * sh.K + lane] = on_d ? __int_as_float(wbits) : 0.0f;
+        a.recv_topk_idx[i * sh.K + lane] = on_d ? e - d * sh.El : -1;
+        a.recv_topk_weights[i * sh.K + lane] = on_d ? __int_as_float(wbits) : 0.0f;
     }
 }
 
