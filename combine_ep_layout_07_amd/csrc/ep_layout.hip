@@ -849,11 +849,12 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_fused(LayoutArgs a) {
 // need no other workgroup.  Writes the tables to memory when `writer`, keeps
 // the receive base of every destination in rbase[R] (LDS) when rbase is not
 // null, and hands every item's slot (row base 0: one source) and expand row
-// to on_item(t, k, slot, pos), in each wave's token order.  LDS as
-// single_lds_bytes.
-template <int NW, bool EXPAND, typename OnItem>
+// to on_item(t, k, slot, pos), in each wave's token order.  on_issued() runs
+// right after the wave has issued its loads of the routing, so that loads it
+// issues queue behind them.  LDS as single_lds_bytes.
+template <int NW, bool EXPAND, typename OnIssued, typename OnItem>
 __device__ __forceinline__ void layout_one_workgroup(const LayoutArgs &a, int *lds, bool writer, int *rbase,
-                                                     OnItem &&on_item) {
+                                                     OnIssued &&on_issued, OnItem &&on_item) {
     constexpr int NT = NW * kWave;
     const Shape &sh = a.sh;
     const int w = threadIdx.x / kWave, tid = threadIdx.x;
@@ -871,6 +872,7 @@ __device__ __forceinline__ void layout_one_workgroup(const LayoutArgs &a, int *l
     const bool one_batch = t1 - t0 <= kBatch * c.tps;
     int64_t first[kBatch] = {};
     if (one_batch) load_batch(sh, a.topk_idx, t0, t1, c, first);
+    on_issued();
     for (int i = tid; i < NW * (R + E) + R + E; i += NT) lds[i] = 0;
     __syncthreads();
     const bool bad = wave_count(sh, a.topk_idx, t0, t1, cnt_d + w * R, cnt_e + w * E, true, c, first, one_batch);
@@ -934,7 +936,7 @@ template <int NW, bool EXPAND>
 __global__ void __launch_bounds__(NW * kWave) k_layout_single(LayoutArgs a) {
     extern __shared__ int lds[];
     const int K = a.sh.K;
-    layout_one_workgroup<NW, EXPAND>(a, lds, true, nullptr, [&](int t, int k, int slot, int pos) {
+    layout_one_workgroup<NW, EXPAND>(a, lds, true, nullptr, [] {}, [&](int t, int k, int slot, int pos) {
         a.dst_slot[(int64_t)t * K + k] = slot;
         if (EXPAND) a.expand_pos[(int64_t)t * K + k] = pos;
     });
@@ -963,7 +965,9 @@ __global__ void __launch_bounds__(NW * kWave) k_layout_dispatch_small(LayoutArgs
     int *rbase = lds + single_lds_bytes(sh, NW) / sizeof(int);  // [R]     first receive row per destination
     int *slots = rbase + sh.R;                                    // [NW][K] slots of this workgroup's tokens
 
-    // This workgroup's tokens, one per wave: issue the token's loads first.
+    // This workgroup's tokens, one per wave: the token's loads are issued
+    // right behind the layout's own loads of the routing, so that the layout
+    // does not wait for them.
     const int g0 = blockIdx.x * NW;
     const int g = g0 + w;
     const bool has_tok = g < sh.T;
@@ -971,21 +975,22 @@ __global__ void __launch_bounds__(NW * kWave) k_layout_dispatch_small(LayoutArgs
     u32x4 v[CPL];
     int e = -1, wbits = 0;
     float sf = 0.0f;
-    if (has_tok) {
-        if (lane < sh.sf_per_row) sf = da.x_sf[(int64_t)g * sh.sf_per_row + lane];
+    auto load_token = [&] {
+        if (!has_tok) return;
 #pragma unroll
         for (int q = 0; q < CPL; ++q) {
             const int c = q * kWave + lane;
             if (c < nchunks) v[q] = ld16<EP_SCATTER_NT_LOAD>(da.x + (int64_t)g * sh.row_bytes + (int64_t)c * 16);
         }
+        if (lane < sh.sf_per_row) sf = da.x_sf[(int64_t)g * sh.sf_per_row + lane];
         if (lane < K) {
             const int64_t e64 = a.topk_idx[(int64_t)g * K + lane];
             e = (e64 >= 0 && e64 < sh.E) ? (int)e64 : -1;
             wbits = __float_as_int(da.topk_weights[(int64_t)g * K + lane]);
         }
-    }
+    };
     for (int i = tid; i < NW * K; i += NT) slots[i] = -1;  // ordered by the layout's first barrier
-    layout_one_workgroup<NW, false>(a, lds, writer, rbase, [&](int t, int k, int slot, int) {
+    layout_one_workgroup<NW, false>(a, lds, writer, rbase, load_token, [&](int t, int k, int slot, int) {
         if (writer) a.dst_slot[(int64_t)t * K + k] = slot;
         if (t >= g0 && t < g0 + NW) slots[(t - g0) * K + k] = slot;
     });
@@ -1008,7 +1013,10 @@ __global__ void __launch_bounds__(NW * kWave) k_layout_dispatch_small(LayoutArgs
     }
 }
 
-constexpr int kSmallWaves = 16;  // waves per workgroup of k_layout_dispatch_small
+#ifndef EP_SMALL_WAVES
+#define EP_SMALL_WAVES 8
+#endif
+constexpr int kSmallWaves = EP_SMALL_WAVES;  // waves (tokens) per workgroup of k_layout_dispatch_small
 
 size_t small_dispatch_lds_bytes(const Shape &sh) {
     return single_lds_bytes(sh, kSmallWaves) + sizeof(int) * ((size_t)sh.R + (size_t)kSmallWaves * sh.K);

@@ -117,13 +117,15 @@ def ep_query_sizes(cfg: EpConfig) -> EpSizes:
     return sz
 
 
-def _stream(stream) -> ctypes.c_void_p:
+# The helpers below run on every call, so they stay cheap: plain integers for
+# pointers and streams (the argtypes convert them), one size property.
+def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    return stream.cuda_stream
 
 
-def _ptr(t: Optional[torch.Tensor], name: str, nbytes: int = 0):
+def _ptr(t: Optional[torch.Tensor], name: str, nbytes: int = 0) -> Optional[int]:
     """Device pointer of a contiguous CUDA tensor holding at least ``nbytes``."""
     if t is None:
         if nbytes:
@@ -133,9 +135,21 @@ def _ptr(t: Optional[torch.Tensor], name: str, nbytes: int = 0):
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if t.numel() * t.element_size() < nbytes:
-        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
-    return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+    nb = t.nbytes
+    if nb < nbytes:
+        raise ValueError(f"{name} holds {nb} bytes, needs {nbytes}")
+    return t.data_ptr() if nb else None
+
+
+def _recv_rows(cfg: EpConfig) -> int:
+    """Receive-row bound of cfg (ep_query_sizes), kept on cfg with the bytes it
+    was computed from and recomputed when any field has changed since."""
+    key = bytes(cfg)
+    memo = getattr(cfg, "_rows_memo", None)
+    if memo is None or memo[0] != key:
+        memo = (key, int(ep_query_sizes(cfg).recv_rows))
+        cfg._rows_memo = memo
+    return memo[1]
 
 
 def _check_elem(t: Optional[torch.Tensor], name: str, size: int) -> None:
@@ -290,7 +304,7 @@ def ep_layout_dispatch(cfg: EpConfig, x: torch.Tensor, x_sf: Optional[torch.Tens
 def ep_combine(cfg: EpConfig, layout: LayoutBuffers, topk_idx: torch.Tensor, topk_weights: torch.Tensor,
                y: torch.Tensor, out: torch.Tensor, stream=None) -> None:
     S, T, K, H = cfg.num_src_ranks, cfg.num_tokens, cfg.num_topk, cfg.hidden
-    rows = int(ep_query_sizes(cfg).recv_rows)
+    rows = _recv_rows(cfg)
     if topk_weights.dtype != torch.float32 or topk_idx.dtype != torch.int64:
         raise ValueError("topk_idx must be int64 and topk_weights float32")
     _check_elem(y, "y", 2)
@@ -307,7 +321,7 @@ def ep_combine_bias(cfg: EpConfig, layout: LayoutBuffers, topk_idx: torch.Tensor
                     out: torch.Tensor, stream=None) -> None:
     """Combine plus up to two bf16 [S][T][H] bias tensors added before the rounding."""
     S, T, K, H = cfg.num_src_ranks, cfg.num_tokens, cfg.num_topk, cfg.hidden
-    rows = int(ep_query_sizes(cfg).recv_rows)
+    rows = _recv_rows(cfg)
     if topk_weights.dtype != torch.float32 or topk_idx.dtype != torch.int64:
         raise ValueError("topk_idx must be int64 and topk_weights float32")
     for t, name in ((y, "y"), (bias0, "bias0"), (bias1, "bias1"), (out, "out")):
