@@ -22,6 +22,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -37,6 +38,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "combine_ep_layout_07_amd", "csrc")
 STAGES = ["layout", "scatter", "epilogue", "combine"]
 N_SETS = 2  # buffer sets the timed steps rotate over
+# The other workloads' lines time at least this long (more steps than K when a
+# step is short): the headline times exactly K steps.
+MIN_TIMED_MS = 20.0
 # Kernel sources per stage: a change to any of them invalidates that stage's
 # stored HBM counters.
 STAGE_SOURCES = {
@@ -472,13 +476,15 @@ class BufferSet:
         self.out = torch.empty((w.S * w.T, w.H), dtype=torch.bfloat16, device="cuda")
 
 
-def measure_workload(w, inputs, steps, warmup, direct=False, n_sets=N_SETS):
+def measure_workload(w, inputs, steps, warmup, direct=False, n_sets=N_SETS, min_timed_ms=0.0):
     """Time a workload: K steps back to back rotating over n_sets buffer sets
     (between two HIP events on the launch stream, synchronised on both sides);
     the same steps with an event between stages (stage_us); and each stage's
     kernel alone, K launches back to back over the rotating sets (the
-    roofline's durations).  Returns the timings and the sets (still holding
-    the last results)."""
+    roofline's durations).  With min_timed_ms, K is raised so that the timed
+    steps take at least that long (a few-microsecond step timed 20 times is
+    mostly the events' own jitter).  Returns the timings and the sets (still
+    holding the last results)."""
     import numpy as np
     import torch
 
@@ -507,13 +513,20 @@ def measure_workload(w, inputs, steps, warmup, direct=False, n_sets=N_SETS):
     for i in range(max(warmup, n_sets)):
         step(sets[i % n_sets])
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(steps):
-        step(sets[i % n_sets])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+
+    def timed_steps(k):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(k):
+            step(sets[i % n_sets])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / k
+
+    ms = timed_steps(steps)
+    if ms * steps < min_timed_ms:
+        steps = int(math.ceil(min_timed_ms / ms))
+        ms = timed_steps(steps)
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     for i in range(steps):
@@ -542,7 +555,7 @@ def measure_workload(w, inputs, steps, warmup, direct=False, n_sets=N_SETS):
     v_rows = int(((topk >= 0) & (topk < w.E)).sum().item())
     pad = int(L.expert_base[-1].item()) - v_rows if w.expand else 0
     return dict(cfg=cfg, sets=sets, topk=topk, wts=wts, calls=calls, step=step, stream=stream, ms=ms,
-                stage_ms=stage_ms, n_rows=n_rows, v_rows=v_rows, pad=pad)
+                stage_ms=stage_ms, n_rows=n_rows, v_rows=v_rows, pad=pad, steps=steps)
 
 
 def workload_summary(w, m, direct=False) -> dict:
@@ -558,7 +571,7 @@ def workload_summary(w, m, direct=False) -> dict:
                     f"{'expand A=%d' % w.alignment if w.expand else 'compact'} layout, {w.routing} routing"
                     f"{', Direct Recv X' if direct else ''}",
         "value": round(value, 2), "unit": "GB/s", "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
-        "ms_per_step": round(ms, 5), "tokens_per_s": round(w.S * w.T / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 5), "steps": m["steps"], "tokens_per_s": round(w.S * w.T / (ms * 1e-3), 1),
         "alg_bytes_per_step": b, "rows": {"dedup_N": m["n_rows"], "valid_V": m["v_rows"], "padding": m["pad"]},
         "stage_us": {k: round(v * 1e3, 2) for k, v in st.items()},
         "stage_gbps_back_to_back": {n: round(b[n] / (st[f"{n}_back_to_back"] * 1e-3) / 1e9, 1) for n in STAGES},
@@ -695,7 +708,7 @@ def measure_extras(steps: int, warmup: int) -> dict:
                                  f"{' n_out=%d' % w.n_out if w.n_out > 1 else ''}",
                      "value": round(total / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
                      "pct_of_peak": round(100.0 * total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
-                     "ms_per_step": round(ms, 5), "tokens_per_s": round(w.S * w.T / (ms * 1e-3), 1),
+                     "ms_per_step": round(ms, 5), "steps": m["steps"], "tokens_per_s": round(w.S * w.T / (ms * 1e-3), 1),
                      "alg_bytes_per_step": total, "rows": {"dedup_N": n_rows, "valid_V": v_rows, "padding": pad}}
         del sets, bias, x
         torch.cuda.empty_cache()
@@ -821,7 +834,7 @@ def main():
             wc = WORKLOADS[cid]
             print(f"[bench] workload {cid} ({wc.name})", file=sys.stderr, flush=True)
             inp = generate(wc, seed_for(cid))
-            mc = measure_workload(wc, inp, args.steps, args.warmup)
+            mc = measure_workload(wc, inp, args.steps, args.warmup, min_timed_ms=MIN_TIMED_MS)
             res["configs"][str(cid)] = workload_summary(wc, mc)
             del mc, inp
             torch.cuda.empty_cache()

@@ -13,8 +13,9 @@
 // wavefront moves one row at a time, lane l taking chunks c = l + 64*i, the
 // whole row (or a CPL-chunk slice of it) loaded into VGPRs before any store, so
 // every lane has CPL independent 16-byte loads in flight.
-//   k_scatter        one wave per token, its row stored to every owner's
-//                    staging row (plus scales and the metadata record);
+//   k_scatter        one wave per token (or per 1 KiB piece of its row, for
+//                    staging rows of more than 1 GiB), its row stored to
+//                    every owner's staging row (plus scales and the record);
 //   k_scatter_pf     the same with each wave pipelining several tokens (next
 //                    row loaded before the current stores): Direct Recv X
 //                    (rows straight to the receive rows) and staging scatters
@@ -59,16 +60,21 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #ifndef EP_EPILOGUE_BLOCKS
 #define EP_EPILOGUE_BLOCKS (1 << 20)
 #endif
-// The staging scatter runs one wave per token with no grid-stride cap
-// (measured at 16 x 2048 tokens: 708 us capped at 2048 workgroups, 674 us
-// uncapped; the same at 4096 tokens, which never reaches the cap) -- or, when
-// its staging rows come to at most EP_SCATTER_PIPELINE_MAX_BYTES, the
+// The staging scatter, with no grid-stride cap (measured at 16 x 2048 tokens:
+// 708 us capped at 2048 workgroups, 674 us uncapped), takes one of two forms.
+// When its staging rows come to at most EP_SCATTER_PIPELINE_MAX_BYTES: the
 // pipelined kernel with two tokens per wave (2 waves per SIMD instead of 4).
-// Measured on MI355X, steps with consecutive steps on alternating buffers:
-// 4096 tokens H = 7168 bf16 283 -> 277.5-278.5 us per step (scatter 73 ->
-// 70 us), the same in fp8 187 -> 185 us, 8192 tokens H = 4096 Zipf 235 ->
-// 234 us, but 16 x 2048 tokens (3 GB of staging rows) 2626 -> 2644 us
-// (scatter 676 -> 706 us, as slow with one token per wave at that occupancy).
+// Measured on MI355X, steps with consecutive steps on alternating buffers,
+// against one token per wave: 4096 tokens H = 7168 bf16 283 -> 277.5-278.5
+// us per step (scatter 73 -> 70 us), the same in fp8 187 -> 185 us, 8192
+// tokens H = 4096 Zipf 235 -> 234 us, but 16 x 2048 tokens (3 GB of staging
+// rows) 2626 -> 2644 us (scatter 676 -> 706 us).  Above that bound: one wave
+// per 1 KiB piece of a token's row (column slices of 64 chunks), which loads
+// its piece and the token's ids at once and stores the piece to each owner:
+// short-lived waves keep the write stream closer to a fill's rate (a plain
+// fill of 3.3 GB in 1 KiB per wave ran at 6.9 TB/s, in 14 KiB per wave at
+// 5.5).  16 x 2048 tokens: scatter 678 -> 606 us (2 KiB pieces 668 us); at
+// 4096 tokens the pieces lose to the pipelined kernel (70.5 -> 73.3 us).
 #ifndef EP_SCATTER_BLOCKS
 #define EP_SCATTER_BLOCKS (1 << 20)
 #endif
@@ -710,6 +716,15 @@ hipError_t launch_dispatch_fused(const DispatchArgs &a, hipStream_t stream) {
 
 hipError_t launch_scatter(const DispatchArgs &a, hipStream_t stream) {
     if ((int64_t)a.sh.S * a.sh.T == 0) return hipSuccess;
+    const int nchunks = a.sh.row_bytes / 16;
+    const int64_t bound = (int64_t)a.sh.S * a.sh.T * (a.sh.K < a.sh.R ? a.sh.K : a.sh.R) * a.sh.row_bytes;
+    if (!a.sh.direct && EP_SCATTER_SLICES == 1 && bound > (int64_t)EP_SCATTER_PIPELINE_MAX_BYTES) {
+        DispatchArgs b = a;
+        b.slices = (nchunks + kWave - 1) / kWave;  // 1 KiB pieces
+        hipLaunchKernelGGL(k_scatter<1>, dim3(grid_for((int64_t)a.sh.S * a.sh.T * b.slices, EP_SCATTER_BLOCKS)),
+                           dim3(kThreads), 0, stream, b);
+        return hipGetLastError();
+    }
     return dispatch_cpl<ScatterL>(chunks_per_lane(a.sh), a, stream);
 }
 
