@@ -708,7 +708,7 @@ def measure_extras(steps: int, warmup: int) -> dict:
                                  f"{' n_out=%d' % w.n_out if w.n_out > 1 else ''}",
                      "value": round(total / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
                      "pct_of_peak": round(100.0 * total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
-                     "ms_per_step": round(ms, 5), "steps": m["steps"], "tokens_per_s": round(w.S * w.T / (ms * 1e-3), 1),
+                     "ms_per_step": round(ms, 5), "steps": steps, "tokens_per_s": round(w.S * w.T / (ms * 1e-3), 1),
                      "alg_bytes_per_step": total, "rows": {"dedup_N": n_rows, "valid_V": v_rows, "padding": pad}}
         del sets, bias, x
         torch.cuda.empty_cache()
