@@ -79,10 +79,21 @@ int64_t recv_rows(const ep::Shape &sh) {
     return S * T * (K < sh.R ? K : sh.R);
 }
 
+// The head of a compact layout's scratch: the receive-row index of the staging
+// path (one int64 staging row per receive row), written by the scatter and read
+// by the copy epilogue; the layout's own words follow it.  Its size depends on
+// the shape only (not on num_layout_cus or the flags), so one layout serves
+// both dispatch paths and any workgroup count.
+uint64_t recv_index_bytes(const ep::Shape &sh) {
+    if (sh.expand) return 0;
+    return ((uint64_t)recv_rows(sh) * sizeof(int64_t) + 255) & ~(uint64_t)255;
+}
+
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
-// need_scratch: the caller's scratch_dev is used (every call but
-// ep_layout_no_alloc, which takes the library's own).
+// need_scratch: the caller's scratch_dev is required (ep_layout; the no-alloc
+// layout takes the library's own, and the dispatch and the combine do not need
+// one).
 int check_layout_ptrs(const ep::Shape &sh, const ep_layout_t *L, bool need_scratch = true) {
     if (!L) return EP_ERR_INVALID_ARG;
     const bool need_tok = (int64_t)sh.S * sh.T * sh.K > 0;
@@ -132,7 +143,8 @@ int ep_query_sizes(const ep_config_t *cfg, ep_sizes_t *sz) {
     sz->expert_base = sh.expand ? (E + 1) * i4 : 0;
     sz->expand_pos = sh.expand ? S * T * K * i4 : 0;
     sz->error_flags = i4;
-    sz->layout_scratch = ep::layout_scratch_bytes(sh, ep::layout_geometry(sh, cfg->num_layout_cus));
+    sz->layout_scratch =
+        recv_index_bytes(sh) + ep::layout_scratch_bytes(sh, ep::layout_geometry(sh, cfg->num_layout_cus));
     sz->recv_psum_scaleup = sh.n_out > 1 ? R * ((uint64_t)sh.n_up + 1) * i4 : 0;
     const uint64_t staging_rows = R * S * Nmax;
     sz->staging_x = sh.direct ? 0 : staging_rows * (uint64_t)sh.row_bytes;
@@ -166,8 +178,8 @@ int make_layout_args(const ep_config_t *cfg, const int64_t *topk_idx_dev, const 
     ep::LayoutArgs &a = *out;
     a.sh = sh;
     a.g = ep::layout_geometry(sh, cfg->num_layout_cus);
-    void *scratch = layout->scratch_dev;
-    if (own_scratch) {
+    void *scratch = layout->scratch_dev ? static_cast<char *>(layout->scratch_dev) + recv_index_bytes(sh) : nullptr;
+    if (own_scratch) {  // the library's array holds the layout's own words only
         if (ep::layout_scratch_bytes(sh, a.g) > EP_NO_ALLOC_SCRATCH_BYTES) return EP_ERR_CAPACITY;
         if (ep::no_alloc_scratch(&scratch) != hipSuccess) return EP_ERR_HIP;
     }
@@ -229,7 +241,7 @@ int make_dispatch_args(const ep_config_t *cfg, const void *x_dev, const float *x
     ep::Shape sh;
     int rc = make_shape(cfg, &sh);
     if (rc != EP_OK) return rc;
-    if ((rc = check_layout_ptrs(sh, layout)) != EP_OK) return rc;
+    if ((rc = check_layout_ptrs(sh, layout, false)) != EP_OK) return rc;
     if (!recv) return EP_ERR_INVALID_ARG;
     const bool tok = (int64_t)sh.S * sh.T > 0;
     if (tok) {
@@ -269,6 +281,13 @@ int make_dispatch_args(const ep_config_t *cfg, const void *x_dev, const float *x
     a.recv_topk_idx = recv->recv_topk_idx_dev;
     a.recv_topk_weights = recv->recv_topk_weights_dev;
     a.recv_capacity_rows = recv->recv_capacity_rows;
+    a.slices = 1;
+    // The receive-row index at the head of the layout's scratch (compact
+    // staging path), when the caller passes one; else the epilogue searches
+    // the receiver tables.
+    a.recv_row_src = (!sh.expand && !sh.direct && layout->scratch_dev && aligned(layout->scratch_dev, 8))
+                         ? static_cast<int64_t *>(layout->scratch_dev)
+                         : nullptr;
     return EP_OK;
 }
 
@@ -330,7 +349,7 @@ int ep_combine_bias(const ep_config_t *cfg, const ep_layout_t *layout, const int
     ep::Shape sh;
     int rc = make_shape(cfg, &sh);
     if (rc != EP_OK) return rc;
-    if ((rc = check_layout_ptrs(sh, layout)) != EP_OK) return rc;
+    if ((rc = check_layout_ptrs(sh, layout, false)) != EP_OK) return rc;
     if ((int64_t)sh.S * sh.T > 0) {
         if (!topk_idx_dev || !aligned(topk_idx_dev, 8) || !topk_weights_dev || !aligned(topk_weights_dev, 4) ||
             !y_dev || !aligned(y_dev, 16) || !out_dev || !aligned(out_dev, 16))

@@ -60,6 +60,10 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #ifndef EP_EPILOGUE_BLOCKS
 #define EP_EPILOGUE_BLOCKS (1 << 20)
 #endif
+#ifndef EP_INDEXED_CPW
+#define EP_INDEXED_CPW 2  // chunks per lane of a k_epilogue_indexed piece
+#endif
+constexpr int kIndexedCpw = EP_INDEXED_CPW;
 // The staging scatter, with no grid-stride cap (measured at 16 x 2048 tokens:
 // 708 us capped at 2048 workgroups, 674 us uncapped), takes one of two forms.
 // When its staging rows come to at most EP_SCATTER_PIPELINE_MAX_BYTES: the
@@ -145,13 +149,15 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
             wbits = __float_as_int(a.topk_weights[g * sh.K + lane]);
         }
         const uint64_t owners = ballot(lane < sh.K && slot >= 0);
-        // Direct Recv X: every owner lane fetches its destination's compact
-        // base recv_base[d] + recv_psum[d][s] at once (one gather, not a
-        // dependent scalar load per owner row).
+        // Direct Recv X (and the receive-row index, slice 0): every owner
+        // lane fetches its destination's compact base recv_base[d] +
+        // recv_psum[d][s] at once (one gather, not a dependent scalar load
+        // per owner row).
         int recv_row0 = 0;
-        if (sh.direct && lane < sh.K && slot >= 0) {
+        if ((sh.direct || (a.recv_row_src && slice == 0)) && lane < sh.K && slot >= 0) {
             const int d = rank_of(sh, e);
             recv_row0 = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s];
+            if (!sh.direct) record_recv_row(a, s, e, slot, recv_row0);
         }
         const uint8_t *src = a.x + g * sh.row_bytes;
         for (int c0 = c_lo; c0 < c_hi; c0 += CPL * kWave) {
@@ -200,9 +206,10 @@ __device__ __forceinline__ void scatter_token(const DispatchArgs &a, int64_t g, 
     const int s = (int)(g / sh.T), t = (int)(g - (int64_t)s * sh.T);
     const uint64_t owners = ballot(lane < sh.K && slot >= 0);
     int recv_row0 = 0;
-    if (sh.direct && lane < sh.K && slot >= 0) {
+    if ((sh.direct || a.recv_row_src) && lane < sh.K && slot >= 0) {
         const int d = rank_of(sh, e);
         recv_row0 = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s];
+        if (!sh.direct) record_recv_row(a, s, e, slot, recv_row0);
     }
     for (uint64_t m = owners; m; m &= m - 1) {
         const int k = __builtin_ctzll(m);
@@ -472,6 +479,50 @@ __device__ __forceinline__ int last_le(const int32_t *tab, int n, int key) {
     return lo;
 }
 
+// Compact copy epilogue with the receive-row index (the staging path when the
+// layout's scratch holds the index the scatter recorded): one wave per piece
+// of CPW chunks per lane (2 KiB at CPW = 2) of receive row i, which loads the
+// row's staging index, then its piece, and stores it; piece 0 also moves the
+// scales and the metadata.  Short-lived waves with one dependent load ahead of
+// the copy.  Measured on MI355X: 4096 tokens H = 7168 bf16, epilogue 129 ->
+// 125 us inside the step (134 -> 123 us back to back); 8192 tokens H = 4096
+// 106 -> 101 us; fp8 63 -> 62 us.  1 / 4 KiB pieces: 140 / 138 us at 4096
+// tokens.  Without the index, pieces that first search the tables were far
+// slower (1 KiB: 199 us; 2 KiB with the tables in LDS 128 us, 4 KiB 137 us).
+template <int CPW>
+__global__ void __launch_bounds__(kThreads) k_epilogue_indexed(DispatchArgs a) {
+    const Shape &sh = a.sh;
+    const int lane = lane_id();
+    const int nchunks = sh.row_bytes / 16;
+    const int P = (nchunks + CPW * kWave - 1) / (CPW * kWave);
+    const int64_t n_units = min((int64_t)a.recv_base[sh.R], a.recv_capacity_rows) * P;
+    const int64_t n_staging = (int64_t)sh.R * sh.S * sh.Nmax;
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t u = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; u < n_units; u += nwaves) {
+        const int64_t i = u / P;
+        const int p = (int)(u - i * P);
+        const int64_t row = a.recv_row_src[i];
+        if (row < 0 || row >= n_staging) continue;  // never true after the scatter of this layout
+        u32x4 v[CPW];
+#pragma unroll
+        for (int q = 0; q < CPW; ++q) {
+            const int c = (p * CPW + q) * kWave + lane;
+            if (c < nchunks) v[q] = ld16<EP_EPILOGUE_NT_LOAD>(a.staging_x + row * sh.row_bytes + (int64_t)c * 16);
+        }
+#pragma unroll
+        for (int q = 0; q < CPW; ++q) {
+            const int c = (p * CPW + q) * kWave + lane;
+            if (c < nchunks) st16<EP_EPILOGUE_NT_STORE>(a.recv_x + i * sh.row_bytes + (int64_t)c * 16, v[q]);
+        }
+        if (p == 0) {
+            const int64_t region = row / sh.Nmax;
+            int d, s;
+            staging_region_inverse(sh, region, d, s);
+            epilogue_row<1>(a, d, s, (int)(row - region * sh.Nmax), (int)i, lane, 0, 0);  // scales and metadata
+        }
+    }
+}
+
 // Metadata-only epilogue (Direct Recv X: the hidden rows are already in
 // place).  One thread per item (i, c) of a filled receive row i: c < K is
 // top-k lane c (c = 0 also writes the source index); each further item copies
@@ -681,7 +732,11 @@ struct EpilogueL {
         if (a.sh.expand)
             hipLaunchKernelGGL(k_epilogue_expand<CPL>, dim3(grid_for(rows, EP_EXPAND_BLOCKS)), dim3(kThreads),
                                std::max<size_t>(fits ? tab : 0, EP_EXPAND_LDS), st, a, (int)fits);
-        else if (a.slices == 1 && a.sh.row_bytes / 16 <= CPL * kWave)
+        else if (a.recv_row_src) {
+            const int64_t pieces = (a.sh.row_bytes / 16 + kIndexedCpw * kWave - 1) / (kIndexedCpw * kWave);
+            hipLaunchKernelGGL(k_epilogue_indexed<kIndexedCpw>, dim3(grid_for(rows * pieces, EP_EPILOGUE_BLOCKS)),
+                               dim3(kThreads), 0, st, a);
+        } else if (a.slices == 1 && a.sh.row_bytes / 16 <= CPL * kWave)
             hipLaunchKernelGGL(k_epilogue_pf<CPL>, dim3(grid_for(rows, EP_EPILOGUE_BLOCKS)), dim3(kThreads),
                                fits ? tab : 0, st, a, (int)fits);
         else

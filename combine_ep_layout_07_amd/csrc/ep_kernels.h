@@ -41,6 +41,15 @@ __host__ __device__ inline int64_t staging_region(const Shape &sh, int d, int s)
     return (int64_t)d * sh.S + s;
 }
 
+// (d, s) of a staging region: the inverse of staging_region (a destination's
+// regions are the S consecutive ones from d*S; in the row form the remainder
+// is (s % n_up) * n_out + s / n_up).
+__host__ __device__ inline void staging_region_inverse(const Shape &sh, int64_t region, int &d, int &s) {
+    d = (int)(region / sh.S);
+    const int rem = (int)(region - (int64_t)d * sh.S);
+    s = sh.n_out > 1 ? (rem % sh.n_out) * sh.n_up + rem / sh.n_out : rem;
+}
+
 // Layout pass geometry: B workgroups per source, each owning `chunk` tokens
 // (split into equal wave ranges, one per wave of the workgroup).
 struct LayoutGeom {
@@ -92,6 +101,10 @@ struct DispatchArgs {
     float *recv_topk_weights;
     int64_t recv_capacity_rows;
     int slices;  // scatter: column slices per token (set by the launcher)
+    // Compact staging path with a layout scratch: the staging row of every
+    // filled receive row, written by the scatter, read by the copy epilogue;
+    // null otherwise (the epilogue then locates rows in the receiver tables).
+    int64_t *recv_row_src;
 };
 
 struct CombineArgs {

@@ -75,6 +75,20 @@ __device__ __forceinline__ void store_records(const DispatchArgs &a, int64_t g, 
     }
 }
 
+// Receive-row index of the compact staging path, recorded by an owner lane
+// (lane < K holding a slot) of token (s, t): at its compact receive row
+// i = recv_base[d] + recv_psum[d][s] + j (recv_row0 = the first two terms),
+// the staging row that will hold that receive row's data, so that the copy
+// epilogue finds its source with one load instead of a search of the tables.
+__device__ __forceinline__ void record_recv_row(const DispatchArgs &a, int s, int e, int slot, int recv_row0) {
+    const Shape &sh = a.sh;
+    const int d = rank_of(sh, e);
+    const int j = slot - row_base(sh, s) * sh.Nmax;
+    const int64_t i = (int64_t)recv_row0 + j;
+    if ((unsigned)j < (unsigned)sh.Nmax && i < a.recv_capacity_rows)
+        a.recv_row_src[i] = staging_region(sh, d, s) * sh.Nmax + j;
+}
+
 // Staging row (d, s, j) to compact receive row i = recv_base[d] +
 // recv_psum[d][s] + j: the hidden row, its scales, and the per-row metadata
 // derived from the record.

@@ -174,7 +174,16 @@ typedef struct ep_sizes {
  *                                the pages' extended psum)
  *   error_flags       [1]        bit 0: some top-k id was >= E
  *   scratch           bytes      ep_sizes_t.layout_scratch, private to the
- *                                library; contents need no initialisation  */
+ *                                library; contents need no initialisation.
+ *                                Compact layouts: its head holds the
+ *                                receive-row index (8 bytes per receive row,
+ *                                rounded up to 256 bytes) that a dispatch's
+ *                                scatter writes and its copy epilogue reads,
+ *                                the layout's own words follow.  Required by
+ *                                ep_layout; may be NULL for ep_dispatch (the
+ *                                epilogue then searches the receiver tables
+ *                                for each row's source: slower) and for
+ *                                ep_combine, which do not allocate it.  */
 typedef struct ep_layout {
     int32_t *dst_slot_dev;
     int32_t *tokens_per_rank_dev;
@@ -236,8 +245,9 @@ int ep_layout(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layo
  * same launches and the same tables as ep_layout, but the scratch is an
  * EP_NO_ALLOC_SCRATCH_BYTES array the library holds on each GPU it runs on
  * until the process ends, so layout->scratch_dev is ignored (may be NULL).
- * The call allocates and frees nothing.  A configuration whose
- * ep_sizes_t.layout_scratch exceeds EP_NO_ALLOC_SCRATCH_BYTES returns
+ * The call allocates and frees nothing.  A configuration whose layout words
+ * (ep_sizes_t.layout_scratch less the receive-row index at its head, which
+ * the array does not hold) exceed EP_NO_ALLOC_SCRATCH_BYTES returns
  * EP_ERR_CAPACITY before anything is enqueued; EP_ERR_HIP if the array's
  * device address cannot be obtained.  Every call on one GPU uses that GPU's
  * one array: calls that overlap on one GPU (on different streams, or from
@@ -254,7 +264,10 @@ int ep_layout_no_alloc(const ep_config_t *cfg, const int64_t *topk_idx_dev, cons
  *   x_sf_dev         [S][T][H/128] fp32 (fp8 only, else NULL)
  *   topk_idx_dev     int64 [S][T][K];  topk_weights_dev fp32 [S][T][K]
  *   phases           enum ep_phase mask; the epilogue reads the staging rows
- *                    the scatter of the same layout wrote. */
+ *                    the scatter of the same layout wrote (and, when the
+ *                    layout's scratch is given, the receive-row index that
+ *                    scatter wrote at its head: give both phases the same
+ *                    layout). */
 int ep_dispatch(const ep_config_t *cfg, const void *x_dev, const float *x_sf_dev,
                 const int64_t *topk_idx_dev, const float *topk_weights_dev,
                 const ep_layout_t *layout, const ep_recv_t *recv, int32_t phases, void *stream);

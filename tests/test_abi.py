@@ -211,9 +211,10 @@ def test_layout_scratch_grows_with_num_layout_cus():
     assert 0 < a.layout_scratch < b.layout_scratch
     # any int32 request is clamped to at least one token per wave: 4096 tokens give at most 1024 units
     c = ep.ep_query_sizes(ep.make_config(1, 4096, 7168, 8, 256, 16, 4096, num_layout_cus=2**31 - 1))
+    # the receive-row index (8 bytes per receive row, 256-byte multiple), then
     # counts per unit, then the one-launch layout's exchange words (8-byte
     # aligned: up to 4 bytes of padding, the epoch, one per unit)
-    assert c.layout_scratch == 1024 * (16 + 256 + 1) * 4 + 4 + (1 + 1024) * 8
+    assert c.layout_scratch == 4096 * 8 * 8 + 1024 * (16 + 256 + 1) * 4 + 4 + (1 + 1024) * 8
     ex = ep.ep_query_sizes(ep.make_config(16, 2048, 7168, 8, 256, 16, 2048, "bf16", True))
     assert ex.layout_scratch % 4 == 0  # the expand layout has no exchange words
 

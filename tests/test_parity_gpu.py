@@ -11,6 +11,7 @@ The five workloads run at their full sizes in the launch configuration the
 benchmark times; the small cases cover edge lanes, ragged sizes and limits.
 """
 import os
+import types
 
 import numpy as np
 import pytest
@@ -25,16 +26,28 @@ from tests.gpu_harness import (bf16_to_f64, compare_combine, compare_dispatch, c
                                run_layout, say, seeded_y, upload)
 
 
-def _full_case(w, seed, edge=None, num_layout_cus=0, check_combine=True, direct=False):
+def _without_scratch(L):
+    """The same layout buffers, with no scratch pointer for the dispatch and
+    the combine (the copy epilogue then has no receive-row index).  Holds L,
+    whose tensors the copied pointers address."""
+    st = ep.EpLayoutT.from_buffer_copy(L.struct)
+    st.scratch_dev = None
+    return types.SimpleNamespace(struct=st, buffers=L)
+
+
+def _full_case(w, seed, edge=None, num_layout_cus=0, check_combine=True, direct=False, scratch=True):
     edge = edge or {}
     say(f"[case] {w.name} S={w.S} T={w.T} H={w.H} K={w.K} E={w.E} R={w.R} Nmax={w.Nmax} {w.dtype} "
-        f"expand={w.expand} A={w.alignment} seed={seed} edge={edge} cus={num_layout_cus} direct={direct}")
+        f"expand={w.expand} A={w.alignment} seed={seed} edge={edge} cus={num_layout_cus} direct={direct} "
+        f"scratch={scratch}")
     inputs = generate(w, seed, **edge)
     lay_o = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment, w.n_out)
     dev = upload(w, inputs)
     say("  ep_layout")
     cfg, L = run_layout(w, dev, num_layout_cus, direct)
     compare_tables(layout_host(L), lay_o)
+    if not scratch:
+        L = _without_scratch(L)
     say("  ep_dispatch")
     R = ep.alloc_recv(cfg)
     ep.ep_dispatch(cfg, dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_weights"], L, R)
@@ -253,6 +266,17 @@ def test_staging_scatter_in_pieces(w):
     scatter in 1 KiB pieces per wave: ragged last pieces (875 and 520 chunks
     per row: 14 and 9 pieces), fp8 scales, masked and duplicate lanes."""
     _full_case(w, 61, EDGE)
+
+
+@pytest.mark.parametrize("w", [WORKLOADS[3], SMALL[0], SMALL[1], SMALL[7], HYBRID[1],
+                               Workload("wide_bf16", S=2, T=45, H=10240, K=4, E=16, R=4, Nmax=48)],
+                         ids=lambda w: w.name)
+def test_dispatch_without_layout_scratch(w):
+    """Dispatch and combine given the layout without its scratch: the copy
+    epilogue has no receive-row index and searches the receiver tables for
+    each row's source (one-pass rows, rows wider than one pass, fp8, the
+    hybrid row form, edge lanes); the oracle's results either way."""
+    _full_case(w, 73, EDGE, scratch=False)
 
 
 def test_expand_alignment_128_at_dsv3_shape():
