@@ -495,7 +495,7 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_indexed(DispatchArgs a) {
     const int lane = lane_id();
     const int nchunks = sh.row_bytes / 16;
     const int P = (nchunks + CPW * kWave - 1) / (CPW * kWave);
-    const int64_t n_units = min((int64_t)a.recv_base[sh.R], a.recv_capacity_rows) * P;
+    const int64_t n_units = min(min((int64_t)a.recv_base[sh.R], a.recv_capacity_rows), compact_rows_bound(sh)) * P;
     const int64_t n_staging = (int64_t)sh.R * sh.S * sh.Nmax;
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
     for (int64_t u = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; u < n_units; u += nwaves) {
@@ -729,11 +729,11 @@ struct EpilogueL {
         const bool fits = tab <= 32768;
         const int64_t rows = a.sh.expand ? (int64_t)a.sh.S * a.sh.T * (a.sh.K < a.sh.R ? a.sh.K : a.sh.R)
                                          : a.recv_capacity_rows;
+        const int64_t pieces = (a.sh.row_bytes / 16 + kIndexedCpw * kWave - 1) / (kIndexedCpw * kWave);
         if (a.sh.expand)
             hipLaunchKernelGGL(k_epilogue_expand<CPL>, dim3(grid_for(rows, EP_EXPAND_BLOCKS)), dim3(kThreads),
                                std::max<size_t>(fits ? tab : 0, EP_EXPAND_LDS), st, a, (int)fits);
         else if (a.recv_row_src) {
-            const int64_t pieces = (a.sh.row_bytes / 16 + kIndexedCpw * kWave - 1) / (kIndexedCpw * kWave);
             hipLaunchKernelGGL(k_epilogue_indexed<kIndexedCpw>, dim3(grid_for(rows * pieces, EP_EPILOGUE_BLOCKS)),
                                dim3(kThreads), 0, st, a);
         } else if (a.slices == 1 && a.sh.row_bytes / 16 <= CPL * kWave)

@@ -107,6 +107,11 @@ struct DispatchArgs {
     int64_t *recv_row_src;
 };
 
+// Compact rows of a layout at most (the receive-row index's length).
+__host__ __device__ inline int64_t compact_rows_bound(const Shape &sh) {
+    return (int64_t)sh.S * sh.T * (sh.K < sh.R ? sh.K : sh.R);
+}
+
 struct CombineArgs {
     Shape sh;
     const int64_t *topk_idx;

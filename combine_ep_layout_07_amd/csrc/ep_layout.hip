@@ -1065,7 +1065,7 @@ bool layout_dispatch_is_one_launch(const LayoutArgs &a, const DispatchArgs &da) 
     return sh.S == 1 && !sh.expand && !sh.direct && sh.T > 0 &&
            (int64_t)sh.T * sh.K <= EP_LAYOUT_SINGLE_MAX_ITEMS && sh.row_bytes <= kWave * 16 &&
            sh.sf_per_row <= kWave &&
-           small_dispatch_lds_bytes(sh) <= 65536 && da.recv_capacity_rows >= (int64_t)sh.T * (sh.K < sh.R ? sh.K : sh.R);
+           small_dispatch_lds_bytes(sh) <= 65536 && da.recv_capacity_rows >= compact_rows_bound(sh);
 }
 
 hipError_t launch_layout_dispatch(const LayoutArgs &a, const DispatchArgs &da, hipStream_t stream) {

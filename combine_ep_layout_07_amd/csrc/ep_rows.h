@@ -85,7 +85,7 @@ __device__ __forceinline__ void record_recv_row(const DispatchArgs &a, int s, in
     const int d = rank_of(sh, e);
     const int j = slot - row_base(sh, s) * sh.Nmax;
     const int64_t i = (int64_t)recv_row0 + j;
-    if ((unsigned)j < (unsigned)sh.Nmax && i < a.recv_capacity_rows)
+    if ((unsigned)j < (unsigned)sh.Nmax && i < a.recv_capacity_rows && i < compact_rows_bound(sh))
         a.recv_row_src[i] = staging_region(sh, d, s) * sh.Nmax + j;
 }
 

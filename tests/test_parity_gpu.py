@@ -268,14 +268,15 @@ def test_staging_scatter_in_pieces(w):
     _full_case(w, 61, EDGE)
 
 
-@pytest.mark.parametrize("w", [WORKLOADS[3], SMALL[0], SMALL[1], SMALL[7], HYBRID[1],
-                               Workload("wide_bf16", S=2, T=45, H=10240, K=4, E=16, R=4, Nmax=48)],
+@pytest.mark.parametrize("w", [WORKLOADS[3], SMALL[0], SMALL[1], SMALL[7], SMALL[8], SMALL[9], HYBRID[1], HYBRID[2],
+                               Workload("wide_bf16", S=2, T=45, H=10240, K=4, E=16, R=4, Nmax=48),
+                               WORKLOADS[5].with_(name="expand_quarter", S=4)],
                          ids=lambda w: w.name)
 def test_dispatch_without_layout_scratch(w):
     """Dispatch and combine given the layout without its scratch: the copy
-    epilogue has no receive-row index and searches the receiver tables for
-    each row's source (one-pass rows, rows wider than one pass, fp8, the
-    hybrid row form, edge lanes); the oracle's results either way."""
+    epilogues have no index and search the receiver tables for each row's
+    source (compact and expand, one-pass rows, rows wider than one pass, fp8,
+    the hybrid row form, edge lanes); the oracle's results either way."""
     _full_case(w, 73, EDGE, scratch=False)
 
 
