@@ -79,17 +79,15 @@ int64_t recv_rows(const ep::Shape &sh) {
     return S * T * (K < sh.R ? K : sh.R);
 }
 
-// The head of a compact layout's scratch: the receive-row index of the staging
-// path (one int64 staging row per receive row), written by the scatter and read
-// by the copy epilogue; the layout's own words follow it.  Its size depends on
-// the shape only (not on num_layout_cus or the flags), so one layout serves
-// both dispatch paths and any workgroup count.  (The same index for the expand
-// epilogue -- staging row plus the token's expand rows per compact row -- was
-// measured slower: its scatter 601 -> 634 us, its epilogue 1234 -> 1257 us at
-// 16 x 2048 tokens.)
+// The head of a layout's scratch: the receive-row index of the staging path,
+// one int64 per receive row (compact: the staging row; expand: the staging row
+// and top-k lane, or -1 for a padding row), written by the scatter (and the
+// padding kernel) and read by the copy epilogue; the layout's own words follow
+// it.  Its size depends on the shape only (not on num_layout_cus or the
+// flags), so one layout serves both dispatch paths and any workgroup count.
 uint64_t recv_index_bytes(const ep::Shape &sh) {
-    if (sh.expand) return 0;
-    return ((uint64_t)ep::compact_rows_bound(sh) * sizeof(int64_t) + 255) & ~(uint64_t)255;
+    const uint64_t rows = sh.expand ? (uint64_t)recv_rows(sh) : (uint64_t)ep::compact_rows_bound(sh);
+    return (rows * sizeof(int64_t) + 255) & ~(uint64_t)255;
 }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -285,12 +283,12 @@ int make_dispatch_args(const ep_config_t *cfg, const void *x_dev, const float *x
     a.recv_topk_weights = recv->recv_topk_weights_dev;
     a.recv_capacity_rows = recv->recv_capacity_rows;
     a.slices = 1;
-    // The receive-row index at the head of the layout's scratch (compact
-    // staging path), when the caller passes one; else the epilogue searches
-    // the receiver tables.
-    a.recv_row_src = (!sh.expand && !sh.direct && layout->scratch_dev && aligned(layout->scratch_dev, 8))
-                         ? static_cast<int64_t *>(layout->scratch_dev)
-                         : nullptr;
+    // The receive-row index at the head of the layout's scratch (staging
+    // path), when the caller passes one; else the epilogues search the
+    // receiver tables.
+    const bool index = !sh.direct && layout->scratch_dev && aligned(layout->scratch_dev, 8);
+    a.recv_row_src = index && !sh.expand ? static_cast<int64_t *>(layout->scratch_dev) : nullptr;
+    a.expand_row_src = index && sh.expand ? static_cast<int64_t *>(layout->scratch_dev) : nullptr;
     return EP_OK;
 }
 
