@@ -80,12 +80,14 @@ int64_t recv_rows(const ep::Shape &sh) {
 }
 
 // The head of a layout's scratch: the receive-row index of the staging path,
-// one int64 per receive row (compact: the staging row; expand: the staging row
-// and top-k lane, or -1 for a padding row), written by the scatter (and the
-// padding kernel) and read by the copy epilogue; the layout's own words follow
-// it.  Its size depends on the shape only (not on num_layout_cus or the
-// flags), so one layout serves both dispatch paths and any workgroup count.
+// one int64 per receive row (compact: the staging row; expand with alignment
+// 1: the staging row and top-k lane), written by the scatter and read by the
+// copy epilogue; the layout's own words follow it.  Its size depends on the
+// shape only (not on num_layout_cus or the flags), so one layout serves both
+// dispatch paths and any workgroup count.  Padded expand layouts have none.
+bool has_recv_index(const ep::Shape &sh) { return !sh.expand || sh.A == 1; }
 uint64_t recv_index_bytes(const ep::Shape &sh) {
+    if (!has_recv_index(sh)) return 0;
     const uint64_t rows = sh.expand ? (uint64_t)recv_rows(sh) : (uint64_t)ep::compact_rows_bound(sh);
     return (rows * sizeof(int64_t) + 255) & ~(uint64_t)255;
 }
@@ -286,7 +288,7 @@ int make_dispatch_args(const ep_config_t *cfg, const void *x_dev, const float *x
     // The receive-row index at the head of the layout's scratch (staging
     // path), when the caller passes one; else the epilogues search the
     // receiver tables.
-    const bool index = !sh.direct && layout->scratch_dev && aligned(layout->scratch_dev, 8);
+    const bool index = has_recv_index(sh) && !sh.direct && layout->scratch_dev && aligned(layout->scratch_dev, 8);
     a.recv_row_src = index && !sh.expand ? static_cast<int64_t *>(layout->scratch_dev) : nullptr;
     a.expand_row_src = index && sh.expand ? static_cast<int64_t *>(layout->scratch_dev) : nullptr;
     return EP_OK;

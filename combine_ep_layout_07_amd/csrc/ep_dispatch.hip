@@ -159,7 +159,6 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
             recv_row0 = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s];
             if (!sh.direct) record_recv_row(a, s, e, slot, recv_row0);
         }
-        if (a.expand_row_src && slice == 0) record_expand_rows(a, g, s, e, slot, owners, lane);
         const uint8_t *src = a.x + g * sh.row_bytes;
         for (int c0 = c_lo; c0 < c_hi; c0 += CPL * kWave) {
             u32x4 v[CPL];
@@ -194,6 +193,7 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
             }
         }
         if (slice == 0) store_records(a, g, s, t, e, slot, wbits, owners, lane);
+        if (a.expand_row_src && slice == 0) record_expand_rows(a, g, s, e, slot, owners, lane);  // after the row
     }
 }
 
@@ -212,7 +212,6 @@ __device__ __forceinline__ void scatter_token(const DispatchArgs &a, int64_t g, 
         recv_row0 = a.recv_base[d] + a.recv_psum[(int64_t)d * (sh.S + 1) + s];
         if (!sh.direct) record_recv_row(a, s, e, slot, recv_row0);
     }
-    if (a.expand_row_src) record_expand_rows(a, g, s, e, slot, owners, lane);
     for (uint64_t m = owners; m; m &= m - 1) {
         const int k = __builtin_ctzll(m);
         const int d = rank_of(sh, read_lane(e, k));
@@ -237,6 +236,7 @@ __device__ __forceinline__ void scatter_token(const DispatchArgs &a, int64_t g, 
         }
     }
     store_records(a, g, s, t, e, slot, wbits, owners, lane);
+    if (a.expand_row_src) record_expand_rows(a, g, s, e, slot, owners, lane);
 }
 
 // Software-pipelined scatter: each wave takes tokens g, g + nwaves, ... and
@@ -525,11 +525,11 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_indexed(DispatchArgs a) {
     }
 }
 
-// Expand epilogue with the expand index (the staging path when the layout's
-// scratch holds it): expand rows in order, one wave per piece of CPW chunks
-// per lane (2 KiB at CPW = 2) of expand row r, which loads r's index entry
-// (its staging row and top-k lane, or -1 for a padding row, which the padding
-// kernel fills), then its piece of that staging row, and stores it; piece 0
+// Expand epilogue with the expand index (the staging path with expert
+// alignment 1 when the layout's scratch holds it: every expand row is a lane
+// row): expand rows in order, one wave per piece of CPW chunks per lane (2 KiB
+// at CPW = 2) of expand row r, which loads r's index entry (its staging row
+// and top-k lane), then its piece of that staging row, and stores it; piece 0
 // also writes the row's scales, source index and the lane's weight.  The
 // writes become one sequential stream; a staging row that feeds several
 // expand rows (1.23 on average at K = 8 of 256 experts on 16 ranks) is read
@@ -539,6 +539,10 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_indexed(DispatchArgs a) {
 // the step, 1235 -> 1135 us back to back, scatter 603 -> 617 us (recording
 // the index), step 2552 -> 2535 us; non-temporal loads 1209 / 1147 us;
 // pieces of 1 / 4 / 7 / 14 KiB: 1285 / 1305 / 1341 / 1430 us in the step.
+// At 4096 tokens: 150 -> 142 us back to back; with alignment 128 (half the
+// rows padding, marked in the index by the padding kernel run first) 206 ->
+// 210 us and the step 0.388 -> 0.419 ms, so padded layouts keep the other
+// kernel.
 template <int CPW>
 __global__ void __launch_bounds__(kThreads) k_epilogue_expand_indexed(DispatchArgs a) {
     const Shape &sh = a.sh;
@@ -552,10 +556,9 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_expand_indexed(DispatchAr
         const int64_t r = u / P;
         const int p = (int)(u - r * P);
         const int64_t code = a.expand_row_src[r];
-        if (code < 0) continue;  // a padding row
         const int64_t row = code & ((1ll << 56) - 1);
         const int k = (int)(code >> 56);
-        if (row >= n_staging || k >= sh.K) continue;  // never true after the scatter of this layout
+        if (code < 0 || row >= n_staging || k >= sh.K) continue;  // never true after the scatter of this layout
         u32x4 v[CPW];
 #pragma unroll
         for (int q = 0; q < CPW; ++q) {
@@ -704,7 +707,6 @@ __global__ void __launch_bounds__(kThreads) k_expand_padding(DispatchArgs a) {
         if (threadIdx.x == 0) {
             a.recv_src_idx[r] = -1;
             a.recv_topk_weights[r] = 0.0f;
-            if (a.expand_row_src && r < expand_rows_bound(sh)) a.expand_row_src[r] = -1;  // the epilogue skips it
         }
     }
 }
@@ -845,18 +847,8 @@ hipError_t launch_scatter(const DispatchArgs &a, hipStream_t stream) {
     return dispatch_cpl<ScatterL>(chunks_per_lane(a.sh), a, stream);
 }
 
-static hipError_t launch_padding(const DispatchArgs &a, hipStream_t stream) {
-    if (!a.sh.expand || a.sh.A <= 1) return hipSuccess;
-    const int split = a.sh.A - 1 < 16 ? a.sh.A - 1 : 16;  // workgroups per expert
-    hipLaunchKernelGGL(k_expand_padding, dim3(a.sh.E, split), dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
-}
-
 hipError_t launch_epilogue(const DispatchArgs &a, hipStream_t stream) {
     hipError_t err = hipSuccess;
-    // With the expand index the padding rows go first: their entries mark
-    // them for the epilogue.
-    if (a.expand_row_src && (err = launch_padding(a, stream)) != hipSuccess) return err;
     if ((int64_t)a.sh.S * a.sh.T > 0) {
         if (a.sh.direct) {
             const size_t tab = sizeof(int32_t) * ((size_t)a.sh.R + 1 + (size_t)a.sh.R * (a.sh.S + 1));
@@ -876,7 +868,12 @@ hipError_t launch_epilogue(const DispatchArgs &a, hipStream_t stream) {
         }
     }
     if (err != hipSuccess) return err;
-    return a.expand_row_src ? hipSuccess : launch_padding(a, stream);
+    if (a.sh.expand && a.sh.A > 1) {
+        const int split = a.sh.A - 1 < 16 ? a.sh.A - 1 : 16;  // workgroups per expert
+        hipLaunchKernelGGL(k_expand_padding, dim3(a.sh.E, split), dim3(kThreads), 0, stream, a);
+        err = hipGetLastError();
+    }
+    return err;
 }
 
 }  // namespace ep

@@ -105,10 +105,10 @@ struct DispatchArgs {
     // filled receive row, written by the scatter, read by the copy epilogue;
     // null otherwise (the epilogue then locates rows in the receiver tables).
     int64_t *recv_row_src;
-    // Expand layout with a layout scratch: per expand row r < expert_base[E],
-    // the staging row it copies with its top-k lane in the top byte (row |
-    // lane << 56), written by the scatter, or -1 for a padding row, written
-    // by the padding kernel; read by the expand epilogue.  Null otherwise.
+    // Expand layout with alignment 1 and a layout scratch: per expand row r <
+    // expert_base[E], the staging row it copies with its top-k lane in the top
+    // byte (row | lane << 56), written by the scatter, read by the expand
+    // epilogue.  Null otherwise.
     int64_t *expand_row_src;
 };
 
@@ -116,7 +116,7 @@ struct DispatchArgs {
 __host__ __device__ inline int64_t compact_rows_bound(const Shape &sh) {
     return (int64_t)sh.S * sh.T * (sh.K < sh.R ? sh.K : sh.R);
 }
-// Expand rows of a layout at most, padding included (the expand index's length).
+// Expand rows of a layout at most, padding included.
 __host__ __device__ inline int64_t expand_rows_bound(const Shape &sh) {
     return (int64_t)sh.S * sh.T * sh.K + (int64_t)sh.E * (sh.A - 1);
 }

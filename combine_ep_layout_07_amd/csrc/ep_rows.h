@@ -89,10 +89,11 @@ __device__ __forceinline__ void record_recv_row(const DispatchArgs &a, int s, in
         a.recv_row_src[i] = staging_region(sh, d, s) * sh.Nmax + j;
 }
 
-// The expand layout's index, recorded for token (s, t) by every lane at once
-// (all lanes active): each valid lane k < K (expert e, destination d) stores,
-// at its expand row, the staging row of (d, s) that holds the token -- its
-// owner's slot j, the owner being the lowest lane with a slot on d -- and k.
+// The expand layout's index (alignment 1), recorded for token (s, t) by every
+// lane at once (all lanes active): each valid lane k < K (expert e,
+// destination d) stores, at its expand row, the staging row of (d, s) that
+// holds the token -- its owner's slot j, the owner being the lowest lane with
+// a slot on d -- and k.
 __device__ __forceinline__ void record_expand_rows(const DispatchArgs &a, int64_t g, int s, int e, int slot,
                                                    uint64_t owners, int lane) {
     const Shape &sh = a.sh;
