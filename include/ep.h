@@ -175,11 +175,12 @@ typedef struct ep_sizes {
  *   error_flags       [1]        bit 0: some top-k id was >= E
  *   scratch           bytes      ep_sizes_t.layout_scratch, private to the
  *                                library; contents need no initialisation.
- *                                Compact layouts: its head holds the
- *                                receive-row index (8 bytes per receive row,
- *                                rounded up to 256 bytes) that a dispatch's
- *                                scatter writes and its copy epilogue reads,
- *                                the layout's own words follow.  Required by
+ *                                Compact layouts and expand layouts with
+ *                                alignment 1: its head holds the receive-row
+ *                                index (8 bytes per receive row, rounded up
+ *                                to 256 bytes) that a dispatch's scatter
+ *                                writes and its copy epilogue reads, the
+ *                                layout's own words follow.  Required by
  *                                ep_layout; may be NULL for ep_dispatch (the
  *                                epilogue then searches the receiver tables
  *                                for each row's source: slower) and for
