@@ -80,9 +80,10 @@ int64_t recv_rows(const ep::Shape &sh) {
 }
 
 // The head of a layout's scratch: the receive-row index of the staging path,
-// one int64 per receive row (compact: the staging row; expand with alignment
-// 1: the staging row and top-k lane), written by the scatter and read by the
-// copy epilogue; the layout's own words follow it.  Its size depends on the
+// one int64 per receive row (compact: the staging row, written by the scatter;
+// expand with alignment 1: the staging row and top-k lane, written by the
+// layout's slot pass), read by the copy epilogue; the layout's own words
+// follow it.  Its size depends on the
 // shape only (not on num_layout_cus or the flags), so one layout serves both
 // dispatch paths and any workgroup count.  Padded expand layouts have none.
 bool has_recv_index(const ep::Shape &sh) { return !sh.expand || sh.A == 1; }
@@ -209,6 +210,12 @@ int make_layout_args(const ep_config_t *cfg, const int64_t *topk_idx_dev, const 
         a.sync = reinterpret_cast<uint64_t *>((end + 7) & ~static_cast<uintptr_t>(7));
     }
     a.one_launch = (cfg->flags & EP_FLAG_LAYOUT_ONE_LAUNCH) ? 1 : 0;
+    // The expand index at the head of the caller's scratch (alignment 1), when
+    // one is given -- also to ep_layout_no_alloc, whose own words live in the
+    // library's array.
+    a.expand_row_src = (sh.expand && has_recv_index(sh) && layout->scratch_dev && aligned(layout->scratch_dev, 8))
+                           ? static_cast<int64_t *>(layout->scratch_dev)
+                           : nullptr;
     // Bounds of the exchange's waits (each poll is one device-scope load and
     // a short sleep, about a microsecond): 2^21 polls for the coordinator and
     // for each unit.  EP_LAYOUT_SYNC_TEST forces a time-out, for tests of the

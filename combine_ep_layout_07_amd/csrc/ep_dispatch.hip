@@ -193,7 +193,6 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
             }
         }
         if (slice == 0) store_records(a, g, s, t, e, slot, wbits, owners, lane);
-        if (a.expand_row_src && slice == 0) record_expand_rows(a, g, s, e, slot, owners, lane);  // after the row
     }
 }
 
@@ -236,7 +235,6 @@ __device__ __forceinline__ void scatter_token(const DispatchArgs &a, int64_t g, 
         }
     }
     store_records(a, g, s, t, e, slot, wbits, owners, lane);
-    if (a.expand_row_src) record_expand_rows(a, g, s, e, slot, owners, lane);
 }
 
 // Software-pipelined scatter: each wave takes tokens g, g + nwaves, ... and
@@ -527,10 +525,11 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_indexed(DispatchArgs a) {
 
 // Expand epilogue with the expand index (the staging path with expert
 // alignment 1 when the layout's scratch holds it: every expand row is a lane
-// row): expand rows in order, one wave per piece of CPW chunks per lane (2 KiB
-// at CPW = 2) of expand row r, which loads r's index entry (its staging row
-// and top-k lane), then its piece of that staging row, and stores it; piece 0
-// also writes the row's scales, source index and the lane's weight.  The
+// row; the layout's slot pass writes the index): expand rows in order, one
+// wave per piece of CPW chunks per lane (2 KiB at CPW = 2) of expand row r,
+// which loads r's index entry (its staging row and top-k lane), then its piece
+// of that staging row, and stores it; piece 0 also writes the row's scales,
+// source index and the lane's weight.  The
 // writes become one sequential stream; a staging row that feeds several
 // expand rows (1.23 on average at K = 8 of 256 experts on 16 ranks) is read
 // once per row, through the caches (cached loads: the repeat reads find

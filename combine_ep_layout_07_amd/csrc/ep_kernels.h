@@ -80,6 +80,10 @@ struct LayoutArgs {
     uint32_t spin_master, spin_unit;  // polls before the coordinator / a unit gives up
     int sync_test;                    // 0; 1 or 2 force a time-out (tests of the error path)
     int one_launch;                   // compact layout: one launch with a grid-wide exchange, where it fits
+    // Expand layout with alignment 1 and a layout scratch: the expand index
+    // (DispatchArgs::expand_row_src) at the scratch's head, written by the
+    // slot pass; null otherwise.
+    int64_t *expand_row_src;
 };
 
 // Words of the one-launch layout's exchange for `units` units.
@@ -107,7 +111,8 @@ struct DispatchArgs {
     int64_t *recv_row_src;
     // Expand layout with alignment 1 and a layout scratch: per expand row r <
     // expert_base[E], the staging row it copies with its top-k lane in the top
-    // byte (row | lane << 56), written by the scatter, read by the expand
+    // byte (row | lane << 56), written by the layout's slot pass (which knows
+    // each lane's expand row and its owner's slot), read by the expand
     // epilogue.  Null otherwise.
     int64_t *expand_row_src;
 };

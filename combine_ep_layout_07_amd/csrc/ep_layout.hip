@@ -129,6 +129,7 @@ namespace {
 struct Item {
     bool in, valid, invalid, owner;
     int t, k, d, e;
+    int owner_lane;     // valid only: the lowest lane of the token with the same destination
     int rank_d, cnt_d;  // owners only: exclusive rank / group size among owners of d
     bool last_d;        // highest owner lane of its destination group
     int rank_e, cnt_e;  // valid only: same among valid lanes of expert e
@@ -179,6 +180,8 @@ __device__ __forceinline__ Item make_item(const Shape &sh, int64_t e64, int t_st
     const uint64_t vmask = ballot(it.valid);
     const uint64_t peers_d = match_key((uint32_t)it.d, sh.bits_R, vmask);
     it.owner = it.valid && ((peers_d & c.seg & mask_lt(c.lane)) == 0);
+    const uint64_t same = peers_d & c.seg;
+    it.owner_lane = it.valid && same ? __builtin_ctzll(same) : c.lane;
     const uint64_t po = peers_d & ballot(it.owner);
     it.rank_d = prefix_count(po);
     it.cnt_d = popc(po);
@@ -355,6 +358,16 @@ __device__ __forceinline__ void wave_bases(int *cnt, int n, const int *base) {
 // Ranking: every item of the wave's tokens [t0, t1) of source s gets its slot
 // (row_base * Nmax + running count, [DET] Approach) and, in the expand layout,
 // its row; run_d / run_e are the wave's running counters in LDS.
+// The expand index entry of a valid lane (alignment 1): at its expand row
+// re + rank_e, the staging row of (d, s) that holds its token -- row j, its
+// owner's slot relative to the source's row base -- and the lane.
+__device__ __forceinline__ void record_expand_row(const LayoutArgs &a, int s, const Item &it, int j, int re) {
+    const Shape &sh = a.sh;
+    const int64_t pos = (int64_t)re + it.rank_e;
+    if (!it.valid || (unsigned)j >= (unsigned)sh.Nmax || pos >= expand_rows_bound(sh)) return;
+    a.expand_row_src[pos] = (staging_region(sh, it.d, s) * sh.Nmax + j) | ((int64_t)it.k << 56);
+}
+
 __device__ __forceinline__ void rank_items(const LayoutArgs &a, bool expand, int s, int t0, int t1,
                                            const StepCtx &c, const int64_t (&first)[kBatch], bool have_first,
                                            int *run_d, int *run_e) {
@@ -364,11 +377,13 @@ __device__ __forceinline__ void rank_items(const LayoutArgs &a, bool expand, int
     walk_steps(sh, topk_src, t0, t1, c, first, have_first, expand, [&](const Item &it) {
         const int rd = it.owner ? run_d[it.d] : 0;
         const int re = (expand && it.valid) ? run_e[it.e] : 0;
+        const int slot = it.owner ? slot_base + rd + it.rank_d : -1;
         if (it.in) {
             const int64_t idx = ((int64_t)s * sh.T + it.t) * sh.K + it.k;
-            a.dst_slot[idx] = it.owner ? slot_base + rd + it.rank_d : -1;
+            a.dst_slot[idx] = slot;
             if (expand) a.expand_pos[idx] = it.valid ? re + it.rank_e : -1;
         }
+        if (expand && a.expand_row_src) record_expand_row(a, s, it, shfl(slot, it.owner_lane) - slot_base, re);
         if (it.last_d) run_d[it.d] = rd + it.rank_d + 1;
         if (expand && it.last_e) run_e[it.e] = re + it.rank_e + 1;
     });
@@ -849,7 +864,8 @@ __global__ void __launch_bounds__(kLayoutThreads) k_layout_fused(LayoutArgs a) {
 // need no other workgroup.  Writes the tables to memory when `writer`, keeps
 // the receive base of every destination in rbase[R] (LDS) when rbase is not
 // null, and hands every item's slot (row base 0: one source) and expand row
-// to on_item(t, k, slot, pos), in each wave's token order.  on_issued() runs
+// to on_item(item, slot, pos, own) -- own: the slot of the lane's owner (its
+// own slot for an owner) -- in each wave's token order.  on_issued() runs
 // right after the wave has issued its loads of the routing, so that loads it
 // issues queue behind them.  LDS as single_lds_bytes.
 template <int NW, bool EXPAND, typename OnIssued, typename OnItem>
@@ -924,7 +940,9 @@ __device__ __forceinline__ void layout_one_workgroup(const LayoutArgs &a, int *l
     walk_steps(sh, a.topk_idx, t0, t1, c, first, one_batch, EXPAND, [&](const Item &it) {
         const int rd = it.owner ? run_d[it.d] : 0;
         const int re = (EXPAND && it.valid) ? run_e[it.e] : 0;
-        if (it.in) on_item(it.t, it.k, it.owner ? rd + it.rank_d : -1, (EXPAND && it.valid) ? re + it.rank_e : -1);
+        const int slot = it.owner ? rd + it.rank_d : -1;
+        const int own = shfl(slot, it.owner_lane);
+        if (it.in) on_item(it, slot, (EXPAND && it.valid) ? re + it.rank_e : -1, own);
         if (it.last_d) run_d[it.d] = rd + it.rank_d + 1;
         if (EXPAND && it.last_e) run_e[it.e] = re + it.rank_e + 1;
     });
@@ -936,9 +954,10 @@ template <int NW, bool EXPAND>
 __global__ void __launch_bounds__(NW * kWave) k_layout_single(LayoutArgs a) {
     extern __shared__ int lds[];
     const int K = a.sh.K;
-    layout_one_workgroup<NW, EXPAND>(a, lds, true, nullptr, [] {}, [&](int t, int k, int slot, int pos) {
-        a.dst_slot[(int64_t)t * K + k] = slot;
-        if (EXPAND) a.expand_pos[(int64_t)t * K + k] = pos;
+    layout_one_workgroup<NW, EXPAND>(a, lds, true, nullptr, [] {}, [&](const Item &it, int slot, int pos, int own) {
+        a.dst_slot[(int64_t)it.t * K + it.k] = slot;
+        if (EXPAND) a.expand_pos[(int64_t)it.t * K + it.k] = pos;
+        if (EXPAND && a.expand_row_src && pos >= 0) record_expand_row(a, 0, it, own, pos - it.rank_e);
     });
 }
 
@@ -990,7 +1009,8 @@ __global__ void __launch_bounds__(NW * kWave) k_layout_dispatch_small(LayoutArgs
         }
     };
     for (int i = tid; i < NW * K; i += NT) slots[i] = -1;  // ordered by the layout's first barrier
-    layout_one_workgroup<NW, false>(a, lds, writer, rbase, load_token, [&](int t, int k, int slot, int) {
+    layout_one_workgroup<NW, false>(a, lds, writer, rbase, load_token, [&](const Item &it, int slot, int, int) {
+        const int t = it.t, k = it.k;
         if (writer) a.dst_slot[(int64_t)t * K + k] = slot;
         if (t >= g0 && t < g0 + NW) slots[(t - g0) * K + k] = slot;
     });

@@ -89,26 +89,6 @@ __device__ __forceinline__ void record_recv_row(const DispatchArgs &a, int s, in
         a.recv_row_src[i] = staging_region(sh, d, s) * sh.Nmax + j;
 }
 
-// The expand layout's index (alignment 1), recorded for token (s, t) by every
-// lane at once (all lanes active): each valid lane k < K (expert e,
-// destination d) stores, at its expand row, the staging row of (d, s) that
-// holds the token -- its owner's slot j, the owner being the lowest lane with
-// a slot on d -- and k.
-__device__ __forceinline__ void record_expand_rows(const DispatchArgs &a, int64_t g, int s, int e, int slot,
-                                                   uint64_t owners, int lane) {
-    const Shape &sh = a.sh;
-    const int d = lane < sh.K && e >= 0 ? rank_of(sh, e) : -1;
-    int j = -1;
-    for (uint64_t m = owners; m; m &= m - 1) {  // owners have distinct destinations
-        const int o = __builtin_ctzll(m);
-        if (rank_of(sh, read_lane(e, o)) == d) j = read_lane(slot, o) - row_base(sh, s) * sh.Nmax;
-    }
-    if (d < 0 || (unsigned)j >= (unsigned)sh.Nmax) return;
-    const int pos = a.expand_pos[g * sh.K + lane];
-    if ((uint64_t)pos < (uint64_t)a.recv_capacity_rows && pos < expand_rows_bound(sh))
-        a.expand_row_src[pos] = (staging_region(sh, d, s) * sh.Nmax + j) | ((int64_t)lane << 56);
-}
-
 // Staging row (d, s, j) to compact receive row i = recv_base[d] +
 // recv_psum[d][s] + j: the hidden row, its scales, and the per-row metadata
 // derived from the record.
