@@ -178,8 +178,10 @@ typedef struct ep_sizes {
  *                                Compact layouts and expand layouts with
  *                                alignment 1: its head holds the receive-row
  *                                index (8 bytes per receive row, rounded up
- *                                to 256 bytes) that a dispatch's scatter
- *                                writes and its copy epilogue reads, the
+ *                                to 256 bytes) that the copy epilogue reads,
+ *                                written by a dispatch's scatter (compact) or
+ *                                by the layout (expand, ep_layout_no_alloc
+ *                                included when a scratch is given); the
  *                                layout's own words follow.  Required by
  *                                ep_layout; may be NULL for ep_dispatch (the
  *                                epilogue then searches the receiver tables
@@ -245,7 +247,8 @@ int ep_layout(const ep_config_t *cfg, const int64_t *topk_idx_dev, const ep_layo
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same launches and the same tables as ep_layout, but the scratch is an
  * EP_NO_ALLOC_SCRATCH_BYTES array the library holds on each GPU it runs on
- * until the process ends, so layout->scratch_dev is ignored (may be NULL).
+ * until the process ends, so layout->scratch_dev is not required (may be
+ * NULL; when given, only the receive-row index at its head is written).
  * The call allocates and frees nothing.  A configuration whose layout words
  * (ep_sizes_t.layout_scratch less the receive-row index at its head, which
  * the array does not hold) exceed EP_NO_ALLOC_SCRATCH_BYTES returns
