@@ -20,11 +20,17 @@
 //                    row loaded before the current stores): Direct Recv X
 //                    (rows straight to the receive rows) and staging scatters
 //                    of at most 1 GiB of rows;
-//   k_epilogue_pf    compact epilogue, pipelined the same way over receive
-//                    rows (k_epilogue for rows wider than one pass);
+//   k_epilogue_indexed  compact epilogue, one wave per 2 KiB piece of a
+//                    receive row, its source found through the receive-row
+//                    index the scatter records in the layout's scratch;
+//   k_epilogue_pf    the compact epilogue without that index, pipelined the
+//                    same way as k_scatter_pf over receive rows (k_epilogue
+//                    for rows wider than one pass);
 //   k_epilogue_meta  Direct Recv X: scales and metadata only, one thread per
 //                    (row, item);
-//   k_epilogue_expand, k_expand_padding   the per-expert layout.
+//   k_epilogue_expand_indexed  the per-expert layout with alignment 1, in
+//                    expand-row order through the index the layout records;
+//   k_epilogue_expand, k_expand_padding   the per-expert layout otherwise.
 // On the hybrid path the same kernels address a destination's staging rows in
 // row form (segment = the source's scale-up index, then its scale-out index),
 // through staging_region.

@@ -355,9 +355,6 @@ __device__ __forceinline__ void wave_bases(int *cnt, int n, const int *base) {
     }
 }
 
-// Ranking: every item of the wave's tokens [t0, t1) of source s gets its slot
-// (row_base * Nmax + running count, [DET] Approach) and, in the expand layout,
-// its row; run_d / run_e are the wave's running counters in LDS.
 // The expand index entry of a valid lane (alignment 1): at its expand row
 // re + rank_e, the staging row of (d, s) that holds its token -- row j, its
 // owner's slot relative to the source's row base -- and the lane.
@@ -368,6 +365,10 @@ __device__ __forceinline__ void record_expand_row(const LayoutArgs &a, int s, co
     a.expand_row_src[pos] = (staging_region(sh, it.d, s) * sh.Nmax + j) | ((int64_t)it.k << 56);
 }
 
+// Ranking: every item of the wave's tokens [t0, t1) of source s gets its slot
+// (row_base * Nmax + running count, [DET] Approach) and, in the expand layout,
+// its row (and, with an expand index, that row's entry); run_d / run_e are the
+// wave's running counters in LDS.
 __device__ __forceinline__ void rank_items(const LayoutArgs &a, bool expand, int s, int t0, int t1,
                                            const StepCtx &c, const int64_t (&first)[kBatch], bool have_first,
                                            int *run_d, int *run_e) {
