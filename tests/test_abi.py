@@ -205,6 +205,20 @@ def test_size_accounting_pages_configuration():
     assert ex.recv_topk_weights == ex.recv_rows * 4 and ex.expand_pos == 16 * 2048 * K * 4
 
 
+def test_layout_scratch_holds_the_receive_row_index():
+    """The scratch's head: 8 bytes per receive row (a 256-byte multiple) for
+    compact layouts and unpadded expand layouts, nothing for padded expand
+    layouts; the same with or without Direct Recv X."""
+    def scratch(**kw):
+        return ep.ep_query_sizes(ep.make_config(2, 1000, 256, 4, 64, 8, 1000, **kw)).layout_scratch
+    index = (2 * 1000 * 4 * 8 + 255) // 256 * 256  # S*T*min(K,R) receive rows of 8 bytes
+    for cus in (32, 64):  # S*B units: per-unit counts, then the exchange words (epoch + one per unit)
+        assert scratch(num_layout_cus=cus) == index + cus * (8 + 64 + 1) * 4 + 4 + (1 + cus) * 8
+    assert scratch(direct_recv_x=True) == scratch()
+    expand_rows = 2 * 1000 * 4  # S*T*K
+    assert scratch(expand=True) - scratch(expand=True, alignment=4) == (expand_rows * 8 + 255) // 256 * 256
+
+
 def test_layout_scratch_grows_with_num_layout_cus():
     a = ep.ep_query_sizes(ep.make_config(1, 4096, 7168, 8, 256, 16, 4096, num_layout_cus=1))
     b = ep.ep_query_sizes(ep.make_config(1, 4096, 7168, 8, 256, 16, 4096, num_layout_cus=64))
