@@ -522,19 +522,50 @@ __device__ __forceinline__ void build_receiver_tables(const LayoutArgs &a, bool 
         });
         __syncthreads();
     }
+    // recv_psum: per destination, the exclusive prefix over sources of the
+    // per-(source, destination) totals.  Few sources (per-thread walk no
+    // longer than the scans' barriers): one thread per destination walks
+    // them.  Many: the totals go to recv_psum[d][s] in parallel, then the
+    // workgroup scans each destination's row in place.
     int *tot_d = part;  // [R] totals per destination (R <= 64)
-    for (int d = tid; d < R; d += kLayoutThreads) {
-        int run = 0;
-        for (int q = 0; q < S; ++q) {
-            a.recv_psum[(int64_t)d * (S + 1) + q] = run;
+    const bool walk = (int64_t)S * (fits ? 1 : B) <= 64 * (int64_t)R;
+    if (!walk) {
+        for (int64_t p = tid; p < (int64_t)S * R; p += kLayoutThreads) {
+            const int q = (int)(p / R), d = (int)(p - (int64_t)q * R);
+            int c = 0;
             if (fits) {
-                run += tot[q * R + d];
+                c = tot[p];
             } else {
-                for (int bb = 0; bb < B; ++bb) run += a.blk_cnt_rank[((int64_t)q * B + bb) * R + d];
+                for (int bb = 0; bb < B; ++bb) c += a.blk_cnt_rank[((int64_t)q * B + bb) * R + d];
+            }
+            a.recv_psum[(int64_t)d * (S + 1) + q] = c;
+        }
+        __syncthreads();
+        tot_d = lds;  // the per-(source, destination) totals in LDS are no longer needed
+        for (int d = 0; d < R; ++d) {
+            int32_t *ps = a.recv_psum + (int64_t)d * (S + 1);
+            const int total = block_exclusive_scan<kLayoutThreads>(ps, S, part);
+            if (tid == 0) {
+                ps[S] = total;
+                tot_d[d] = total;
             }
         }
-        a.recv_psum[(int64_t)d * (S + 1) + S] = run;
-        tot_d[d] = run;
+        __syncthreads();
+    }
+    for (int d = tid; d < R; d += kLayoutThreads) {
+        if (walk) {
+            int run = 0;
+            for (int q = 0; q < S; ++q) {
+                a.recv_psum[(int64_t)d * (S + 1) + q] = run;
+                if (fits) {
+                    run += tot[q * R + d];
+                } else {
+                    for (int bb = 0; bb < B; ++bb) run += a.blk_cnt_rank[((int64_t)q * B + bb) * R + d];
+                }
+            }
+            a.recv_psum[(int64_t)d * (S + 1) + S] = run;
+            tot_d[d] = run;
+        }
         if (sh.n_out > 1) {
             // Hybrid row form: prefix over scale-up segments; segment u
             // holds the sources s with s % n_up == u.

@@ -122,6 +122,20 @@ def test_direct_recv_x_small(w):
     _full_case(w, 11, EDGE, direct=True)
 
 
+@pytest.mark.parametrize("w", [
+    Workload("sources_1000_fits", S=1000, T=3, H=8, K=2, E=1024, R=2, Nmax=3),
+    Workload("sources_600_fits_expand", S=600, T=4, H=8, K=2, E=1024, R=2, Nmax=4, expand=True),
+    Workload("sources_700_hybrid", S=700, T=3, H=8, K=2, E=256, R=4, Nmax=3, n_out=7),
+], ids=lambda w: w.name)
+def test_receiver_tables_of_many_sources(w):
+    """Many sources for few destinations: the receiver tables' prefix over
+    sources is a workgroup scan per destination instead of one thread's walk
+    (per-source totals gathered in LDS, or -- the hybrid case's 700 sources x 4
+    destinations -- straight from the unit counts); the row form's segments
+    on top."""
+    _full_case(w, 37, EDGE)
+
+
 @pytest.mark.parametrize("mode", ["staging", "direct", "expand"])
 def test_receiver_tables_beyond_lds(mode):
     """R * (S + 1) > 8192 table entries: the epilogues search recv_base and
