@@ -84,7 +84,12 @@ constexpr int kIndexedCpw = EP_INDEXED_CPW;
 // short-lived waves keep the write stream closer to a fill's rate (a plain
 // fill of 3.3 GB in 1 KiB per wave ran at 6.9 TB/s, in 14 KiB per wave at
 // 5.5).  16 x 2048 tokens: scatter 678 -> 606 us (2 KiB pieces 668 us); at
-// 4096 tokens the pieces lose to the pipelined kernel (70.5 -> 73.3 us).
+// 4096 tokens the pieces lose to the pipelined kernel (70.5 -> 73.3 us).  The
+// pieces' staging stores are non-temporal: rows that large leave the
+// Infinity Cache full of dirty lines that the copy epilogue then pays to
+// write back (16 x 2048 tokens: scatter 600 -> 607 us, epilogue 1193 -> 1132
+// us, step 2515 -> 2461 us), while below 1 GiB the cache absorbs the staging
+// writes and the epilogue reads them from it (non-temporal: 14% slower).
 #ifndef EP_SCATTER_BLOCKS
 #define EP_SCATTER_BLOCKS (1 << 20)
 #endif
@@ -129,7 +134,7 @@ constexpr int kIndexedCpw = EP_INDEXED_CPW;
 // every owner lane's destination d (with Direct Recv X, used here only for
 // rows wider than one pass, to the compact receive row recv_base[d] +
 // recv_psum[d][s] + j), with the fp8 scales and the metadata record.
-template <int CPL>
+template <int CPL, bool NT_STAGING = EP_SCATTER_NT_STORE != 0>
 __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
     const Shape &sh = a.sh;
     const int lane = lane_id();
@@ -193,7 +198,7 @@ __global__ void __launch_bounds__(kThreads) k_scatter(DispatchArgs a) {
 #pragma unroll
                     for (int q = 0; q < CPL; ++q) {
                         const int c = c0 + q * kWave + lane;
-                        if (c < c_hi) st16<EP_SCATTER_NT_STORE>(dst + (int64_t)c * 16, v[q]);
+                        if (c < c_hi) st16<NT_STAGING>(dst + (int64_t)c * 16, v[q]);
                     }
                 }
             }
@@ -845,7 +850,7 @@ hipError_t launch_scatter(const DispatchArgs &a, hipStream_t stream) {
     if (!a.sh.direct && EP_SCATTER_SLICES == 1 && bound > (int64_t)EP_SCATTER_PIPELINE_MAX_BYTES) {
         DispatchArgs b = a;
         b.slices = (nchunks + kWave - 1) / kWave;  // 1 KiB pieces
-        hipLaunchKernelGGL(k_scatter<1>, dim3(grid_for((int64_t)a.sh.S * a.sh.T * b.slices, EP_SCATTER_BLOCKS)),
+        hipLaunchKernelGGL((k_scatter<1, true>), dim3(grid_for((int64_t)a.sh.S * a.sh.T * b.slices, EP_SCATTER_BLOCKS)),
                            dim3(kThreads), 0, stream, b);
         return hipGetLastError();
     }
