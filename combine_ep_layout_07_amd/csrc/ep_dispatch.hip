@@ -66,6 +66,9 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #ifndef EP_EPILOGUE_BLOCKS
 #define EP_EPILOGUE_BLOCKS (1 << 20)
 #endif
+#ifndef EP_EXPAND_PULL_NT_LOAD
+#define EP_EXPAND_PULL_NT_LOAD 0  // the expand epilogue re-reads staging rows: through the caches
+#endif
 #ifndef EP_INDEXED_CPW
 #define EP_INDEXED_CPW 2  // chunks per lane of a k_epilogue_indexed piece
 #endif
@@ -573,7 +576,7 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_expand_indexed(DispatchAr
 #pragma unroll
         for (int q = 0; q < CPW; ++q) {
             const int c = (p * CPW + q) * kWave + lane;
-            if (c < nchunks) v[q] = ld16<false>(a.staging_x + row * sh.row_bytes + (int64_t)c * 16);
+            if (c < nchunks) v[q] = ld16<EP_EXPAND_PULL_NT_LOAD>(a.staging_x + row * sh.row_bytes + (int64_t)c * 16);
         }
 #pragma unroll
         for (int q = 0; q < CPW; ++q) {
