@@ -99,6 +99,16 @@ constexpr int kIndexedCpw = EP_INDEXED_CPW;
 #ifndef EP_SCATTER_PIPELINE_MAX_BYTES
 #define EP_SCATTER_PIPELINE_MAX_BYTES (1ll << 30)
 #endif
+// Direct Recv X writes its rows straight to the receive rows (non-temporal),
+// pipelined (k_scatter_pf) below EP_DIRECT_PIECES_MIN_BYTES of rows (bound
+// S*T*min(K,R) rows) and in 2 KiB pieces per wave from there (k_scatter<2>, column
+// slices of 128 chunks).  Measured on MI355X, whole steps at H = 7168 bf16,
+// top-8 of 256 on 16 ranks: 8192 tokens 349 -> 311 us, 16384 675 -> 658 us,
+// 32768 1329 -> 1307 us, 4096 (470 MB) 164.2 -> 164.8 us; 8192 tokens of
+// H = 4096 rows (537 MB) 141.7 -> 136.4 us; 1 KiB pieces lost at every size.
+#ifndef EP_DIRECT_PIECES_MIN_BYTES
+#define EP_DIRECT_PIECES_MIN_BYTES (1ll << 29)
+#endif
 // Compact-layout problems of at most this many tokens (all sources) with
 // rows of at most EP_FUSED_DISPATCH_MAX_ROW bytes dispatch in one launch
 // (k_dispatch_fused) when both phases are asked for.  Measured on MI355X:
@@ -850,6 +860,13 @@ hipError_t launch_scatter(const DispatchArgs &a, hipStream_t stream) {
     if ((int64_t)a.sh.S * a.sh.T == 0) return hipSuccess;
     const int nchunks = a.sh.row_bytes / 16;
     const int64_t bound = (int64_t)a.sh.S * a.sh.T * (a.sh.K < a.sh.R ? a.sh.K : a.sh.R) * a.sh.row_bytes;
+    if (a.sh.direct && EP_SCATTER_SLICES == 1 && bound >= (int64_t)EP_DIRECT_PIECES_MIN_BYTES) {
+        DispatchArgs b = a;
+        b.slices = (nchunks + 2 * kWave - 1) / (2 * kWave);  // 2 KiB pieces
+        hipLaunchKernelGGL(k_scatter<2>, dim3(grid_for((int64_t)a.sh.S * a.sh.T * b.slices, EP_SCATTER_BLOCKS)),
+                           dim3(kThreads), 0, stream, b);
+        return hipGetLastError();
+    }
     if (!a.sh.direct && EP_SCATTER_SLICES == 1 && bound > (int64_t)EP_SCATTER_PIPELINE_MAX_BYTES) {
         DispatchArgs b = a;
         b.slices = (nchunks + kWave - 1) / kWave;  // 1 KiB pieces

@@ -271,15 +271,17 @@ def test_rows_wider_than_one_pass(mode):
     _full_case(w, 51, EDGE, direct=mode == "direct")
 
 
+@pytest.mark.parametrize("direct", [False, True], ids=["staging", "direct"])
 @pytest.mark.parametrize("w", [
     Workload("pieces_bf16_ragged", S=5, T=2048, H=7000, K=8, E=256, R=16, Nmax=2048),
     Workload("pieces_fp8_ragged", S=8, T=2048, H=8320, K=8, E=256, R=16, Nmax=2048, dtype="fp8"),
 ], ids=lambda w: w.name)
-def test_staging_scatter_in_pieces(w):
-    """Staging rows of more than 1 GiB (bound S*T*min(K,R) rows) take the
-    scatter in 1 KiB pieces per wave: ragged last pieces (875 and 520 chunks
-    per row: 14 and 9 pieces), fp8 scales, masked and duplicate lanes."""
-    _full_case(w, 61, EDGE)
+def test_scatter_in_pieces(w, direct):
+    """Rows of more than 1 GiB (bound S*T*min(K,R) rows) take the staging
+    scatter in 1 KiB pieces per wave, and Direct Recv X (from 512 MiB) in 2 KiB
+    pieces: ragged last pieces (875 and 520 chunks per row), fp8 scales,
+    masked and duplicate lanes."""
+    _full_case(w, 61, EDGE, direct=direct)
 
 
 @pytest.mark.parametrize("w", [WORKLOADS[3], SMALL[0], SMALL[1], SMALL[7], SMALL[8], SMALL[9], HYBRID[1], HYBRID[2],
