@@ -13,13 +13,15 @@
 // wavefront moves one row at a time, lane l taking chunks c = l + 64*i, the
 // whole row (or a CPL-chunk slice of it) loaded into VGPRs before any store, so
 // every lane has CPL independent 16-byte loads in flight.
-//   k_scatter        one wave per token (or per 1 KiB piece of its row, for
-//                    staging rows of more than 1 GiB), its row stored to
-//                    every owner's staging row (plus scales and the record);
+//   k_scatter        one wave per token (or per piece of its row: 1 KiB for
+//                    staging rows of more than 1 GiB, 2 KiB for Direct Recv X
+//                    from 512 MiB of rows), its row stored to every owner's
+//                    staging row or, with Direct Recv X, receive row (plus
+//                    scales and the record);
 //   k_scatter_pf     the same with each wave pipelining several tokens (next
 //                    row loaded before the current stores): Direct Recv X
-//                    (rows straight to the receive rows) and staging scatters
-//                    of at most 1 GiB of rows;
+//                    below 512 MiB of rows and staging scatters of at most
+//                    1 GiB of rows;
 //   k_epilogue_indexed  compact epilogue, one wave per 2 KiB piece of a
 //                    receive row, its source found through the receive-row
 //                    index the scatter records in the layout's scratch;
