@@ -271,16 +271,22 @@ def test_rows_wider_than_one_pass(mode):
     _full_case(w, 51, EDGE, direct=mode == "direct")
 
 
-@pytest.mark.parametrize("direct", [False, True], ids=["staging", "direct"])
-@pytest.mark.parametrize("w", [
+PIECES = [
     Workload("pieces_bf16_ragged", S=5, T=2048, H=7000, K=8, E=256, R=16, Nmax=2048),
     Workload("pieces_fp8_ragged", S=8, T=2048, H=8320, K=8, E=256, R=16, Nmax=2048, dtype="fp8"),
-], ids=lambda w: w.name)
+    Workload("pieces_hybrid_2x4", S=8, T=2048, H=7000, K=8, E=256, R=16, Nmax=2048, n_out=2),
+]
+
+
+@pytest.mark.parametrize("w,direct", [(w, d) for w in PIECES for d in (False, True)] +
+                         [(Workload("pieces_expand_a4", S=8, T=2048, H=7000, K=8, E=256, R=16, Nmax=2048,
+                                    expand=True, alignment=4), False)],
+                         ids=lambda c: getattr(c, "name", None) or ("direct" if c else "staging"))
 def test_scatter_in_pieces(w, direct):
     """Rows of more than 1 GiB (bound S*T*min(K,R) rows) take the staging
     scatter in 1 KiB pieces per wave, and Direct Recv X (from 512 MiB) in 2 KiB
-    pieces: ragged last pieces (875 and 520 chunks per row), fp8 scales,
-    masked and duplicate lanes."""
+    pieces: ragged last pieces (875 and 520 chunks per row), fp8 scales, the
+    hybrid row form, a padded expand layout, masked and duplicate lanes."""
     _full_case(w, 61, EDGE, direct=direct)
 
 
