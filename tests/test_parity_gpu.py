@@ -425,6 +425,49 @@ def test_one_launch_layout_parity(name):
     _full_case(SINGLE[name], 62, EDGE)
 
 
+SOURCE_TOP8 = [  # one source, compact, top-8, from just above the one-workgroup layout to 16385 tokens
+    Workload("top8_257", S=1, T=257, H=64, K=8, E=256, R=16, Nmax=257),
+    Workload("top8_ragged_4097", S=1, T=4097, H=64, K=8, E=256, R=16, Nmax=4100),
+    Workload("top8_r64_e1024", S=1, T=3000, H=64, K=8, E=1024, R=64, Nmax=3000),
+    Workload("top8_r64_e64", S=1, T=2000, H=64, K=8, E=64, R=64, Nmax=2000),
+    Workload("top8_r1", S=1, T=5000, H=64, K=8, E=8, R=1, Nmax=5000),
+    Workload("top8_r3_e24", S=1, T=700, H=64, K=8, E=24, R=3, Nmax=700),
+    Workload("top8_16384", S=1, T=16384, H=64, K=8, E=256, R=16, Nmax=16384),
+    Workload("top8_16385", S=1, T=16385, H=64, K=8, E=256, R=16, Nmax=16385),
+]
+
+
+@pytest.mark.parametrize("w", SOURCE_TOP8, ids=lambda w: w.name)
+def test_single_source_layout_sizes(w):
+    """One source at top-8: ragged unit counts, one to 64 destinations, 64 to
+    1024 experts, up to 16385 tokens, with masked, out-of-range and duplicate
+    lanes; dispatch and combine follow from its tables.  Three layouts in a
+    row into tables filled with junk stay exact, and so does routing that
+    starts 8 bytes off a 16-byte boundary (the alignment the ABI requires)."""
+    _full_case(w, 83, EDGE)
+    inputs = generate(w, 84, with_x=False, masked_frac=0.1, invalid_frac=0.02, dup_frac=0.2)
+    inputs["x"] = np.zeros((w.S, w.T, 16), np.uint8)
+    dev = upload(w, inputs)
+    lay_o = oracle.layout(w.S, w.T, w.K, w.E, w.R, w.Nmax, inputs["topk_idx"], w.expand, w.alignment, w.n_out)
+    cfg = ep.config_for(w)
+    L = ep.alloc_layout(cfg)
+    for _ in range(3):
+        for t in L.tables().values():
+            t.fill_(-7)
+        ep.ep_layout(cfg, dev["topk_idx"], L)
+        torch.cuda.synchronize()
+        compare_tables(layout_host(L), lay_o)
+    flat = torch.empty(dev["topk_idx"].numel() + 1, dtype=torch.int64, device="cuda")
+    off = flat[1:].view(dev["topk_idx"].shape)
+    off.copy_(dev["topk_idx"])
+    assert off.data_ptr() % 16 == 8
+    for t in L.tables().values():
+        t.fill_(-7)
+    ep.ep_layout(cfg, off, L)
+    torch.cuda.synchronize()
+    compare_tables(layout_host(L), lay_o)
+
+
 def test_dispatch_is_bitwise_reproducible():
     w = WORKLOADS[4]
     inputs = generate(w, seed_for(4))
