@@ -561,13 +561,12 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_indexed(DispatchArgs a) {
 // once per row, through the caches (cached loads: the repeat reads find
 // some of it there).  Measured on MI355X at 16 x 2048 tokens, H = 7168 bf16,
 // against the one-wave-per-staging-row kernel: epilogue 1235 -> 1198 us in
-// the step, 1235 -> 1135 us back to back, scatter 603 -> 617 us (recording
-// the index), step 2552 -> 2535 us; non-temporal loads 1209 / 1147 us;
+// the step, 1235 -> 1135 us back to back; non-temporal loads 1209 / 1147 us;
 // pieces of 1 / 4 / 7 / 14 KiB: 1285 / 1305 / 1341 / 1430 us in the step.
-// At 4096 tokens: 150 -> 142 us back to back; with alignment 128 (half the
-// rows padding, marked in the index by the padding kernel run first) 206 ->
-// 210 us and the step 0.388 -> 0.419 ms, so padded layouts keep the other
-// kernel.
+// At 4096 tokens: 150 -> 142 us back to back.  A trial with alignment 128
+// (half the rows padding, marked in the index by the padding kernel run
+// first) measured 206 -> 210 us and the step 0.388 -> 0.419 ms, so padded
+// layouts keep the other kernel and have no index.
 template <int CPW>
 __global__ void __launch_bounds__(kThreads) k_epilogue_expand_indexed(DispatchArgs a) {
     const Shape &sh = a.sh;
