@@ -75,6 +75,17 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #define EP_INDEXED_CPW 2  // chunks per lane of a k_epilogue_indexed piece
 #endif
 constexpr int kIndexedCpw = EP_INDEXED_CPW;
+// The indexed copy epilogue's grid covers this many thirds of the pieces of
+// the receive capacity; waves past the end take further pieces (grid-stride).
+// The host cannot know how many rows are filled, and each wave launched past
+// them still costs a launch.  Measured on MI355X, whole steps (filled / capacity rows):
+// 8192 tokens H = 4096 Zipf (35731 / 65536) 231-233 -> 225-226 us, the same
+// as a grid sized to the filled rows exactly; 4096 tokens H = 7168 (26758 /
+// 32768) 278.5-279.7 -> 276.3-276.6 us; fp8 188-189 -> 187-188 us; with half
+// the capacity 225 / 278-280 / 186 us.
+#ifndef EP_INDEXED_GRID_THIRDS
+#define EP_INDEXED_GRID_THIRDS 2
+#endif
 // The staging scatter, with no grid-stride cap (measured at 16 x 2048 tokens:
 // 708 us capped at 2048 workgroups, 674 us uncapped), takes one of two forms.
 // When its staging rows come to at most EP_SCATTER_PIPELINE_MAX_BYTES: the
@@ -506,11 +517,13 @@ __device__ __forceinline__ int last_le(const int32_t *tab, int n, int key) {
 }
 
 // Compact copy epilogue with the receive-row index (the staging path when the
-// layout's scratch holds the index the scatter recorded): one wave per piece
+// layout's scratch holds the index the scatter recorded): a wave per piece
 // of CPW chunks per lane (2 KiB at CPW = 2) of receive row i, which loads the
 // row's staging index, then its piece, and stores it; piece 0 also moves the
 // scales and the metadata.  Short-lived waves with one dependent load ahead of
-// the copy.  Measured on MI355X: 4096 tokens H = 7168 bf16, epilogue 129 ->
+// the copy; the grid covers two thirds of the capacity's pieces
+// (EP_INDEXED_GRID_THIRDS), and a wave takes a further piece when the filled
+// rows reach past it.  Measured on MI355X: 4096 tokens H = 7168 bf16, epilogue 129 ->
 // 125 us inside the step (134 -> 123 us back to back); 8192 tokens H = 4096
 // 106 -> 101 us; fp8 63 -> 62 us.  1 / 4 KiB pieces: 140 / 138 us at 4096
 // tokens.  Without the index, pieces that first search the tables were far
@@ -822,7 +835,8 @@ struct EpilogueL {
             hipLaunchKernelGGL(k_epilogue_expand<CPL>, dim3(grid_for(rows, EP_EXPAND_BLOCKS)), dim3(kThreads),
                                std::max<size_t>(fits ? tab : 0, EP_EXPAND_LDS), st, a, (int)fits);
         else if (a.recv_row_src) {
-            hipLaunchKernelGGL(k_epilogue_indexed<kIndexedCpw>, dim3(grid_for(rows * pieces, EP_EPILOGUE_BLOCKS)),
+            const int64_t units = (rows * pieces * EP_INDEXED_GRID_THIRDS + 2) / 3;
+            hipLaunchKernelGGL(k_epilogue_indexed<kIndexedCpw>, dim3(grid_for(units, EP_EPILOGUE_BLOCKS)),
                                dim3(kThreads), 0, st, a);
         } else if (a.slices == 1 && a.sh.row_bytes / 16 <= CPL * kWave)
             hipLaunchKernelGGL(k_epilogue_pf<CPL>, dim3(grid_for(rows, EP_EPILOGUE_BLOCKS)), dim3(kThreads),
