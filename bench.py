@@ -761,7 +761,7 @@ def main():
     b = head["alg_bytes_per_step"]
     dom = head["dominant"]["stage"]
     dom_kernel = {"layout": "k_layout", "scatter": "k_scatter", "combine": "k_combine",
-                  "epilogue": ("k_epilogue_expand_indexed" if w.alignment == 1 else "k_epilogue_expand")
+                  "epilogue": ("k_epilogue_expand_indexed" if w.alignment == 1 else "k_epilogue_expand_pieces")
                   if w.expand else "k_epilogue_indexed"}[dom]
     res = {
         "metric": METRIC,

@@ -32,12 +32,12 @@
 //                    (row, item);
 //   k_epilogue_expand_indexed  the per-expert layout with alignment 1, in
 //                    expand-row order through the index the layout records;
-//   k_epilogue_expand, k_expand_padding   the per-expert layout otherwise.
+//   k_epilogue_expand_pieces, k_expand_padding   the per-expert layout
+//                    otherwise (in 2 KiB pieces of staging rows, then the
+//                    padding rows).
 // On the hybrid path the same kernels address a destination's staging rows in
 // row form (segment = the source's scale-up index, then its scale-out index),
 // through staging_region.
-#include <algorithm>
-
 #include "ep_device.h"
 #include "ep_kernels.h"
 #include "ep_rows.h"
@@ -140,18 +140,11 @@ constexpr int kIndexedCpw = EP_INDEXED_CPW;
 #ifndef EP_COPY_BLOCKS
 #define EP_COPY_BLOCKS 2048
 #endif
-// The expand epilogue runs one wave per staging row with no grid-stride cap:
-// its per-row chain (locate, record, the lanes' expand rows) needs many waves
-// in flight.  Measured on MI355X at 16 x 2048 tokens: 2048 / 16384 / 65536
-// workgroups 1349 / 1327 / 1280 us.  Its launch also asks for enough LDS that
-// at most two workgroups are resident per CU (2 waves per SIMD, the occupancy
-// the compact epilogue's registers give it): 1284 -> 1228 us there, while 3
-// waves per SIMD measured the same as the 4 its registers allow.
-#ifndef EP_EXPAND_LDS
-#define EP_EXPAND_LDS lds_to_cap_residency(2)
-#endif
-#ifndef EP_EXPAND_BLOCKS
-#define EP_EXPAND_BLOCKS (1 << 20)
+// Chunks per lane of a k_epilogue_expand_pieces piece.  Measured on MI355X
+// at 4096 tokens, H = 7168 bf16, expert alignment 128, whole steps: 1 / 2 / 4
+// KiB pieces 409 / 380 / 389 us; one wave per staging row 384 us.
+#ifndef EP_EXPAND_PIECE_CPW
+#define EP_EXPAND_PIECE_CPW 2
 #endif
 
 // ----------------------------------------------------------------- scatter
@@ -659,58 +652,59 @@ __global__ void __launch_bounds__(kThreads) k_epilogue_meta(DispatchArgs a, int 
 }
 
 // -------------------------------------------------- expand copy epilogue
-// One wave per filled staging row (d, s, j): the row goes to the expand row of
-// every lane of that token on destination d (one per lane, duplicates
-// included), with the source index and the lane's weight.
-template <int CPL>
-__global__ void __launch_bounds__(kThreads) k_epilogue_expand(DispatchArgs a, int tables_in_lds) {
+// Without the expand index: one wave per piece of CPW chunks per lane (2 KiB
+// at CPW = 2) of filled staging row i (compact receive-row order), which finds
+// (d, s, j) in the receiver tables (staged in LDS), loads its piece of the
+// staging row together with the row's record, then the expand rows of the
+// token's lanes on d, and stores the piece to each (one per lane, duplicates
+// included); piece 0 also writes the rows' scales, source index and the
+// lanes' weights.  Used for expert alignment > 1, or without a layout scratch.
+template <int CPW>
+__global__ void __launch_bounds__(kThreads) k_epilogue_expand_pieces(DispatchArgs a, int tables_in_lds) {
     const Shape &sh = a.sh;
     extern __shared__ int32_t lds_tab[];
     const int32_t *tab = stage_tables(a, lds_tab, tables_in_lds != 0);
     const int32_t *rbase = tab ? tab : a.recv_base;
     const int32_t *rpsum = tab ? tab + sh.R + 1 : a.recv_psum;
     const int lane = lane_id();
-    const int n_rows = (int)min((int64_t)a.recv_base[sh.R], a.recv_capacity_rows);
     const int nchunks = sh.row_bytes / 16;
-    const int wave0 = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-    const int nwaves = gridDim.x * kWavesPerBlock;
-    for (int64_t i64 = wave0; i64 < n_rows; i64 += nwaves) {  // 64-bit: rows may approach 2^31
-        const int i = (int)i64;
+    const int P = (nchunks + CPW * kWave - 1) / (CPW * kWave);
+    const int64_t n_units = min((int64_t)rbase[sh.R], compact_rows_bound(sh)) * P;
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t u = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; u < n_units; u += nwaves) {
+        const int i = (int)(u / P);  // < S*T*min(K,R) <= 2^31 - 1
+        const int p = (int)(u - (int64_t)i * P);
         int d, s, j;
         locate_row(rbase, rpsum, sh.R, sh.S, i, lane, d, s, j);
         if ((unsigned)j >= (unsigned)sh.Nmax) continue;  // never true for tables of one layout
         const int64_t row = staging_region(sh, d, s) * sh.Nmax + j;
+        u32x4 v[CPW];
+#pragma unroll
+        for (int q = 0; q < CPW; ++q) {
+            const int c = (p * CPW + q) * kWave + lane;
+            if (c < nchunks) v[q] = ld16<EP_EPILOGUE_NT_LOAD>(a.staging_x + row * sh.row_bytes + (int64_t)c * 16);
+        }
         const int32_t *meta = a.staging_meta + row * sh.meta_words;
         const int t = meta[0];
+        const int e = lane < sh.K ? meta[1 + lane] : -1;
         if ((unsigned)t >= (unsigned)sh.T) continue;  // never true for staging rows the scatter wrote
         int pos = -1, wbits = 0;
-        if (lane < sh.K) {
-            const int e = meta[1 + lane];
-            if ((unsigned)e < (unsigned)sh.E && rank_of(sh, e) == d) {
-                pos = a.expand_pos[((int64_t)s * sh.T + t) * sh.K + lane];
-                wbits = meta[1 + sh.K + lane];
-            }
+        if (lane < sh.K && (unsigned)e < (unsigned)sh.E && rank_of(sh, e) == d) {
+            pos = a.expand_pos[((int64_t)s * sh.T + t) * sh.K + lane];
+            wbits = meta[1 + sh.K + lane];
         }
         const uint64_t lanes_on_d = ballot(pos >= 0);
-        const uint8_t *src = a.staging_x + row * sh.row_bytes;
-        for (int c0 = 0; c0 < nchunks; c0 += CPL * kWave) {
-            u32x4 v[CPL];
+        for (uint64_t m = lanes_on_d; m; m &= m - 1) {
+            const int r = read_lane(pos, __builtin_ctzll(m));
+            if ((uint64_t)r >= (uint64_t)a.recv_capacity_rows) continue;
+            uint8_t *dst = a.recv_x + (int64_t)r * sh.row_bytes;
 #pragma unroll
-            for (int q = 0; q < CPL; ++q) {
-                const int c = c0 + q * kWave + lane;
-                if (c < nchunks) v[q] = ld16<EP_EPILOGUE_NT_LOAD>(src + (int64_t)c * 16);
-            }
-            for (uint64_t m = lanes_on_d; m; m &= m - 1) {
-                const int r = read_lane(pos, __builtin_ctzll(m));
-                if ((uint64_t)r >= (uint64_t)a.recv_capacity_rows) continue;
-                uint8_t *dst = a.recv_x + (int64_t)r * sh.row_bytes;
-#pragma unroll
-                for (int q = 0; q < CPL; ++q) {
-                    const int c = c0 + q * kWave + lane;
-                    if (c < nchunks) st16<EP_EPILOGUE_NT_STORE>(dst + (int64_t)c * 16, v[q]);
-                }
+            for (int q = 0; q < CPW; ++q) {
+                const int c = (p * CPW + q) * kWave + lane;
+                if (c < nchunks) st16<EP_EPILOGUE_NT_STORE>(dst + (int64_t)c * 16, v[q]);
             }
         }
+        if (p != 0) continue;
         for (uint64_t m = lanes_on_d; m; m &= m - 1) {
             const int k = __builtin_ctzll(m);
             const int r = read_lane(pos, k);
@@ -831,9 +825,13 @@ struct EpilogueL {
             hipLaunchKernelGGL(k_epilogue_expand_indexed<kIndexedCpw>,
                                dim3(grid_for(a.recv_capacity_rows * pieces, EP_EPILOGUE_BLOCKS)), dim3(kThreads), 0,
                                st, a);
-        else if (a.sh.expand)
-            hipLaunchKernelGGL(k_epilogue_expand<CPL>, dim3(grid_for(rows, EP_EXPAND_BLOCKS)), dim3(kThreads),
-                               std::max<size_t>(fits ? tab : 0, EP_EXPAND_LDS), st, a, (int)fits);
+        else if (a.sh.expand) {
+            constexpr int cpw = EP_EXPAND_PIECE_CPW;
+            const int64_t xp = (a.sh.row_bytes / 16 + cpw * kWave - 1) / (cpw * kWave);
+            hipLaunchKernelGGL(k_epilogue_expand_pieces<cpw>,
+                               dim3(grid_for((rows * xp * EP_INDEXED_GRID_THIRDS + 2) / 3, EP_EPILOGUE_BLOCKS)),
+                               dim3(kThreads), fits ? tab : 0, st, a, (int)fits);
+        }
         else if (a.recv_row_src) {
             const int64_t units = (rows * pieces * EP_INDEXED_GRID_THIRDS + 2) / 3;
             hipLaunchKernelGGL(k_epilogue_indexed<kIndexedCpw>, dim3(grid_for(units, EP_EPILOGUE_BLOCKS)),
