@@ -38,6 +38,8 @@
 // On the hybrid path the same kernels address a destination's staging rows in
 // row form (segment = the source's scale-up index, then its scale-out index),
 // through staging_region.
+#include <algorithm>
+
 #include "ep_device.h"
 #include "ep_kernels.h"
 #include "ep_rows.h"
@@ -75,16 +77,24 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 #define EP_INDEXED_CPW 2  // chunks per lane of a k_epilogue_indexed piece
 #endif
 constexpr int kIndexedCpw = EP_INDEXED_CPW;
-// The indexed copy epilogue's grid covers this many thirds of the pieces of
-// the receive capacity; waves past the end take further pieces (grid-stride).
+// The indexed copy epilogue's grid covers this many sixths of the pieces of
+// the receive capacity (and the expand epilogue's without the index of its
+// staging-row bound); waves past the end take further pieces (grid-stride).
 // The host cannot know how many rows are filled, and each wave launched past
-// them still costs a launch.  Measured on MI355X, whole steps (filled / capacity rows):
-// 8192 tokens H = 4096 Zipf (35731 / 65536) 231-233 -> 225-226 us, the same
-// as a grid sized to the filled rows exactly; 4096 tokens H = 7168 (26758 /
-// 32768) 278.5-279.7 -> 276.3-276.6 us; fp8 188-189 -> 187-188 us; with half
-// the capacity 225 / 278-280 / 186 us.
-#ifndef EP_INDEXED_GRID_THIRDS
-#define EP_INDEXED_GRID_THIRDS 2
+// them still costs a launch.  Measured on MI355X, whole steps (filled /
+// capacity rows): 8192 tokens H = 4096 Zipf (35731 / 65536) 231-233 ->
+// 225-226 us, the same as a grid sized to the filled rows exactly; 4096
+// tokens H = 7168 (26758 / 32768) 278.5-279.7 -> 276.3-276.6 us; fp8 188-189
+// -> 187-188 us; with half the capacity (3 sixths) 225 / 278-280 / 186 us.
+#ifndef EP_INDEXED_GRID_SIXTHS
+#define EP_INDEXED_GRID_SIXTHS 4
+#endif
+// Waves per workgroup of k_epilogue_indexed.  Measured on MI355X, whole
+// steps against 4 waves: 2 waves 1 us faster at 4096 tokens H = 7168 bf16,
+// 2-6 us slower at 8192 tokens H = 4096 and 3-5 us slower in fp8; 1 wave up
+// to 15 us slower; 8 / 16 waves 5 / 20 us slower at 4096 tokens.
+#ifndef EP_INDEXED_WAVES
+#define EP_INDEXED_WAVES 4
 #endif
 // The staging scatter, with no grid-stride cap (measured at 16 x 2048 tokens:
 // 708 us capped at 2048 workgroups, 674 us uncapped), takes one of two forms.
@@ -515,22 +525,22 @@ __device__ __forceinline__ int last_le(const int32_t *tab, int n, int key) {
 // row's staging index, then its piece, and stores it; piece 0 also moves the
 // scales and the metadata.  Short-lived waves with one dependent load ahead of
 // the copy; the grid covers two thirds of the capacity's pieces
-// (EP_INDEXED_GRID_THIRDS), and a wave takes a further piece when the filled
+// (EP_INDEXED_GRID_SIXTHS), and a wave takes a further piece when the filled
 // rows reach past it.  Measured on MI355X: 4096 tokens H = 7168 bf16, epilogue 129 ->
 // 125 us inside the step (134 -> 123 us back to back); 8192 tokens H = 4096
 // 106 -> 101 us; fp8 63 -> 62 us.  1 / 4 KiB pieces: 140 / 138 us at 4096
 // tokens.  Without the index, pieces that first search the tables were far
 // slower (1 KiB: 199 us; 2 KiB with the tables in LDS 128 us, 4 KiB 137 us).
-template <int CPW>
-__global__ void __launch_bounds__(kThreads) k_epilogue_indexed(DispatchArgs a) {
+template <int CPW, int NW = kWavesPerBlock>
+__global__ void __launch_bounds__(NW * kWave) k_epilogue_indexed(DispatchArgs a) {
     const Shape &sh = a.sh;
     const int lane = lane_id();
     const int nchunks = sh.row_bytes / 16;
     const int P = (nchunks + CPW * kWave - 1) / (CPW * kWave);
     const int64_t n_units = min(min((int64_t)a.recv_base[sh.R], a.recv_capacity_rows), compact_rows_bound(sh)) * P;
     const int64_t n_staging = (int64_t)sh.R * sh.S * sh.Nmax;
-    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t u = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; u < n_units; u += nwaves) {
+    const int64_t nwaves = (int64_t)gridDim.x * NW;
+    for (int64_t u = (int64_t)blockIdx.x * NW + threadIdx.x / kWave; u < n_units; u += nwaves) {
         const int64_t i = u / P;
         const int p = (int)(u - i * P);
         const int64_t row = a.recv_row_src[i];
@@ -829,13 +839,14 @@ struct EpilogueL {
             constexpr int cpw = EP_EXPAND_PIECE_CPW;
             const int64_t xp = (a.sh.row_bytes / 16 + cpw * kWave - 1) / (cpw * kWave);
             hipLaunchKernelGGL(k_epilogue_expand_pieces<cpw>,
-                               dim3(grid_for((rows * xp * EP_INDEXED_GRID_THIRDS + 2) / 3, EP_EPILOGUE_BLOCKS)),
+                               dim3(grid_for((rows * xp * EP_INDEXED_GRID_SIXTHS + 5) / 6, EP_EPILOGUE_BLOCKS)),
                                dim3(kThreads), fits ? tab : 0, st, a, (int)fits);
         }
         else if (a.recv_row_src) {
-            const int64_t units = (rows * pieces * EP_INDEXED_GRID_THIRDS + 2) / 3;
-            hipLaunchKernelGGL(k_epilogue_indexed<kIndexedCpw>, dim3(grid_for(units, EP_EPILOGUE_BLOCKS)),
-                               dim3(kThreads), 0, st, a);
+            const int64_t units = (rows * pieces * EP_INDEXED_GRID_SIXTHS + 5) / 6;
+            constexpr int nw = EP_INDEXED_WAVES;
+            const int64_t blocks = std::min<int64_t>(std::max<int64_t>((units + nw - 1) / nw, 1), EP_EPILOGUE_BLOCKS);
+            hipLaunchKernelGGL((k_epilogue_indexed<kIndexedCpw, nw>), dim3((int)blocks), dim3(nw * kWave), 0, st, a);
         } else if (a.slices == 1 && a.sh.row_bytes / 16 <= CPL * kWave)
             hipLaunchKernelGGL(k_epilogue_pf<CPL>, dim3(grid_for(rows, EP_EPILOGUE_BLOCKS)), dim3(kThreads),
                                fits ? tab : 0, st, a, (int)fits);
