@@ -23,8 +23,14 @@
 namespace ep {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWavesPerBlock = kThreads / kWave;
+// Waves per workgroup.  Measured on MI355X (4096 tokens H = 7168 bf16 and
+// fp8, 8192 tokens H = 4096): 1 or 2 waves 0.3-1 us and 8 waves 2 us slower
+// in the combine than 4.
+#ifndef EP_COMBINE_WAVES
+#define EP_COMBINE_WAVES 4
+#endif
+constexpr int kWavesPerBlock = EP_COMBINE_WAVES;
+constexpr int kThreads = kWavesPerBlock * kWave;
 #ifndef EP_COMBINE_ROWS
 #define EP_COMBINE_ROWS 8  // G: distinct rows loaded together
 #endif
