@@ -119,6 +119,13 @@ constexpr int kIndexedCpw = EP_INDEXED_CPW;
 #ifndef EP_SCATTER_BLOCKS
 #define EP_SCATTER_BLOCKS (1 << 20)
 #endif
+// Tokens per wave of the pipelined staging scatter.  Measured on MI355X
+// (scatter inside the step): 4096 tokens H = 7168 bf16 2 / 3 / 4 per wave
+// 70 / 84-85 / 71 us, fp8 41 / 50 / 49 us, 8192 tokens H = 4096 60 / 67 / 63 us
+// (3 per wave leaves the device's wave slots part empty).
+#ifndef EP_SCATTER_TOKENS_PER_WAVE
+#define EP_SCATTER_TOKENS_PER_WAVE 2
+#endif
 #ifndef EP_SCATTER_PIPELINE_MAX_BYTES
 #define EP_SCATTER_PIPELINE_MAX_BYTES (1ll << 30)
 #endif
@@ -812,8 +819,10 @@ struct ScatterL {
         // per wave.
         const int64_t bound = (int64_t)a.sh.S * a.sh.T * (a.sh.K < a.sh.R ? a.sh.K : a.sh.R) * a.sh.row_bytes;
         if (a.slices == 1 && nchunks <= CPL * kWave && bound <= (int64_t)EP_SCATTER_PIPELINE_MAX_BYTES) {
-            hipLaunchKernelGGL(k_scatter_pf<CPL>, dim3(grid_for((units + 1) / 2, EP_SCATTER_BLOCKS)), dim3(kThreads), 0,
-                               st, a);
+            hipLaunchKernelGGL(k_scatter_pf<CPL>,
+                               dim3(grid_for((units + EP_SCATTER_TOKENS_PER_WAVE - 1) / EP_SCATTER_TOKENS_PER_WAVE,
+                                             EP_SCATTER_BLOCKS)),
+                               dim3(kThreads), 0, st, a);
             return hipGetLastError();
         }
         hipLaunchKernelGGL(k_scatter<CPL>, dim3(grid_for(units, EP_SCATTER_BLOCKS)), dim3(kThreads), 0, st, a);
